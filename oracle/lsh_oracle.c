@@ -1,0 +1,402 @@
+/*
+ * lsh_oracle.c -- plain, slow, fp64 CPU oracle of the Reformer LSH-attention
+ * forward pass (hash -> sort -> chunked attention -> unsort + round combine).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file; only the tests, the package smoke check and the
+ * CPU-baseline leg of the benchmark do.  It shares no code, header, table or
+ * helper with the HIP library: it has its own argument list (plain ints), its
+ * own index arithmetic and its own loops.
+ *
+ * Source of every step ("the pages" = the five web pages on Reformer: The
+ * Efficient Transformer, Kitaev, Kaiser, Levskaya, ICLR 2020):
+ *   hash      -- Reformer study note (eightmm.github.io), section "LSH
+ *                Attention", equation h(x) in {1..B}; the concrete hash is the
+ *                random-rotation angular hash argmax([xR ; -xR]).
+ *   sort      -- same note, section "Sorting and Chunking" (hash -> sort ->
+ *                bucket-contiguous sequence -> chunked attention).
+ *   attend    -- same note, "LSH Attention" equations N_LSH(i) and y_i,
+ *                "Shared Query-Key Space" (Q = K), "Sorting and Chunking"
+ *                (attention inside chunks of nearby sorted positions) and
+ *                "Implementation Reading" (causal mask must survive the sort;
+ *                same-token policy).
+ *   combine   -- same note, "Multiple Hash Rounds", N(i) = union over r of
+ *                N^(r)(i), realised as a logsumexp-weighted combine.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - buckets are 0-based indices into the concatenation [xR ; -xR]; ties go
+ *     to the lowest index; B = 1 means "no hashing" (bucket 0);
+ *   - x.R_j is summed sequentially over k = 0..d-1 in fp64 starting from 0.0;
+ *   - the rotation of head h, round r is stored as B/2 direction rows:
+ *     rot[h][r][j][k] = R_{h,r}[k][j];
+ *   - each (batch, head, round) segment is sorted and chunked independently,
+ *     by the key (bucket, original position);
+ *   - the window of sorted chunk c is chunk c-1 (if c > 0) and chunk c;
+ *   - keys are L2-normalised: k_j = x_j / max(|x_j|_2, 1e-6); score
+ *     s_ij = (x_i . k_j) / sqrt(d);
+ *   - causal masking compares ORIGINAL positions (j <= i);
+ *   - self-mask: token i is never its own candidate in any round; if no round
+ *     leaves any candidate, y_i = v_i (the token attends only to itself);
+ *   - rounds combine as a multiset: a key found in k rounds counts k times.
+ *
+ * Layouts (all row-major, all arrays owned by the caller):
+ *   qk, v      [batch][heads][L][d]            double
+ *   rot        [heads][rounds][B/2][d]         double (empty if B == 1)
+ *   buckets    [batch][heads][rounds][L]       int32, original order
+ *   perm       [batch][heads][rounds][L]       int32, sorted slot -> position
+ *   inv_perm   [batch][heads][rounds][L]       int32, position -> sorted slot
+ *   o_rounds   [batch][heads][rounds][L][d]    double, sorted order
+ *   lse        [batch][heads][rounds][L]       double, sorted order (-inf = no candidate)
+ *   y          [batch][heads][L][d]            double, original order
+ *
+ * Every function returns 0 on success and -1 on an invalid argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_NORM_EPS 1e-6
+
+typedef struct {
+  int batch, heads, len, dim, buckets, rounds, chunk, causal, self_mask;
+} shape_t;
+
+static int make_shape(shape_t* s, int batch, int heads, int len, int dim,
+                      int n_buckets, int rounds, int chunk, int causal,
+                      int self_mask) {
+  if (batch < 1 || heads < 1 || len < 1 || dim < 1 || rounds < 1 || chunk < 1)
+    return -1;
+  if (n_buckets < 1 || (n_buckets > 1 && (n_buckets % 2) != 0)) return -1;
+  if (len % chunk != 0) return -1;
+  s->batch = batch; s->heads = heads; s->len = len; s->dim = dim;
+  s->buckets = n_buckets; s->rounds = rounds; s->chunk = chunk;
+  s->causal = causal ? 1 : 0; s->self_mask = self_mask ? 1 : 0;
+  return 0;
+}
+
+/* ------------------------------------------------------------------ hash */
+
+/* Bucket of one token vector x (length d) under one rotation (rows
+ * rot_hr[j][k], j < B/2).  The candidates are c = [s_0..s_{B/2-1},
+ * -s_0..-s_{B/2-1}] with s_j = sum_k x_k R[k][j]; the bucket is the smallest
+ * index t attaining max(c).  s[] is scratch of length B/2. */
+static int32_t hash_one(const double* x, const double* rot_hr, int d, int nb,
+                        double* s) {
+  if (nb == 1) return 0;
+  const int half = nb / 2;
+  for (int j = 0; j < half; ++j) {
+    double acc = 0.0;
+    for (int k = 0; k < d; ++k) acc = acc + x[k] * rot_hr[(int64_t)j * d + k];
+    s[j] = acc;
+  }
+  double best = s[0];
+  int32_t arg = 0;
+  for (int t = 1; t < nb; ++t) {
+    const double c = (t < half) ? s[t] : -s[t - half];
+    if (c > best) { best = c; arg = t; }
+  }
+  return arg;
+}
+
+/* idx[n] are flat indices into buckets[batch][heads][rounds][L]. */
+int oracle_lsh_hash_rows(int batch, int heads, int len, int dim, int n_buckets,
+                         int rounds, const double* qk, const double* rot,
+                         int64_t n, const int64_t* idx, int32_t* out) {
+  shape_t s;
+  if (make_shape(&s, batch, heads, len, dim, n_buckets, rounds, len, 0, 0))
+    return -1;
+  const int64_t total = (int64_t)batch * heads * rounds * len;
+  for (int64_t q = 0; q < n; ++q)
+    if (idx[q] < 0 || idx[q] >= total) return -1;
+  const int half = n_buckets / 2;
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    double* sbuf = (double*)malloc(sizeof(double) * (size_t)(half > 0 ? half : 1));
+    if (!sbuf) bad |= 1;
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t q = 0; q < n; ++q) {
+      if (!sbuf) continue;
+      const int64_t f = idx[q];
+      const int i = (int)(f % len);
+      const int r = (int)((f / len) % rounds);
+      const int h = (int)((f / ((int64_t)len * rounds)) % heads);
+      const int b = (int)(f / ((int64_t)len * rounds * heads));
+      const double* x = qk + (((int64_t)b * heads + h) * len + i) * dim;
+      const double* rhr = rot + ((int64_t)h * rounds + r) * half * dim;
+      out[q] = hash_one(x, rhr, dim, n_buckets, sbuf);
+    }
+    free(sbuf);
+  }
+  return bad ? -1 : 0;
+}
+
+int oracle_lsh_hash(int batch, int heads, int len, int dim, int n_buckets,
+                    int rounds, const double* qk, const double* rot,
+                    int32_t* buckets) {
+  const int64_t total = (int64_t)batch * heads * rounds * len;
+  if (total <= 0) return -1;
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)total);
+  if (!idx) return -1;
+  for (int64_t f = 0; f < total; ++f) idx[f] = f;
+  const int rc = oracle_lsh_hash_rows(batch, heads, len, dim, n_buckets, rounds,
+                                      qk, rot, total, idx, buckets);
+  free(idx);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ sort */
+
+typedef struct { int32_t bucket, pos; } sort_key_t;
+
+static int key_cmp(const void* a, const void* b) {
+  const sort_key_t* p = (const sort_key_t*)a;
+  const sort_key_t* q = (const sort_key_t*)b;
+  if (p->bucket != q->bucket) return p->bucket < q->bucket ? -1 : 1;
+  if (p->pos != q->pos) return p->pos < q->pos ? -1 : 1;
+  return 0;
+}
+
+/* Every (batch, head, round) segment of length L is sorted by the unique key
+ * (bucket, original position); perm[s] is the position at sorted slot s and
+ * inv_perm is its inverse. */
+int oracle_lsh_sort(int n_segments, int len, const int32_t* buckets,
+                    int32_t* perm, int32_t* inv_perm) {
+  if (n_segments < 1 || len < 1) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int g = 0; g < n_segments; ++g) {
+    const int32_t* bk = buckets + (int64_t)g * len;
+    sort_key_t* keys = (sort_key_t*)malloc(sizeof(sort_key_t) * (size_t)len);
+    if (!keys) { bad |= 1; continue; }
+    for (int i = 0; i < len; ++i) { keys[i].bucket = bk[i]; keys[i].pos = i; }
+    qsort(keys, (size_t)len, sizeof(sort_key_t), key_cmp);
+    for (int s = 0; s < len; ++s) {
+      perm[(int64_t)g * len + s] = keys[s].pos;
+      inv_perm[(int64_t)g * len + keys[s].pos] = s;
+    }
+    free(keys);
+  }
+  return bad ? -1 : 0;
+}
+
+/* --------------------------------------------------------------- attend */
+
+/* Candidate keys of the query at sorted slot `slot` of segment `seg`
+ * (segment = (b*heads + h)*rounds + r): the original positions j of the
+ * tokens in the window of its chunk that share its bucket, satisfy the causal
+ * rule and are not the query itself (when self-masking).  Written to out[] in
+ * window order; returns their number. */
+static int candidates(const shape_t* s, const int32_t* buckets,
+                      const int32_t* perm, int64_t seg, int slot,
+                      int32_t* out) {
+  const int32_t* bk = buckets + seg * s->len;
+  const int32_t* pm = perm + seg * s->len;
+  const int i = pm[slot];
+  const int c = slot / s->chunk;
+  const int lo = (c > 0) ? (c - 1) * s->chunk : 0;
+  const int hi = (c + 1) * s->chunk;
+  int n = 0;
+  for (int t = lo; t < hi; ++t) {
+    const int j = pm[t];
+    if (bk[j] != bk[i]) continue;
+    if (s->causal && j > i) continue;
+    if (s->self_mask && j == i) continue;
+    out[n++] = j;
+  }
+  return n;
+}
+
+static double norm2(const double* x, int d) {
+  double acc = 0.0;
+  for (int k = 0; k < d; ++k) acc = acc + x[k] * x[k];
+  return sqrt(acc);
+}
+
+/* o (length d) and lse of one query row. */
+static void attend_one(const shape_t* s, const double* qk, const double* v,
+                       const int32_t* buckets, const int32_t* perm,
+                       int64_t seg, int slot, int32_t* cand, double* score,
+                       double* o, double* lse) {
+  const int d = s->dim;
+  const int64_t bh = seg / s->rounds;
+  const double* xs = qk + bh * (int64_t)s->len * d;
+  const double* vs = v + bh * (int64_t)s->len * d;
+  const int i = perm[seg * s->len + slot];
+  const int n = candidates(s, buckets, perm, seg, slot, cand);
+  for (int k = 0; k < d; ++k) o[k] = 0.0;
+  if (n == 0) { *lse = -INFINITY; return; }
+  const double* xi = xs + (int64_t)i * d;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  double mx = -INFINITY;
+  for (int a = 0; a < n; ++a) {
+    const double* xj = xs + (int64_t)cand[a] * d;
+    double dot = 0.0;
+    for (int k = 0; k < d; ++k) dot = dot + xi[k] * xj[k];
+    double nj = norm2(xj, d);
+    if (nj < ORACLE_NORM_EPS) nj = ORACLE_NORM_EPS;
+    score[a] = dot / nj * inv_sqrt_d;
+    if (score[a] > mx) mx = score[a];
+  }
+  double sum = 0.0;
+  for (int a = 0; a < n; ++a) sum += exp(score[a] - mx);
+  const double l = mx + log(sum);
+  for (int a = 0; a < n; ++a) {
+    const double p = exp(score[a] - l);
+    const double* vj = vs + (int64_t)cand[a] * d;
+    for (int k = 0; k < d; ++k) o[k] += p * vj[k];
+  }
+  *lse = l;
+}
+
+/* idx[n] are flat indices seg*L + slot into o_rounds rows / lse. */
+int oracle_lsh_attend_rows(int batch, int heads, int len, int dim,
+                           int n_buckets, int rounds, int chunk, int causal,
+                           int self_mask, const double* qk, const double* v,
+                           const int32_t* buckets, const int32_t* perm,
+                           int64_t n, const int64_t* idx, double* o,
+                           double* lse) {
+  shape_t s;
+  if (make_shape(&s, batch, heads, len, dim, n_buckets, rounds, chunk, causal,
+                 self_mask))
+    return -1;
+  const int64_t total = (int64_t)batch * heads * rounds * len;
+  for (int64_t q = 0; q < n; ++q)
+    if (idx[q] < 0 || idx[q] >= total) return -1;
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * 2 * (size_t)chunk);
+    double* score = (double*)malloc(sizeof(double) * 2 * (size_t)chunk);
+    if (!cand || !score) bad |= 1;
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t q = 0; q < n; ++q) {
+      if (!cand || !score) continue;
+      attend_one(&s, qk, v, buckets, perm, idx[q] / len, (int)(idx[q] % len),
+                 cand, score, o + q * dim, lse + q);
+    }
+    free(cand);
+    free(score);
+  }
+  return bad ? -1 : 0;
+}
+
+int oracle_lsh_attend(int batch, int heads, int len, int dim, int n_buckets,
+                      int rounds, int chunk, int causal, int self_mask,
+                      const double* qk, const double* v, const int32_t* buckets,
+                      const int32_t* perm, double* o_rounds, double* lse) {
+  const int64_t total = (int64_t)batch * heads * rounds * len;
+  if (total <= 0) return -1;
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)total);
+  if (!idx) return -1;
+  for (int64_t f = 0; f < total; ++f) idx[f] = f;
+  const int rc = oracle_lsh_attend_rows(batch, heads, len, dim, n_buckets,
+                                        rounds, chunk, causal, self_mask, qk,
+                                        v, buckets, perm, total, idx, o_rounds,
+                                        lse);
+  free(idx);
+  return rc;
+}
+
+/* Candidate list of one query (for tests of the window rule). */
+int oracle_lsh_candidates(int batch, int heads, int len, int n_buckets,
+                          int rounds, int chunk, int causal, int self_mask,
+                          const int32_t* buckets, const int32_t* perm,
+                          int64_t seg, int slot, int32_t* out) {
+  shape_t s;
+  if (make_shape(&s, batch, heads, len, 1, n_buckets, rounds, chunk, causal,
+                 self_mask))
+    return -1;
+  if (seg < 0 || seg >= (int64_t)batch * heads * rounds || slot < 0 ||
+      slot >= len)
+    return -1;
+  return candidates(&s, buckets, perm, seg, slot, out);
+}
+
+/* -------------------------------------------------------------- combine */
+
+/* y_i from the R rounds' (o, lse) of token i: softmax weights over the
+ * rounds' logsumexps; if every round is empty, y_i = v_i. */
+static void combine_one(const shape_t* s, const double* o_rounds,
+                        const double* lse, const int32_t* inv_perm,
+                        const double* v, int64_t bh, int i, double* y) {
+  const int d = s->dim;
+  const int64_t L = s->len;
+  double mx = -INFINITY;
+  for (int r = 0; r < s->rounds; ++r) {
+    const int64_t seg = bh * s->rounds + r;
+    const double l = lse[seg * L + inv_perm[seg * L + i]];
+    if (l > mx) mx = l;
+  }
+  if (mx == -INFINITY) {
+    for (int k = 0; k < d; ++k) y[k] = v[(bh * L + i) * d + k];
+    return;
+  }
+  double wsum = 0.0;
+  for (int k = 0; k < d; ++k) y[k] = 0.0;
+  for (int r = 0; r < s->rounds; ++r) {
+    const int64_t seg = bh * s->rounds + r;
+    const int64_t slot = inv_perm[seg * L + i];
+    const double w = exp(lse[seg * L + slot] - mx);
+    wsum += w;
+    for (int k = 0; k < d; ++k) y[k] += w * o_rounds[(seg * L + slot) * d + k];
+  }
+  for (int k = 0; k < d; ++k) y[k] /= wsum;
+}
+
+/* idx[n] are flat indices (b*heads + h)*L + i into y rows. */
+int oracle_lsh_combine_rows(int batch, int heads, int len, int dim, int rounds,
+                            const double* o_rounds, const double* lse,
+                            const int32_t* inv_perm, const double* v,
+                            int64_t n, const int64_t* idx, double* y) {
+  shape_t s;
+  if (make_shape(&s, batch, heads, len, dim, 1, rounds, len, 0, 0)) return -1;
+  const int64_t total = (int64_t)batch * heads * len;
+  for (int64_t q = 0; q < n; ++q)
+    if (idx[q] < 0 || idx[q] >= total) return -1;
+#pragma omp parallel for schedule(dynamic, 256)
+  for (int64_t q = 0; q < n; ++q)
+    combine_one(&s, o_rounds, lse, inv_perm, v, idx[q] / len,
+                (int)(idx[q] % len), y + q * dim);
+  return 0;
+}
+
+int oracle_lsh_combine(int batch, int heads, int len, int dim, int rounds,
+                       const double* o_rounds, const double* lse,
+                       const int32_t* inv_perm, const double* v, double* y) {
+  const int64_t total = (int64_t)batch * heads * len;
+  if (total <= 0) return -1;
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)total);
+  if (!idx) return -1;
+  for (int64_t f = 0; f < total; ++f) idx[f] = f;
+  const int rc = oracle_lsh_combine_rows(batch, heads, len, dim, rounds,
+                                         o_rounds, lse, inv_perm, v, total, idx,
+                                         y);
+  free(idx);
+  return rc;
+}
+
+/* -------------------------------------------------------------- forward */
+
+/* All four steps; every intermediate is returned to the caller. */
+int oracle_lsh_forward(int batch, int heads, int len, int dim, int n_buckets,
+                       int rounds, int chunk, int causal, int self_mask,
+                       const double* qk, const double* v, const double* rot,
+                       int32_t* buckets, int32_t* perm, int32_t* inv_perm,
+                       double* o_rounds, double* lse, double* y) {
+  shape_t s;
+  if (make_shape(&s, batch, heads, len, dim, n_buckets, rounds, chunk, causal,
+                 self_mask))
+    return -1;
+  if (oracle_lsh_hash(batch, heads, len, dim, n_buckets, rounds, qk, rot,
+                      buckets))
+    return -1;
+  if (oracle_lsh_sort(batch * heads * rounds, len, buckets, perm, inv_perm))
+    return -1;
+  if (oracle_lsh_attend(batch, heads, len, dim, n_buckets, rounds, chunk,
+                        causal, self_mask, qk, v, buckets, perm, o_rounds, lse))
+    return -1;
+  return oracle_lsh_combine(batch, heads, len, dim, rounds, o_rounds, lse,
+                            inv_perm, v, y);
+}

@@ -1,0 +1,372 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every expectation is a closed
+form, a hand-worked fixture (tests/golden), an identity of the method, a
+textbook special case (dense softmax attention, banded local attention) or a
+brute-force enumeration written independently in NumPy below.
+
+Passages (Reformer study note, eightmm.github.io/papers/architectures/reformer,
+unless noted):
+  "LSH Attention"          h(x) in {1..B}; N_LSH(i) = {j : h(q_i) = h(k_j)};
+                           y_i = sum_{j in N(i)} softmax_j(q_i.k_j / sqrt(d_k)) v_j
+  "Question"               dense attention A = Q K^T / sqrt(d_k)
+  "Shared Query-Key Space" Q = K
+  "Sorting and Chunking"   hash -> sort -> bucket-contiguous -> chunked attention
+  "Multiple Hash Rounds"   N(i) = union over rounds of N^(r)(i)
+  "Implementation Reading" causal masking must survive the sort; same-token policy
+  yomu.fyi summary, "Takeaways": local attention over chunks with overlap
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EPS = 1e-6
+
+
+# ----------------------------------------------------------- brute force
+def np_scores(x, d):
+    """s[i, j] = x_i . x_j / (max(|x_j|, eps) sqrt(d)) (all pairs)."""
+    n = np.maximum(np.sqrt((x * x).sum(-1)), EPS)
+    return (x @ x.T) / n[None, :] / math.sqrt(d)
+
+
+def np_masked_softmax_attention(x, v, allowed):
+    """Row-wise softmax attention over the boolean matrix `allowed`;
+    rows with no allowed key return (v_i, -inf)."""
+    L, d = x.shape
+    s = np_scores(x, d)
+    y = np.empty_like(v)
+    lse = np.empty(L)
+    for i in range(L):
+        idx = np.nonzero(allowed[i])[0]
+        if idx.size == 0:
+            y[i] = v[i]
+            lse[i] = -np.inf
+            continue
+        si = s[i, idx]
+        m = si.max()
+        w = np.exp(si - m)
+        lse[i] = m + math.log(w.sum())
+        y[i] = (w / w.sum()) @ v[idx]
+    return y, lse
+
+
+def dense_allowed(L, causal, self_mask):
+    a = np.ones((L, L), bool)
+    if causal:
+        a &= np.tril(np.ones((L, L), bool))
+    if self_mask:
+        a &= ~np.eye(L, dtype=bool)
+    return a
+
+
+def rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ------------------------------------------------------------ the hash
+def test_hash_closed_form_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "hash_closed_form.json")))
+    xs = np.array([c["x"] for c in g["cases"]], np.float64)
+    rot = np.array(g["rot"], np.float64)[None, None]          # [H=1][R=1][2][2]
+    bk = oracle.hash(xs[None, None], rot, 4, 1)[0, 0, 0]
+    assert bk.tolist() == [c["bucket"] for c in g["cases"]]
+    # the fixture's own candidate vectors agree with x R (stated by hand)
+    for c in g["cases"]:
+        assert c["c"] == pytest.approx(list(np.concatenate([c["x"], -np.array(c["x"])])))
+
+
+def test_hash_integer_inputs_brute_force():
+    """Small-integer inputs make every dot product exact in any order, so the
+    first maximum of [xR; -xR] is fixed exactly (many ties included)."""
+    g = np.random.default_rng(7)
+    H, R, L, d, B = 2, 3, 257, 64, 16
+    x = g.integers(-3, 4, size=(1, H, L, d)).astype(np.float64)
+    rot = g.integers(-2, 3, size=(H, R, B // 2, d)).astype(np.float64)
+    got = oracle.hash(x, rot, B, R)
+    xi = x.astype(np.int64)
+    ri = rot.astype(np.int64)
+    for h in range(H):
+        for r in range(R):
+            s = xi[0, h] @ ri[h, r].T                        # exact integers [L][B/2]
+            c = np.concatenate([s, -s], axis=1)
+            assert np.array_equal(got[0, h, r], np.argmax(c, axis=1))  # first max
+    # ties really occur in this case (the tie rule is exercised)
+    s = xi[0, 0] @ ri[0, 0].T
+    c = np.concatenate([s, -s], axis=1)
+    assert ((c == c.max(1, keepdims=True)).sum(1) > 1).any()
+
+
+def test_hash_b1_is_zero_and_b2_is_sign():
+    x = rand(1, 1, 2, 100, 8)
+    assert (oracle.hash(x, np.zeros((2, 3, 0, 8)), 1, 3) == 0).all()
+    rot = rand(2, 2, 1, 1, 8)
+    bk = oracle.hash(x, rot, 2, 1)
+    s = np.einsum("bhld,hjd->bhlj", x, rot[:, 0])[..., 0]
+    assert np.array_equal(bk[:, :, 0], np.where(s >= 0, 0, 1))
+
+
+def test_hash_random_matches_matmul_argmax():
+    x = rand(3, 2, 2, 300, 64)
+    rot = rand(4, 2, 2, 32, 64)
+    bk = oracle.hash(x, rot, 64, 2)
+    s = np.einsum("bhld,hrjd->bhrlj", x, rot)
+    ref = np.argmax(np.concatenate([s, -s], -1), -1)
+    assert np.array_equal(bk, ref)
+
+
+def test_hash_negation_and_scaling_identities():
+    x = rand(5, 1, 2, 500, 64)
+    rot = rand(6, 2, 3, 16, 64)
+    B = 32
+    bk = oracle.hash(x, rot, B, 3)
+    assert np.array_equal(oracle.hash(-x, rot, B, 3), (bk + B // 2) % B)
+    for k in (-7, -1, 1, 3, 20):
+        assert np.array_equal(oracle.hash(x * 2.0 ** k, rot, B, 3), bk)
+
+
+def test_hash_direction_permutation_relabels():
+    x = rand(8, 1, 1, 400, 64)
+    rot = rand(9, 1, 1, 16, 64)
+    B = 32
+    p = np.random.default_rng(10).permutation(16)
+    bk = oracle.hash(x, rot, B, 1)
+    bk2 = oracle.hash(x, rot[:, :, p], B, 1)
+    inv = np.argsort(p)                       # new row inv[j] holds old direction j
+    lab = np.concatenate([inv, inv + 16])
+    assert np.array_equal(bk2, lab[bk])
+
+
+def test_hash_rows_matches_full():
+    x = rand(11, 2, 2, 128, 64)
+    rot = rand(12, 2, 2, 8, 64)
+    full = oracle.hash(x, rot, 16, 2)
+    idx = np.random.default_rng(13).integers(0, full.size, 300)
+    assert np.array_equal(oracle.hash_rows(x, rot, 16, 2, idx), full.ravel()[idx])
+
+
+# ------------------------------------------------------------- the sort
+def test_sort_is_the_bucket_position_order():
+    g = np.random.default_rng(14)
+    L = 999
+    bk = np.stack([g.integers(0, 7, L), np.minimum(g.geometric(0.3, L), 40), np.zeros(L, int),
+                   np.arange(L)[::-1] % 5]).astype(np.int32).reshape(1, 2, 2, L)
+    perm, inv = oracle.sort(bk)
+    for s in range(4):
+        b = bk.reshape(4, L)[s]
+        p = perm.reshape(4, L)[s]
+        q = inv.reshape(4, L)[s]
+        assert p.tolist() == sorted(range(L), key=lambda i: (b[i], i))
+        assert np.array_equal(q[p], np.arange(L))
+        assert np.array_equal(np.sort(p), np.arange(L))
+
+
+# ------------------------------------------------ dense special case (B=1, m=L)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("self_mask", [False, True])
+@pytest.mark.parametrize("rounds", [1, 3])
+def test_b1_one_chunk_is_dense_attention(causal, self_mask, rounds):
+    L, d = 96, 64
+    x = rand(20, 1, 2, L, d)
+    v = rand(21, 1, 2, L, d)
+    out = oracle.forward(x, v, np.zeros((2, rounds, 0, d)), 1, rounds, L, causal, self_mask)
+    for h in range(2):
+        y, lse = np_masked_softmax_attention(x[0, h], v[0, h], dense_allowed(L, causal, self_mask))
+        np.testing.assert_allclose(out["y"][0, h], y, rtol=0, atol=1e-12)
+        assert np.array_equal(out["perm"][0, h], np.tile(np.arange(L), (rounds, 1)))
+        np.testing.assert_allclose(out["lse"][0, h, 0], lse, rtol=0, atol=1e-12)
+
+
+def test_softmax_two_keys_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "softmax_two_keys.json")))
+    x = np.array(g["x"])[None, None]
+    v = np.array(g["v"])[None, None]
+    out = oracle.forward(x, v, np.zeros((1, 1, 0, 4)), 1, 1, 3, False, True)
+    env = {"e": math.e, "sqrt": math.sqrt, "log": math.log}
+    y = np.array([[eval(e, {}, env) for e in row] for row in g["y_expr"]])
+    lse = np.array([eval(e, {}, env) for e in g["lse_expr"]])
+    np.testing.assert_allclose(out["y"][0, 0], y, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out["lse"][0, 0, 0], lse, rtol=0, atol=1e-15)
+
+
+# -------------------------------------- local attention (B=1, m=64 < L)
+@pytest.mark.parametrize("causal", [False, True])
+def test_b1_chunked_is_banded_local_attention(causal):
+    L, d, m = 320, 64, 64
+    x = rand(22, 1, 1, L, d)
+    v = rand(23, 1, 1, L, d)
+    out = oracle.forward(x, v, np.zeros((1, 1, 0, d)), 1, 1, m, causal, True)
+    assert np.array_equal(out["perm"][0, 0, 0], np.arange(L))
+    ci = np.arange(L) // m
+    allowed = (ci[None, :] <= ci[:, None]) & (ci[None, :] >= ci[:, None] - 1)
+    allowed &= dense_allowed(L, causal, True)
+    y, lse = np_masked_softmax_attention(x[0, 0], v[0, 0], allowed)
+    np.testing.assert_allclose(out["y"][0, 0], y, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["lse"][0, 0, 0], lse, rtol=0, atol=1e-12)
+
+
+# ----------------------------- exact-bucket special case (m = L, any B)
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_chunk_is_exact_bucket_attention(causal):
+    L, d, B, R = 128, 64, 8, 2
+    x = rand(24, 1, 1, L, d)
+    v = rand(25, 1, 1, L, d)
+    rot = rand(26, 1, R, B // 2, d)
+    out = oracle.forward(x, v, rot, B, R, L, causal, True)
+    for r in range(R):
+        bk = out["buckets"][0, 0, r]
+        allowed = (bk[:, None] == bk[None, :]) & dense_allowed(L, causal, True)
+        _, lse = np_masked_softmax_attention(x[0, 0], v[0, 0], allowed)
+        # per-round outputs are in sorted order: map back with perm
+        p = out["perm"][0, 0, r]
+        np.testing.assert_allclose(out["lse"][0, 0, r], lse[p], rtol=0, atol=1e-12)
+        o_nat = np.empty((L, d))
+        o_nat[p] = out["o_rounds"][0, 0, r]
+        y_r, _ = np_masked_softmax_attention(x[0, 0], v[0, 0], allowed)
+        empty = ~allowed.any(1)
+        np.testing.assert_allclose(o_nat[~empty], y_r[~empty], rtol=0, atol=1e-12)
+        assert (o_nat[empty] == 0).all()
+
+
+# -------------------------------------------------------- the window rule
+@pytest.mark.parametrize("causal,self_mask", [(False, False), (False, True), (True, True),
+                                              (True, False)])
+def test_candidates_follow_the_window_rule(causal, self_mask):
+    L, d, B, R, m = 192, 16, 8, 2, 32
+    x = rand(27, 2, 1, L, d)
+    rot = rand(28, 1, R, B // 2, d)
+    bk = oracle.hash(x, rot, B, R)
+    perm, inv = oracle.sort(bk)
+    for seg in range(2 * R):
+        b, r = seg // R, seg % R
+        bkr, invr, pr = bk[b, 0, r], inv[b, 0, r], perm[b, 0, r]
+        for slot in range(L):
+            i = pr[slot]
+            c = slot // m
+            want = [j for j in pr  # window order = sorted order
+                    if bkr[j] == bkr[i] and c - 1 <= invr[j] // m <= c
+                    and (not causal or j <= i) and (not self_mask or j != i)]
+            got = oracle.candidates(bk, perm, B, m, causal, self_mask, seg, slot)
+            assert got.tolist() == want
+
+
+def test_only_candidates_influence_a_row():
+    """Perturbing v_j moves o_r(i) iff j is a candidate of i in round r."""
+    L, d, B, R, m = 128, 16, 4, 1, 32
+    x = rand(29, 1, 1, L, d)
+    v = rand(30, 1, 1, L, d)
+    rot = rand(31, 1, R, B // 2, d)
+    bk = oracle.hash(x, rot, B, R)
+    perm, _ = oracle.sort(bk)
+    o0, _ = oracle.attend(x, v, bk, perm, B, m, True, True)
+    for j in (0, 17, 63, 127):
+        v2 = v.copy()
+        v2[0, 0, j] += 1.0
+        o1, _ = oracle.attend(x, v2, bk, perm, B, m, True, True)
+        for slot in range(L):
+            cand = oracle.candidates(bk, perm, B, m, True, True, 0, slot)
+            moved = not np.array_equal(o0[0, 0, 0, slot], o1[0, 0, 0, slot])
+            assert moved == (j in cand.tolist())
+
+
+# ------------------------------------------------------ rounds and combine
+def test_identical_rounds_equal_one_round():
+    L, d, B, m = 256, 64, 16, 64
+    x = rand(32, 1, 2, L, d)
+    v = rand(33, 1, 2, L, d)
+    rot1 = rand(34, 2, 1, B // 2, d)
+    one = oracle.forward(x, v, rot1, B, 1, m, True, True)
+    three = oracle.forward(x, v, np.repeat(rot1, 3, axis=1), B, 3, m, True, True)
+    np.testing.assert_allclose(three["y"], one["y"], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_combine_is_multiset_softmax(causal):
+    """y_i is the softmax over the multiset union of the rounds' candidates."""
+    L, d, B, R, m = 192, 32, 8, 3, 32
+    x = rand(35, 1, 1, L, d)
+    v = rand(36, 1, 1, L, d)
+    rot = rand(37, 1, R, B // 2, d)
+    out = oracle.forward(x, v, rot, B, R, m, causal, True)
+    s = np_scores(x[0, 0], d)
+    for i in range(L):
+        js = []
+        for r in range(R):
+            seg = r
+            slot = out["inv_perm"][0, 0, r, i]
+            js += oracle.candidates(out["buckets"], out["perm"], B, m, causal, True, seg,
+                                    slot).tolist()
+        if not js:
+            np.testing.assert_array_equal(out["y"][0, 0, i], v[0, 0, i])
+            continue
+        js = np.array(js)
+        w = np.exp(s[i, js] - s[i, js].max())
+        np.testing.assert_allclose(out["y"][0, 0, i], (w / w.sum()) @ v[0, 0, js], rtol=0,
+                                   atol=1e-12)
+
+
+def test_causal_future_values_never_reach_the_past():
+    L, d, B, R, m = 256, 64, 16, 2, 64
+    x = rand(38, 1, 1, L, d)
+    v = rand(39, 1, 1, L, d)
+    rot = rand(40, 1, R, B // 2, d)
+    base = oracle.forward(x, v, rot, B, R, m, True, True)["y"]
+    for j in (1, 100, 255):
+        v2 = v.copy()
+        v2[0, 0, j:] = rand(41 + j, L - j, d)
+        y2 = oracle.forward(x, v2, rot, B, R, m, True, True)["y"]
+        assert np.array_equal(y2[0, 0, :j], base[0, 0, :j])
+
+
+def test_self_only_token_returns_its_value():
+    L, d, B, R, m = 128, 64, 8, 2, 64
+    x = rand(42, 1, 1, L, d)
+    v = rand(43, 1, 1, L, d)
+    out = oracle.forward(x, v, rand(44, 1, R, B // 2, d), B, R, m, True, True)
+    # position 0 under a causal self-masked rule has no candidate in any round
+    assert (out["lse"][0, 0, np.arange(R), out["inv_perm"][0, 0, :, 0]] == -np.inf).all()
+    assert np.array_equal(out["y"][0, 0, 0], v[0, 0, 0])
+
+
+def test_empty_rounds_have_minus_inf_and_zero_output():
+    L, d, B, R, m = 128, 16, 64, 2, 64
+    x = rand(45, 1, 1, L, d)
+    v = rand(46, 1, 1, L, d)
+    out = oracle.forward(x, v, rand(47, 1, R, B // 2, d), B, R, m, False, True)
+    lse, o = out["lse"][0, 0], out["o_rounds"][0, 0]
+    empty = lse == -np.inf
+    assert empty.any() and (~empty).any()
+    for r in range(R):
+        for slot in range(L):
+            n = oracle.candidates(out["buckets"], out["perm"], B, m, False, True, r, slot).size
+            assert (n == 0) == empty[r, slot]
+    assert (o[empty] == 0).all()
+
+
+def test_rows_variants_match_full():
+    L, d, B, R, m = 256, 64, 16, 2, 64
+    x = rand(48, 2, 2, L, d)
+    v = rand(49, 2, 2, L, d)
+    out = oracle.forward(x, v, rand(50, 2, R, B // 2, d), B, R, m, True, True)
+    g = np.random.default_rng(51)
+    idx = g.integers(0, out["lse"].size, 200)
+    o, lse = oracle.attend_rows(x, v, out["buckets"], out["perm"], B, m, True, True, idx)
+    np.testing.assert_array_equal(lse, out["lse"].ravel()[idx])
+    np.testing.assert_array_equal(o, out["o_rounds"].reshape(-1, d)[idx])
+    idx = g.integers(0, 2 * 2 * L, 200)
+    y = oracle.combine_rows(out["o_rounds"], out["lse"], out["inv_perm"], v, idx)
+    np.testing.assert_array_equal(y, out["y"].reshape(-1, d)[idx])
+
+
+def test_invalid_arguments_raise():
+    x = rand(52, 1, 1, 100, 8)
+    with pytest.raises(ValueError):
+        oracle.forward(x, x, np.zeros((1, 1, 1, 8)), 3, 1, 10, False, False)   # odd B
+    with pytest.raises(ValueError):
+        oracle.forward(x, x, np.zeros((1, 1, 0, 8)), 1, 1, 64, False, False)   # L % m
