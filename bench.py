@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""LSH-attention forward benchmark on one MI355X.
+
+One step is one pass of the whole hot path -- hash -> sort -> chunked
+attention -> unsort + round combine -- over one batch of seeded synthetic
+input with every tensor already resident in HBM.  Default workload: the
+headline shape (batch 1, 8 heads, L = 65,536, d = 64, B = 1,024 buckets,
+8 hash rounds, chunk 64, causal, self-masked, bf16 inputs).
+
+Prints one JSON line: tokens/s (batch * L per step, all heads and rounds),
+the roofline position of the dominant kernel (per-launch time from HIP
+events on the stream the kernels run on) and the fp64 CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+METRIC = "LSH-attention fwd tokens/s (all heads, rounds) at L=64K; % of HBM/MFMA roofline"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(w):
+    """Algorithmic work per launch of each kernel (bytes or flops)."""
+    N = w.token_rounds
+    T = w.batch * w.heads * w.seq_len
+    d = w.head_dim
+    el = 2 if w.dtype == "bf16" else 4
+    rot = w.heads * w.n_rounds * (w.n_buckets // 2) * d * el
+    return {
+        # x read once, rotations read, bucket ids written; contraction flops
+        "hash": {"bytes": T * d * el + rot + 4 * N, "flops": N * d * w.n_buckets},
+        # keys read twice, perm and inv_perm written
+        "sort": {"bytes": 16 * N},
+        # per token-round: x and v rows gathered (predecessor reused), perm and
+        # bucket id, fp32 output row and lse
+        "attend": {"bytes": N * (2 * d * el + 8 + 4 * d + 4), "flops": N * 4 * 2 * 64 * d},
+        # per token-round: o row, lse and inv_perm read; per token-head: y row written
+        "combine": {"bytes": N * (4 * d + 8) + T * 4 * d},
+    }
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+KERNEL_SOURCES = {
+    "attend": ["lsh_sparse_attention_hash_amd/csrc/attend.hip",
+               "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
+    "hash": ["lsh_sparse_attention_hash_amd/csrc/hash.hip",
+             "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
+    "combine": ["lsh_sparse_attention_hash_amd/csrc/combine.hip",
+                "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
+    "sort": ["lsh_sparse_attention_hash_amd/csrc/sort.hip",
+             "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current source of that kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest(KERNEL_SOURCES[kernel])
+    pat = re.compile(r"^\|\s*%s\s*\|\s*%s\s*\|\s*([0-9a-f]+)\s*\|\s*([0-9.eE+]+)\s*\|" %
+                     (kernel, workload))
+    for line in open(path):
+        m = pat.match(line)
+        if m and m.group(1) == digest:
+            return float(m.group(2))
+    return None
+
+
+def cpu_baseline(w, inputs):
+    """The fp64 oracle on one head of the workload (all rounds, all tokens)."""
+    threads = len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    from lsh_sparse_attention_hash_amd import synth
+    from oracle import oracle
+    oracle.build(force=False)
+    hs = 1
+    qk = synth.to_f64(inputs["qk"][:, :hs], w.dtype)
+    v = synth.to_f64(inputs["v"][:, :hs], w.dtype)
+    rot = synth.to_f64(inputs["rot"][:hs], w.dtype)
+    t0 = time.perf_counter()
+    oracle.forward(qk, v, rot, w.n_buckets, w.n_rounds, w.chunk_len, w.causal, w.self_mask)
+    dt = time.perf_counter() - t0
+    full_est = dt * w.heads / hs
+    return {"value": w.batch * w.seq_len / full_est, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{hs} of {w.heads} heads (batch {w.batch}, L={w.seq_len}, all "
+                      f"{w.n_rounds} rounds), full fp64 forward; tokens/s scaled by "
+                      f"{w.heads // hs}x to all heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run plain device copies of known size "
+                         "(reference for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+    from lsh_sparse_attention_hash_amd import build as lib_build
+    if not os.path.exists(lib_build.LIB):
+        lib_build.build()
+    from lsh_sparse_attention_hash_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] workload {w}")
+    inputs = synth.make_inputs(w)
+    qk = binding.to_device(inputs["qk"], w.dtype)
+    v = binding.to_device(inputs["v"], w.dtype)
+    rot = binding.to_device(inputs["rot"], w.dtype)
+    f = binding.Forward(binding.config_for(w))
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        f.run(qk, v, rot)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    names = ("hash", "sort", "attend", "combine")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        f.hash(qk, rot)
+        e[1].record(stream)
+        f.sort()
+        e[2].record(stream)
+        f.attend(qk, v)
+        e[3].record(stream)
+        f.combine(v)
+        e[4].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    per = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
+           for i, n in enumerate(names)}
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s); per call ms: "
+        + ", ".join(f"{n} {per[n]:.4f}" for n in names))
+
+    if args.copy_calibration:
+        nbytes = 512 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {nbytes} B device copies")
+
+    work = algorithmic(w)
+    kernels = {}
+    for n in names:
+        t = per[n] * 1e-3
+        kb = {"ms": round(per[n], 5), "algorithmic_bytes": work[n]["bytes"],
+              "GBps": round(work[n]["bytes"] / t / 1e9, 1)}
+        if "flops" in work[n]:
+            kb["algorithmic_flops"] = work[n]["flops"]
+            kb["TFLOPs"] = round(work[n]["flops"] / t / 1e12, 2)
+        kernels[n] = kb
+    # the dominant step by time among the single-launch kernels
+    dom = max(("hash", "attend", "combine"), key=lambda n: per[n])
+    t = per[dom] * 1e-3
+    if dom == "hash":
+        ach = work["hash"]["flops"] / t / 1e12
+        roof = {"kernel": "hash_bf16_kernel", "bound": "mfma", "achieved": round(ach, 2),
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        ach = work[dom]["bytes"] / t / 1e9
+        roof = {"kernel": {"attend": "attend_bf16_kernel", "combine": "combine_kernel"}[dom],
+                "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(dom, w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) / Gaussian-mixture inputs, random rotations)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "head_dim": w.head_dim, "n_buckets": w.n_buckets, "n_rounds": w.n_rounds,
+                   "chunk_len": w.chunk_len, "causal": w.causal, "self_mask": w.self_mask,
+                   "qk": ("gaussian mixture, %d clusters" % w.n_clusters) if w.n_clusters
+                   else "N(0,1)"},
+        "roofline": roof,
+        "kernels": kernels,
+        "hash_fallback_rows_per_step": int(f.fallback_rows.item()) // (args.warmup + args.steps),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w, inputs)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * lsh.h -- C ABI of the MI355X (gfx950) LSH-attention forward library,
+ * liblsh.so.
+ *
+ * The library computes the forward pass of Reformer's LSH attention (Kitaev,
+ * Kaiser, Levskaya, "Reformer: The Efficient Transformer", ICLR 2020) as four
+ * calls that follow the pipeline the Reformer study note
+ * (eightmm.github.io/papers/architectures/reformer) states in its section
+ * "Sorting and Chunking":
+ *
+ *     X --hash--> bucket ids --sort--> bucket-contiguous sequence
+ *       --chunked attention--> per-round outputs --unsort + combine--> Y
+ *
+ * Notation: batch b, heads H, sequence length L, head dim d, buckets B,
+ * rounds R, chunk length m.  A "segment" is one (batch, head, round) triple,
+ * numbered seg = (b_idx * H + h) * R + r.  x_i is the shared query/key vector
+ * of token i (Q = K, note section "Shared Query-Key Space"), v_i its value.
+ *
+ * Conventions shared by every call
+ *   - Every tensor is dense, row-major and lives in device memory owned by the
+ *     caller; the library never allocates device memory and keeps no state
+ *     between calls.  Device pointers must be 16-byte aligned.
+ *   - Every call is asynchronous: it validates its arguments on the host,
+ *     enqueues its kernels on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns.  The caller synchronises.
+ *   - Argument errors are detected on the host before anything is enqueued,
+ *     so an error leaves every output untouched.  A failed launch returns
+ *     LSH_ERR_HIP.  lsh_last_error() describes the last failure of the
+ *     calling thread.
+ *   - Supported shapes: head_dim == 64 and chunk_len == 64 (else
+ *     LSH_ERR_UNSUPPORTED); seq_len a multiple of chunk_len; n_buckets 1 or
+ *     even with 2 <= n_buckets <= 16384; 1 <= n_rounds <= 1024;
+ *     batch * heads * n_rounds * seq_len < 2^31.  A zero batch, heads or
+ *     seq_len is an empty problem: the call returns LSH_OK and does nothing.
+ *   - Inputs must be finite.
+ *   - Calls are thread-safe and may run concurrently on different streams.
+ */
+#ifndef LSH_H_
+#define LSH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LSH_OK = 0,
+  LSH_ERR_INVALID_ARGUMENT = 1,
+  LSH_ERR_UNSUPPORTED = 2,
+  LSH_ERR_WORKSPACE_TOO_SMALL = 3,
+  LSH_ERR_HIP = 4
+} lsh_status;
+
+typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype;
+
+typedef struct {
+  int32_t batch;     /* b */
+  int32_t heads;     /* H */
+  int32_t seq_len;   /* L */
+  int32_t head_dim;  /* d (64) */
+  int32_t n_buckets; /* B: 1 (no hashing, every token in bucket 0) or even */
+  int32_t n_rounds;  /* R: independent hash rounds */
+  int32_t chunk_len; /* m (64) */
+  int32_t causal;    /* 1: key j is masked for query i when j > i (original positions) */
+  int32_t self_mask; /* 1: a token is never its own key; if no round leaves it
+                        any key, its output is its own value */
+  int32_t dtype;     /* lsh_dtype of qk, v and rot */
+} lsh_config;
+
+/*
+ * lsh_hash -- angular LSH bucket of every token in every round.
+ * Follows: Reformer study note, section "LSH Attention" (a hash h(x) into B
+ * buckets under which similar vectors collide more often), realised as the
+ * random-rotation angular hash; "Multiple Hash Rounds" (R independent hashes).
+ *
+ *   qk       [b][H][L][d]      dtype  shared query/key vectors x
+ *   rot      [H][R][B/2][d]    dtype  rotation of head h, round r stored as
+ *                                     B/2 direction rows: rot[h][r][j][k] is
+ *                                     R_{h,r}[k][j].  May be NULL if B == 1.
+ *   buckets  [b][H][R][L]      int32  output, original token order
+ *   fallback_rows  optional device uint32 counter (NULL = not wanted).  The
+ *            call ADDS the number of (token, round) rows whose bucket it
+ *            decided by exact fp64 recomputation because the fast matrix-core
+ *            scores could not separate the two best candidates.
+ *
+ * bucket = the 0-based index of the largest entry of the B-vector
+ * [x R ; -(x R)], lowest index on ties, where x R is defined as the fp64 sum
+ * over k = 0..d-1 taken in that order.  The result equals that definition
+ * bit for bit: bf16 inputs are scored on the matrix cores with fp32
+ * accumulation and every row whose margin is within the proven rounding bound
+ * is recomputed in fp64 in the defining order; fp32 inputs are scored in fp64.
+ * B == 1: every bucket is 0.
+ */
+lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* rot,
+                    int32_t* buckets, uint32_t* fallback_rows, void* stream);
+
+/* Bytes of device workspace lsh_sort needs for cfg (0 for an empty problem). */
+size_t lsh_sort_workspace_bytes(const lsh_config* cfg);
+
+/*
+ * lsh_sort -- stable sort of every segment by bucket.
+ * Follows: Reformer study note, section "Sorting and Chunking" (tokens are
+ * sorted by hash bucket so that each bucket is contiguous).
+ *
+ *   buckets   [b][H][R][L] int32 in [0, B)     input (from lsh_hash)
+ *   perm      [b][H][R][L] int32               output: perm[seg][s] is the
+ *                                              original position at sorted slot s
+ *   inv_perm  [b][H][R][L] int32               output: inv_perm[seg][perm[seg][s]] = s
+ *   workspace device scratch of at least lsh_sort_workspace_bytes(cfg) bytes
+ *             (else LSH_ERR_WORKSPACE_TOO_SMALL); contents on entry ignored.
+ *
+ * Sorted order is by the unique key (bucket, original position), so the
+ * result is unique.  Bucket ids outside [0, B) are clamped into range (the
+ * outputs are then still permutations, but the order is unspecified).
+ */
+lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets,
+                    int32_t* perm, int32_t* inv_perm, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * lsh_chunk_attend -- attention inside chunks of the bucket-sorted sequence.
+ * Follows: Reformer study note, sections "LSH Attention" (candidate set
+ * N_LSH(i) = same-bucket keys; y_i = softmax-weighted sum of v_j over it with
+ * scores q_i.k_j / sqrt(d)), "Shared Query-Key Space" (Q = K), "Sorting and
+ * Chunking" (attention over chunks of nearby sorted positions) and
+ * "Implementation Reading" (causal masking by original position; same-token
+ * policy).
+ *
+ *   qk, v     [b][H][L][d]        dtype
+ *   buckets   [b][H][R][L]        int32, original order (from lsh_hash)
+ *   perm      [b][H][R][L]        int32 (from lsh_sort)
+ *   o_rounds  [b][H][R][L][d]     fp32 output, SORTED order
+ *   lse       [b][H][R][L]        fp32 output, SORTED order
+ *
+ * For the query i = perm[seg][s] of sorted chunk c = s / m, the window is the
+ * slots of chunks c-1 (if c > 0) and c.  Its keys are the tokens j of the
+ * window with bucket_j == bucket_i, j <= i if causal, and j != i if
+ * self_mask.  With s_ij = (x_i . x_j) / (max(|x_j|_2, 1e-6) * sqrt(d)):
+ *   lse[seg][s] = log sum_j exp(s_ij)           (-inf if there is no key)
+ *   o_rounds[seg][s] = sum_j exp(s_ij - lse) v_j  (0 if there is no key)
+ * bf16 inputs use bf16 matrix-core products with fp32 accumulation; fp32
+ * inputs use fp32 arithmetic.
+ */
+lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk,
+                            const void* v, const int32_t* buckets,
+                            const int32_t* perm, float* o_rounds, float* lse,
+                            void* stream);
+
+/*
+ * lsh_unsort_combine -- back to original order and combine the rounds.
+ * Follows: Reformer study note, section "Multiple Hash Rounds" (the
+ * neighbourhood of token i is the union over rounds of the per-round
+ * neighbourhoods), taken as a multiset: the rounds' softmaxes are merged with
+ * weights from their logsumexps.
+ *
+ *   o_rounds, lse   from lsh_chunk_attend (sorted order)
+ *   inv_perm        [b][H][R][L] int32 (from lsh_sort)
+ *   v               [b][H][L][d] dtype
+ *   y               [b][H][L][d] fp32 output, original order
+ *
+ * y_i = sum_r w_r o_r(i) with w_r = exp(lse_r(i) - M) / sum_r' exp(lse_r'(i) - M),
+ * M = max_r lse_r(i), where o_r(i), lse_r(i) are read at slot inv_perm[r][i].
+ * If every lse_r(i) is -inf (self-masked token with no other key), y_i = v_i.
+ */
+lsh_status lsh_unsort_combine(const lsh_config* cfg, const float* o_rounds,
+                              const float* lse, const int32_t* inv_perm,
+                              const void* v, float* y, void* stream);
+
+/* Static description of a status code. */
+const char* lsh_status_string(lsh_status status);
+
+/* Human-readable detail of the calling thread's last failed call ("" if none). */
+const char* lsh_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int lsh_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSH_H_ */

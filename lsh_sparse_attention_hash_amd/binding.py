@@ -1,0 +1,221 @@
+"""Thin ctypes binding of liblsh.so (the C ABI in include/lsh.h).
+
+Argument marshalling only: every function takes torch device tensors, checks
+that they have the dtype and shape the ABI documents, passes their data
+pointers and the current HIP stream to the library and raises LshError on a
+non-OK status.  All computation happens in the library's gfx950 kernels; there
+is no fallback of any kind.  If liblsh.so is missing the import of this module
+fails loudly (build it with ``python -m lsh_sparse_attention_hash_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblsh.so")
+
+LSH_OK = 0
+LSH_ERR_INVALID_ARGUMENT = 1
+LSH_ERR_UNSUPPORTED = 2
+LSH_ERR_WORKSPACE_TOO_SMALL = 3
+LSH_ERR_HIP = 4
+LSH_F32 = 0
+LSH_BF16 = 1
+
+EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attend",
+           "lsh_unsort_combine", "lsh_status_string", "lsh_last_error", "lsh_version")
+
+
+class LshError(RuntimeError):
+    def __init__(self, call: str, status: int, detail: str):
+        super().__init__(f"{call} failed with status {status}: {detail}")
+        self.status = status
+
+
+class LshConfig(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "heads", "seq_len", "head_dim", "n_buckets", "n_rounds", "chunk_len",
+        "causal", "self_mask", "dtype")]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m lsh_sparse_attention_hash_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(LshConfig)
+    lib.lsh_hash.argtypes = [cfgp, P, P, P, P, P]
+    lib.lsh_sort_workspace_bytes.argtypes = [cfgp]
+    lib.lsh_sort_workspace_bytes.restype = SZ
+    lib.lsh_sort.argtypes = [cfgp, P, P, P, P, SZ, P]
+    lib.lsh_chunk_attend.argtypes = [cfgp, P, P, P, P, P, P, P]
+    lib.lsh_unsort_combine.argtypes = [cfgp, P, P, P, P, P, P]
+    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine"):
+        getattr(lib, f).restype = I32
+    lib.lsh_status_string.argtypes = [I32]
+    lib.lsh_status_string.restype = ctypes.c_char_p
+    lib.lsh_last_error.argtypes = []
+    lib.lsh_last_error.restype = ctypes.c_char_p
+    lib.lsh_version.argtypes = []
+    lib.lsh_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = load_library()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def make_config(batch, heads, seq_len, n_buckets, n_rounds, causal, self_mask, dtype,
+                head_dim=64, chunk_len=64) -> LshConfig:
+    dt = {"bf16": LSH_BF16, "f32": LSH_F32}.get(dtype, dtype)
+    return LshConfig(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len,
+                     int(bool(causal)), int(bool(self_mask)), dt)
+
+
+def config_for(w) -> LshConfig:
+    """LshConfig of a synth.Workload."""
+    return make_config(w.batch, w.heads, w.seq_len, w.n_buckets, w.n_rounds, w.causal,
+                       w.self_mask, w.dtype, w.head_dim, w.chunk_len)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors passed to liblsh must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to liblsh must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_of(cfg: LshConfig):
+    return torch.bfloat16 if cfg.dtype == LSH_BF16 else torch.float32
+
+
+def _expect(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def _check(call, status):
+    if status != LSH_OK:
+        raise LshError(call, status, _lib.lsh_last_error().decode())
+
+
+def lsh_hash(cfg: LshConfig, qk, rot, buckets, fallback_rows=None, stream=None):
+    b, H, L, d, B, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_buckets, cfg.n_rounds
+    dt = _dtype_of(cfg)
+    _expect(qk, (b, H, L, d), dt, "qk")
+    if B > 1:
+        _expect(rot, (H, R, B // 2, d), dt, "rot")
+    _expect(buckets, (b, H, R, L), torch.int32, "buckets")
+    if fallback_rows is not None:
+        _expect(fallback_rows, (1,), torch.int32, "fallback_rows")
+    _check("lsh_hash", _lib.lsh_hash(ctypes.byref(cfg), _ptr(qk), _ptr(rot) if B > 1 else None,
+                                     _ptr(buckets), _ptr(fallback_rows), _stream(stream)))
+
+
+def lsh_sort_workspace_bytes(cfg: LshConfig) -> int:
+    return int(_lib.lsh_sort_workspace_bytes(ctypes.byref(cfg)))
+
+
+def lsh_sort(cfg: LshConfig, buckets, perm, inv_perm, workspace, stream=None):
+    shape = (cfg.batch, cfg.heads, cfg.n_rounds, cfg.seq_len)
+    for t, n in ((buckets, "buckets"), (perm, "perm"), (inv_perm, "inv_perm")):
+        _expect(t, shape, torch.int32, n)
+    _check("lsh_sort", _lib.lsh_sort(ctypes.byref(cfg), _ptr(buckets), _ptr(perm), _ptr(inv_perm),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+
+
+def lsh_chunk_attend(cfg: LshConfig, qk, v, buckets, perm, o_rounds, lse, stream=None):
+    b, H, L, d, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_rounds
+    dt = _dtype_of(cfg)
+    _expect(qk, (b, H, L, d), dt, "qk")
+    _expect(v, (b, H, L, d), dt, "v")
+    _expect(buckets, (b, H, R, L), torch.int32, "buckets")
+    _expect(perm, (b, H, R, L), torch.int32, "perm")
+    _expect(o_rounds, (b, H, R, L, d), torch.float32, "o_rounds")
+    _expect(lse, (b, H, R, L), torch.float32, "lse")
+    _check("lsh_chunk_attend",
+           _lib.lsh_chunk_attend(ctypes.byref(cfg), _ptr(qk), _ptr(v), _ptr(buckets), _ptr(perm),
+                                 _ptr(o_rounds), _ptr(lse), _stream(stream)))
+
+
+def lsh_unsort_combine(cfg: LshConfig, o_rounds, lse, inv_perm, v, y, stream=None):
+    b, H, L, d, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_rounds
+    _expect(o_rounds, (b, H, R, L, d), torch.float32, "o_rounds")
+    _expect(lse, (b, H, R, L), torch.float32, "lse")
+    _expect(inv_perm, (b, H, R, L), torch.int32, "inv_perm")
+    _expect(v, (b, H, L, d), _dtype_of(cfg), "v")
+    _expect(y, (b, H, L, d), torch.float32, "y")
+    _check("lsh_unsort_combine",
+           _lib.lsh_unsort_combine(ctypes.byref(cfg), _ptr(o_rounds), _ptr(lse), _ptr(inv_perm),
+                                   _ptr(v), _ptr(y), _stream(stream)))
+
+
+class Forward:
+    """Device buffers for one problem size plus the four calls in order.
+
+    Allocation happens here (torch device memory), never inside the calls;
+    ``run`` enqueues hash -> sort -> chunk attention -> unsort + combine on the
+    current stream (or ``stream``).
+    """
+
+    def __init__(self, cfg: LshConfig, device="cuda"):
+        b, H, L, d, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_rounds
+        self.cfg = cfg
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.buckets = torch.empty((b, H, R, L), **i32)
+        self.perm = torch.empty((b, H, R, L), **i32)
+        self.inv_perm = torch.empty((b, H, R, L), **i32)
+        self.o_rounds = torch.empty((b, H, R, L, d), **f32)
+        self.lse = torch.empty((b, H, R, L), **f32)
+        self.y = torch.empty((b, H, L, d), **f32)
+        nbytes = max(16, lsh_sort_workspace_bytes(cfg))
+        self.workspace = torch.empty(((nbytes + 15) // 16) * 16, dtype=torch.uint8, device=device)
+        self.fallback_rows = torch.zeros(1, **i32)
+
+    def hash(self, qk, rot, stream=None):
+        lsh_hash(self.cfg, qk, rot, self.buckets, self.fallback_rows, stream)
+
+    def sort(self, stream=None):
+        lsh_sort(self.cfg, self.buckets, self.perm, self.inv_perm, self.workspace, stream)
+
+    def attend(self, qk, v, stream=None):
+        lsh_chunk_attend(self.cfg, qk, v, self.buckets, self.perm, self.o_rounds, self.lse, stream)
+
+    def combine(self, v, stream=None):
+        lsh_unsort_combine(self.cfg, self.o_rounds, self.lse, self.inv_perm, v, self.y, stream)
+
+    def run(self, qk, v, rot, stream=None):
+        self.hash(qk, rot, stream)
+        self.sort(stream)
+        self.attend(qk, v, stream)
+        self.combine(v, stream)
+        return self.y
+
+
+def to_device(stored, dtype: str, device="cuda"):
+    """numpy storage from synth (uint16 bf16 bits or float32) -> device tensor."""
+    import numpy as np
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(stored).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(stored, dtype=np.float32))
+    return t.to(device)

@@ -1,0 +1,332 @@
+// attend.hip -- attention inside chunks of the bucket-sorted sequence
+// (Reformer study note: "LSH Attention" -- same-bucket candidates and the
+// softmax-weighted value sum with scores q.k / sqrt(d); "Shared Query-Key
+// Space" -- Q = K with unit-length keys; "Sorting and Chunking" -- attention
+// over chunks of nearby sorted positions; "Implementation Reading" -- causal
+// masking by original position and the same-token policy).
+//
+// For sorted chunk c of a segment the window is chunks c-1 and c (128 keys);
+// the 64 queries are chunk c.  One workgroup (4 waves, 16 queries each) walks
+// a run of consecutive chunks: chunk c's rows stay in LDS as chunk c+1's
+// predecessor, so each row is gathered from HBM once per round.
+//
+// bf16: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 (fp32
+// accumulation).  The S^T layout puts one query per lane column, so the
+// P^T fragments of two score tiles are directly the B operand of the PV
+// product (the contraction over keys is permuted consistently in A and B).
+// V is stored transposed in LDS while it is staged.
+// fp32: one thread per query, fp32 arithmetic with an online softmax.
+#include <math.h>
+
+#include "lsh_device.h"
+#include "lsh_launch.h"
+
+namespace lsh {
+
+constexpr int kXStride = 72;    // bf16 per x row in LDS (64 + 8 pad: 144 B)
+constexpr int kVStride = 136;   // bf16 per V^T row in LDS (128 keys + 8 pad: 272 B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNormEps = 1e-6f;
+
+struct AttendArgs {
+  const void* qk;
+  const void* v;
+  const int32_t* buckets;
+  const int32_t* perm;
+  float* o;
+  float* lse;
+  int rounds, L, nchunks, cpw, runs_per_seg, causal, self_mask;
+};
+
+// ------------------------------------------------------------------- bf16
+struct AttendLds {
+  uint16_t xs[128 * kXStride];
+  uint16_t vt[kHeadDim * kVStride];
+  float kinv[128];     // log2(e) / (max(|x_j|, eps) * sqrt(d))
+  int32_t kbk[128];    // bucket of the key
+  int32_t kpos[128];   // original position of the key
+};
+
+// Gather sorted chunk c (64 rows of x and v) into LDS half (c & 1).
+__device__ __forceinline__ void stage_chunk_bf16(AttendLds& sm, const uint16_t* xb,
+                                                 const uint16_t* vb, const int32_t* bk,
+                                                 const int32_t* pm, int c, int L) {
+  const int tid = threadIdx.x;
+  const int p = tid >> 3;          // key pair 0..31
+  const int dblk = tid & 7;        // 16-byte column block
+  const int row = 64 * (c & 1) + 2 * p;
+  int2 pos = *reinterpret_cast<const int2*>(pm + (size_t)c * kChunk + 2 * p);
+  pos.x = clamp_index(pos.x, L);
+  pos.y = clamp_index(pos.y, L);
+  const uint4 xa = load16(xb + (size_t)pos.x * kHeadDim + 8 * dblk);
+  const uint4 xc = load16(xb + (size_t)pos.y * kHeadDim + 8 * dblk);
+  const uint4 va = load16(vb + (size_t)pos.x * kHeadDim + 8 * dblk);
+  const uint4 vc = load16(vb + (size_t)pos.y * kHeadDim + 8 * dblk);
+  store16(&sm.xs[row * kXStride + 8 * dblk], xa);
+  store16(&sm.xs[(row + 1) * kXStride + 8 * dblk], xc);
+  const uint32_t wa[4] = {va.x, va.y, va.z, va.w};
+  const uint32_t wc[4] = {vc.x, vc.y, vc.z, vc.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t even = (wa[e] & 0xffffu) | (wc[e] << 16);
+    const uint32_t odd = (wa[e] >> 16) | (wc[e] & 0xffff0000u);
+    *reinterpret_cast<uint32_t*>(&sm.vt[(8 * dblk + 2 * e) * kVStride + row]) = even;
+    *reinterpret_cast<uint32_t*>(&sm.vt[(8 * dblk + 2 * e + 1) * kVStride + row]) = odd;
+  }
+  const uint32_t ua[4] = {xa.x, xa.y, xa.z, xa.w};
+  const uint32_t uc[4] = {xc.x, xc.y, xc.z, xc.w};
+  float sa = 0.f, sc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = bf16lo(ua[e]), a1 = bf16hi(ua[e]);
+    const float c0 = bf16lo(uc[e]), c1 = bf16hi(uc[e]);
+    sa += a0 * a0 + a1 * a1;
+    sc += c0 * c0 + c1 * c1;
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    sa += __shfl_xor(sa, off);
+    sc += __shfl_xor(sc, off);
+  }
+  if (dblk == 0) {
+    sm.kinv[row] = kLog2e / (fmaxf(sqrtf(sa), kNormEps) * 8.0f);
+    sm.kinv[row + 1] = kLog2e / (fmaxf(sqrtf(sc), kNormEps) * 8.0f);
+    sm.kbk[row] = bk[pos.x];
+    sm.kbk[row + 1] = bk[pos.y];
+    sm.kpos[row] = pos.x;
+    sm.kpos[row + 1] = pos.y;
+  }
+}
+
+__device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArgs& a, int64_t seg,
+                                                  int c) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;          // 16-lane group
+  const int ql = lane & 15;         // query column of this lane
+  const int hq = c & 1, hp = hq ^ 1;
+  const int qrow = 64 * hq + 16 * wave + ql;
+  const int tfirst = (c == 0) ? 4 : 0;   // chunk 0 has no predecessor
+
+  // B operand: Q^T (d x query), lane holds x_q[8*g + 32*ks .. +7]
+  bf16x8 qf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) qf[ks] = as_bf16x8(load16(&sm.xs[qrow * kXStride + 8 * g + 32 * ks]));
+  const int qb = sm.kbk[qrow];
+  const int qp = sm.kpos[qrow];
+
+  // scores, log2-scaled: s[t][i] is key 16t + 4g + i of the window for query ql
+  float s[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if (t < tfirst) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[t][i] = -INFINITY;
+      continue;
+    }
+    const int krow = (16 * t + ql + 64 * hp) & 127;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 kf = as_bf16x8(load16(&sm.xs[krow * kXStride + 8 * g + 32 * ks]));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+    }
+    const int row4 = (16 * t + 4 * g + 64 * hp) & 127;
+    const float4 kv = *reinterpret_cast<const float4*>(&sm.kinv[row4]);
+    const int4 kb = *reinterpret_cast<const int4*>(&sm.kbk[row4]);
+    const int4 kp = *reinterpret_cast<const int4*>(&sm.kpos[row4]);
+    const float kva[4] = {kv.x, kv.y, kv.z, kv.w};
+    const int kba[4] = {kb.x, kb.y, kb.z, kb.w};
+    const int kpa[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = kba[i] == qb && (!a.causal || kpa[i] <= qp) && (!a.self_mask || kpa[i] != qp);
+      s[t][i] = ok ? acc[i] * kva[i] : -INFINITY;
+    }
+  }
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float msafe = (mx == -INFINITY) ? 0.f : mx;
+
+  // probabilities rounded to bf16 (the PV operand); the denominator sums the
+  // same rounded values so the weights of a row add up to one
+  uint32_t pw[8][2];
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const uint32_t w = pack_bf16x2(exp2f(s[t][i] - msafe), exp2f(s[t][i + 1] - msafe));
+      pw[t][i >> 1] = w;
+      sum += bf16lo(w) + bf16hi(w);
+    }
+  }
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+
+  const int kfirst = (c == 0) ? 2 : 0;
+  f32x4 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k2 = 0; k2 < 4; ++k2) {
+    if (k2 < kfirst) continue;
+    // MFMA contraction index 8g + j <-> window key 32*k2 + 16*(j/4) + 4g + j%4
+    const bf16x8 pb = __builtin_bit_cast(
+        bf16x8, make_uint4(pw[2 * k2][0], pw[2 * k2][1], pw[2 * k2 + 1][0], pw[2 * k2 + 1][1]));
+    const int c0 = (32 * k2 + 4 * g + 64 * hp) & 127;
+    const int c1 = (32 * k2 + 16 + 4 * g + 64 * hp) & 127;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint16_t* vrow = &sm.vt[(16 * dt + ql) * kVStride];
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + c0);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + c1);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, oacc[dt], 0, 0, 0);
+    }
+  }
+
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  const int64_t slot = (int64_t)c * kChunk + 16 * wave + ql;
+  float* orow = a.o + ((int64_t)seg * a.L + slot) * kHeadDim;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const float4 val = make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
+                                   oacc[dt][3] * inv);
+    *reinterpret_cast<float4*>(orow + 16 * dt + 4 * g) = val;
+  }
+  if (g == 0)
+    a.lse[(int64_t)seg * a.L + slot] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
+}
+
+__global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) AttendLds sm;
+  const int64_t seg = blockIdx.x / a.runs_per_seg;
+  const int run = blockIdx.x % a.runs_per_seg;
+  const int c0 = run * a.cpw;
+  const int c1 = min(a.nchunks, c0 + a.cpw);
+  const int64_t bh = seg / a.rounds;
+  const uint16_t* xb = static_cast<const uint16_t*>(a.qk) + bh * (int64_t)a.L * kHeadDim;
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.L * kHeadDim;
+  const int32_t* bk = a.buckets + seg * a.L;
+  const int32_t* pm = a.perm + seg * a.L;
+  if (c0 > 0) stage_chunk_bf16(sm, xb, vb, bk, pm, c0 - 1, a.L);
+  for (int c = c0; c < c1; ++c) {
+    stage_chunk_bf16(sm, xb, vb, bk, pm, c, a.L);
+    __syncthreads();
+    attend_chunk_bf16(sm, a, seg, c);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------- fp32
+// One wave per chunk; lane q is query q of the chunk.  The window is staged
+// one chunk (64 keys) at a time; the softmax runs online in fp32.
+__global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
+  __shared__ float xw[kChunk][kHeadDim];
+  __shared__ float vw[kChunk][kHeadDim];
+  __shared__ float kinv[kChunk];
+  __shared__ int32_t kbk[kChunk], kpos[kChunk];
+  const int lane = lane_id();
+  const int64_t seg = blockIdx.x / a.nchunks;
+  const int c = blockIdx.x % a.nchunks;
+  const int64_t bh = seg / a.rounds;
+  const float* xb = static_cast<const float*>(a.qk) + bh * (int64_t)a.L * kHeadDim;
+  const float* vb = static_cast<const float*>(a.v) + bh * (int64_t)a.L * kHeadDim;
+  const int32_t* bk = a.buckets + seg * a.L;
+  const int32_t* pm = a.perm + seg * a.L;
+
+  const int qp = clamp_index(pm[(int64_t)c * kChunk + lane], a.L);
+  const int qb = bk[qp];
+  float xq[kHeadDim];
+#pragma unroll
+  for (int k = 0; k < kHeadDim; ++k) xq[k] = xb[(int64_t)qp * kHeadDim + k];
+  float m = -INFINITY, l = 0.f, o[kHeadDim];
+#pragma unroll
+  for (int k = 0; k < kHeadDim; ++k) o[k] = 0.f;
+
+  for (int cc = (c == 0 ? 0 : c - 1); cc <= c; ++cc) {
+    __syncthreads();
+    const int pos = clamp_index(pm[(int64_t)cc * kChunk + lane], a.L);
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kHeadDim; ++k) {
+      const float xv = xb[(int64_t)pos * kHeadDim + k];
+      xw[lane][k] = xv;
+      vw[lane][k] = vb[(int64_t)pos * kHeadDim + k];
+      ss += xv * xv;
+    }
+    kinv[lane] = 1.0f / (fmaxf(sqrtf(ss), kNormEps) * 8.0f);
+    kbk[lane] = bk[pos];
+    kpos[lane] = pos;
+    __syncthreads();
+    for (int kk = 0; kk < kChunk; ++kk) {
+      if (kbk[kk] != qb || (a.causal && kpos[kk] > qp) || (a.self_mask && kpos[kk] == qp)) continue;
+      float dot = 0.f;
+#pragma unroll
+      for (int k = 0; k < kHeadDim; ++k) dot = fmaf(xq[k], xw[kk][k], dot);
+      const float sc = dot * kinv[kk];
+      if (sc > m) {
+        const float f = expf(m - sc);
+        l *= f;
+#pragma unroll
+        for (int k = 0; k < kHeadDim; ++k) o[k] *= f;
+        m = sc;
+      }
+      const float p = expf(sc - m);
+      l += p;
+#pragma unroll
+      for (int k = 0; k < kHeadDim; ++k) o[k] = fmaf(p, vw[kk][k], o[k]);
+    }
+  }
+  const int64_t slot = (int64_t)c * kChunk + lane;
+  float* orow = a.o + (seg * a.L + slot) * kHeadDim;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int k = 0; k < kHeadDim; k += 4)
+    *reinterpret_cast<float4*>(orow + k) =
+        make_float4(o[k] * inv, o[k + 1] * inv, o[k + 2] * inv, o[k + 3] * inv);
+  a.lse[seg * a.L + slot] = (m == -INFINITY) ? -INFINITY : m + logf(l);
+}
+
+hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const int32_t* buckets,
+                         const int32_t* perm, float* o_rounds, float* lse, hipStream_t stream) {
+  AttendArgs a;
+  a.qk = qk;
+  a.v = v;
+  a.buckets = buckets;
+  a.perm = perm;
+  a.o = o_rounds;
+  a.lse = lse;
+  a.rounds = s.rounds;
+  a.L = s.len;
+  a.nchunks = s.len / kChunk;
+  a.causal = s.causal;
+  a.self_mask = s.self_mask;
+  const int64_t S = s.segments();
+  if (!s.bf16) {
+    a.cpw = 1;
+    a.runs_per_seg = a.nchunks;
+    hipLaunchKernelGGL(attend_f32_kernel, dim3((unsigned)(S * a.nchunks)), dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
+  // runs of consecutive chunks per workgroup: long runs re-gather fewer
+  // predecessor chunks; keep at least ~2048 workgroups in flight
+  const int64_t total = S * a.nchunks;
+  int cpw = (int)(total / 2048);
+  cpw = cpw < 1 ? 1 : (cpw > 16 ? 16 : cpw);
+  a.cpw = cpw;
+  a.runs_per_seg = (a.nchunks + cpw - 1) / cpw;
+  hipLaunchKernelGGL(attend_bf16_kernel, dim3((unsigned)(S * a.runs_per_seg)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

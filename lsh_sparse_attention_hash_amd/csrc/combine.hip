@@ -1,0 +1,84 @@
+// combine.hip -- unsort and combine the hash rounds (Reformer study note,
+// section "Multiple Hash Rounds": the neighbourhood of a token is the union of
+// its per-round neighbourhoods).  Taken as a multiset, the softmax over the
+// union is the rounds' softmaxes merged with weights exp(lse_r - M) / sum.
+//
+// 16 lanes per token (4 floats of the 64-wide row each); a 256-thread
+// workgroup covers 16 consecutive tokens of one (batch, head), so y is written
+// with full 256-byte rows while the per-round rows are gathered through
+// inv_perm.
+#include <math.h>
+
+#include "lsh_device.h"
+#include "lsh_launch.h"
+
+namespace lsh {
+
+template <typename T>
+__device__ __forceinline__ float4 load_v4(const T* row, int c4);
+template <>
+__device__ __forceinline__ float4 load_v4<uint16_t>(const uint16_t* row, int c4) {
+  const uint2 u = *reinterpret_cast<const uint2*>(row + c4);
+  return make_float4(bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y));
+}
+template <>
+__device__ __forceinline__ float4 load_v4<float>(const float* row, int c4) {
+  return *reinterpret_cast<const float4*>(row + c4);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_rounds,
+                                                      const float* __restrict__ lse,
+                                                      const int32_t* __restrict__ inv_perm,
+                                                      const T* __restrict__ v, float* __restrict__ y,
+                                                      int rounds, int L, int64_t total) {
+  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (tok >= total) return;
+  const int c4 = (threadIdx.x & 15) * 4;
+  const int64_t bh = tok / L;
+  const int i = (int)(tok % L);
+  const int64_t seg0 = bh * rounds;
+
+  float mx = -INFINITY;
+  for (int r = 0; r < rounds; ++r) {
+    const int64_t seg = seg0 + r;
+    const int slot = clamp_index(inv_perm[seg * L + i], L);
+    mx = fmaxf(mx, lse[seg * L + slot]);
+  }
+  float4 out;
+  if (mx == -INFINITY) {
+    out = load_v4<T>(v + tok * kHeadDim, c4);
+  } else {
+    float ws = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < rounds; ++r) {
+      const int64_t seg = seg0 + r;
+      const int64_t row = seg * L + clamp_index(inv_perm[seg * L + i], L);
+      const float w = expf(lse[row] - mx);
+      const float4 o = *reinterpret_cast<const float4*>(o_rounds + row * kHeadDim + c4);
+      ws += w;
+      acc.x = fmaf(w, o.x, acc.x);
+      acc.y = fmaf(w, o.y, acc.y);
+      acc.z = fmaf(w, o.z, acc.z);
+      acc.w = fmaf(w, o.w, acc.w);
+    }
+    const float inv = 1.0f / ws;
+    out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  *reinterpret_cast<float4*>(y + tok * kHeadDim + c4) = out;
+}
+
+hipError_t launch_combine(const Shape& s, const float* o_rounds, const float* lse,
+                          const int32_t* inv_perm, const void* v, float* y, hipStream_t stream) {
+  const int64_t total = s.token_heads();
+  const dim3 grid((unsigned)((total + 15) / 16));
+  if (s.bf16)
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, stream, o_rounds, lse,
+                       inv_perm, static_cast<const uint16_t*>(v), y, s.rounds, s.len, total);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream, o_rounds, lse, inv_perm,
+                       static_cast<const float*>(v), y, s.rounds, s.len, total);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

@@ -1,0 +1,280 @@
+// hash.hip -- angular LSH bucket ids (Reformer study note, section "LSH
+// Attention": a hash h(x) into B buckets; here the random-rotation hash
+// bucket = first argmax of [x R ; -x R]) for every token and round.
+//
+// bf16 inputs: x R is contracted on the matrix cores (v_mfma_f32_32x32x16_bf16,
+// exact bf16 products, fp32 accumulation).  The epilogue keeps, per token, the
+// two largest |x R_j| as packed keys (magnitude bits with the direction index
+// in the low mantissa bits) and the largest signed key.  A row is accepted
+// only when the gap between the two best candidates exceeds twice a proven
+// bound on the fp32 accumulation error (plus the fp64 rounding of the defining
+// sum), so that its bucket is provably the one of the fp64 definition.  Other
+// rows are recomputed by one wave in fp64 in the defining order.
+// fp32 inputs are scored in fp64 directly (the same wave routine).
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+
+#include "lsh_device.h"
+#include "lsh_launch.h"
+
+namespace lsh {
+
+constexpr int kHashWaves = 4;
+constexpr int kHashTokWave = 64;                       // two 32-token MFMA column blocks
+constexpr int kHashTokWG = kHashWaves * kHashTokWave;  // 256 tokens per workgroup
+constexpr int kStageRows = 128;                        // rotation rows staged per LDS pass
+constexpr int kRowStride = 72;                         // bf16 per staged row (144 B, padded)
+
+// ---------------------------------------------------------------------------
+// Exact bucket of one token, computed by one wave in the defining arithmetic:
+// s_j = sum_{k=0..63} x_k R[k][j] in fp64, k ascending from 0.0 (each product
+// of two bf16/fp32 values is exact in fp64, so fused or separate multiply-add
+// give the same result); candidates +s_j at index j and -s_j at j + half; the
+// first (lowest-index) maximum wins.  x: 64 doubles in LDS.
+template <typename T>
+__device__ __forceinline__ double rot_elem(const T* row, int k);
+template <>
+__device__ __forceinline__ double rot_elem<uint16_t>(const uint16_t* row, int k) {
+  return (double)bf16_to_f32(row[k]);
+}
+template <>
+__device__ __forceinline__ double rot_elem<float>(const float* row, int k) {
+  return (double)row[k];
+}
+
+template <typename T>
+__device__ int exact_bucket(const double* x, const T* rot_hr, int half) {
+  const int lane = lane_id();
+  double best = -INFINITY;
+  int besti = INT_MAX;
+  for (int j = lane; j < half; j += kWave) {
+    const T* row = rot_hr + (size_t)j * kHeadDim;
+    double acc = 0.0;
+#pragma unroll 8
+    for (int k = 0; k < kHeadDim; ++k) acc = acc + x[k] * rot_elem<T>(row, k);
+    // Visit order is not index order (-s_j at j + half comes before +s_{j+64}),
+    // so equal values are resolved by index explicitly.
+    if (acc > best || (acc == best && j < besti)) { best = acc; besti = j; }
+    if (-acc > best || (-acc == best && j + half < besti)) { best = -acc; besti = j + half; }
+  }
+  // lane-ordered merge: larger value wins, lower index on equal values
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double ob = __shfl_xor(best, off);
+    const int oi = __shfl_xor(besti, off);
+    if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
+  }
+  return besti;
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void hash_bf16_kernel(
+    const uint16_t* __restrict__ qk, const uint16_t* __restrict__ rot,
+    int32_t* __restrict__ buckets, uint32_t* __restrict__ fallback_rows, int heads, int L,
+    int half, int rounds, int ib) {
+  __shared__ __attribute__((aligned(16))) uint16_t rs[kStageRows * kRowStride];
+  __shared__ float gram_part[kHashWaves];
+  __shared__ double xfb[kHashWaves][kHeadDim];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  const size_t bh = (size_t)blockIdx.z * heads + h;
+  const int tok_wave = blockIdx.x * kHashTokWG + wave * kHashTokWave;
+  const uint16_t* xbase = qk + bh * (size_t)L * kHeadDim;
+
+  // B operand (x^T, k x token): lane holds x[token = lane%32][k = 8*(lane/32) + 16*ks + 0..7].
+  bf16x8 xf[2][4];
+  float xnorm[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int tok = tok_wave + nb * 32 + (lane & 31);
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (tok < L) u = load16(xbase + (size_t)tok * kHeadDim + 8 * (lane >> 5) + 16 * ks);
+      xf[nb][ks] = as_bf16x8(u);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16lo(w[e]), b = bf16hi(w[e]);
+        ss += a * a + b * b;
+      }
+    }
+    ss += __shfl_xor(ss, 32);
+    xnorm[nb] = sqrtf(ss);
+  }
+
+  const uint32_t idxmask = (1u << ib) - 1u;
+  const uint32_t keymask = ~idxmask;
+  const int nstages = (half + kStageRows - 1) / kStageRows;
+
+  for (int r = 0; r < rounds; ++r) {
+    const uint16_t* rhr = rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim;
+    float m1[2] = {0.f, 0.f}, m2[2] = {0.f, 0.f}, smax[2] = {-INFINITY, -INFINITY};
+    float gmax = 0.f;
+
+    for (int st = 0; st < nstages; ++st) {
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = threadIdx.x + 256 * q;
+        const int row = c >> 3, col = (c & 7) * 8;
+        const int j = st * kStageRows + row;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (j < half) u = load16(rhr + (size_t)j * kHeadDim + col);
+        store16(&rs[row * kRowStride + col], u);
+      }
+      __syncthreads();
+
+#pragma unroll
+      for (int t = 0; t < kStageRows / 32; ++t) {
+        const int jt = st * kStageRows + t * 32;
+        if (jt >= half) break;
+        // A operand (R^T, direction x k): lane holds R[k = 8*(lane/32)+16*ks..][j = jt + lane%32].
+        bf16x8 a[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          a[ks] = as_bf16x8(load16(&rs[(t * 32 + (lane & 31)) * kRowStride + 8 * (lane >> 5) + 16 * ks]));
+
+        if (((st * 4 + t) & (kHashWaves - 1)) == wave) {
+          // Gram block R_tile^T R_tile: its largest entry is the largest squared
+          // direction norm of the tile (off-diagonal entries never exceed it).
+          f32x16 g = {};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], a[ks], g, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) gmax = fmaxf(gmax, g[i]);
+        }
+
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], xf[nb][ks], acc, 0, 0, 0);
+          // Output layout: register i of lane l is direction jt + 8*(i/4) + 4*(l/32) + i%4
+          // for token l%32.  The key carries jt + 8*(i/4) + i%4; the lane-half bit (4)
+          // is restored after the two halves merge.
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const uint32_t ja = (uint32_t)(jt + 8 * (i >> 2) + (i & 3));
+            const float ka = __uint_as_float((__float_as_uint(acc[i]) & keymask) | ja);
+            const float kb = __uint_as_float((__float_as_uint(acc[i + 1]) & keymask) | (ja + 1));
+            smax[nb] = fmaxf(smax[nb], fmaxf(ka, kb));
+            const float aa = fabsf(ka), ab = fabsf(kb);
+            const float n1 = fmaxf(m1[nb], fmaxf(aa, ab));
+            m2[nb] = fmaxf(m2[nb], __builtin_amdgcn_fmed3f(m1[nb], aa, ab));
+            m1[nb] = n1;
+          }
+        }
+      }
+    }
+
+    // Largest direction norm of this rotation (all waves' Gram tiles).
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off));
+    if (lane == 0) gram_part[wave] = gmax;
+    __syncthreads();
+    float g2 = gram_part[0];
+#pragma unroll
+    for (int w = 1; w < kHashWaves; ++w) g2 = fmaxf(g2, gram_part[w]);
+    const float rcol = sqrtf(g2 * (1.0f + 0x1p-10f));
+
+    int32_t* bout = buckets + (bh * rounds + r) * (size_t)L;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float pm1 = __shfl_xor(m1[nb], 32);
+      const float pm2 = __shfl_xor(m2[nb], 32);
+      const int own_pos = __float_as_uint(smax[nb]) == __float_as_uint(m1[nb]);
+      const int other_pos = __shfl_xor(own_pos, 32);
+      const bool other = pm1 > m1[nb];
+      const float w1 = other ? pm1 : m1[nb];
+      const float w2 = fmaxf(fminf(m1[nb], pm1), fmaxf(m2[nb], pm2));
+      const int half_id = (other ? (lane ^ 32) : lane) >> 5;
+      const uint32_t jstar = (__float_as_uint(w1) & idxmask) | ((uint32_t)half_id << 2);
+      const bool pos = other ? other_pos : own_pos;
+      const float lower1 = __uint_as_float(__float_as_uint(w1) & keymask);
+      const float upper2 = __uint_as_float((__float_as_uint(w2) & keymask) + (1u << ib));
+      // |fp32 MFMA score - exact| <= 64 * 2^-23 * sum_k |x_k R_kj| <= 64 * 2^-23 |x| |R_j|;
+      // doubled to cover the fp64 rounding of the definition, plus flush-to-zero slack.
+      const float E = xnorm[nb] * rcol * (64.0f * 0x1p-22f * 1.01f) +
+                      (xnorm[nb] + rcol) * 0x1p-120f + 0x1p-118f;
+      const bool cert = (lower1 - upper2 > 2.0f * E + lower1 * 0x1p-20f) && (jstar < (uint32_t)half);
+      const int bucket = pos ? (int)jstar : (int)jstar + half;
+
+      const int tok = tok_wave + nb * 32 + (lane & 31);
+      const bool mine = lane < 32 && tok < L;
+      if (mine && cert) bout[tok] = bucket;
+      uint64_t need = __ballot(mine && !cert);
+      if (fallback_rows && lane == 0 && need) atomicAdd(fallback_rows, (uint32_t)__popcll(need));
+      while (need) {
+        const int q = __ffsll((unsigned long long)need) - 1;
+        need &= need - 1;
+        const int ftok = tok_wave + nb * 32 + q;
+        xfb[wave][lane] = (double)bf16_to_f32(xbase[(size_t)ftok * kHeadDim + lane]);
+        __builtin_amdgcn_wave_barrier();
+        const int bk = exact_bucket<uint16_t>(xfb[wave], rhr, half);
+        if (lane == 0) bout[ftok] = bk;
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+}
+
+// fp32 inputs: every row in fp64 (one wave per (token, round) row).
+__global__ __launch_bounds__(256) void hash_exact_f32_kernel(
+    const float* __restrict__ qk, const float* __restrict__ rot, int32_t* __restrict__ buckets,
+    int heads, int L, int half, int rounds, int64_t rows) {
+  __shared__ double xs[4][kHeadDim];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  // row indexes buckets[b][H][R][L]
+  const int i = (int)(row % L);
+  const int64_t seg = row / L;
+  const int r = (int)(seg % rounds);
+  const int64_t bh = seg / rounds;
+  const int h = (int)(bh % heads);
+  xs[wave][lane] = (double)qk[(bh * L + i) * kHeadDim + lane];
+  __builtin_amdgcn_wave_barrier();
+  const int bk = exact_bucket<float>(xs[wave], rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim,
+                                     half);
+  if (lane == 0) buckets[row] = bk;
+}
+
+__global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t* buckets,
+                       uint32_t* fallback_rows, hipStream_t stream) {
+  const int64_t rows = s.segments() * s.len;
+  if (s.buckets == 1) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       stream, buckets, rows);
+    return hipGetLastError();
+  }
+  const int half = s.buckets / 2;
+  if (!s.bf16) {
+    hipLaunchKernelGGL(hash_exact_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                       stream, static_cast<const float*>(qk), static_cast<const float*>(rot),
+                       buckets, s.heads, s.len, half, s.rounds, rows);
+    return hipGetLastError();
+  }
+  int ib = 5;
+  while ((1 << ib) < half) ++ib;
+  const dim3 grid((unsigned)((s.len + kHashTokWG - 1) / kHashTokWG), (unsigned)s.heads,
+                  (unsigned)s.batch);
+  hipLaunchKernelGGL(hash_bf16_kernel, grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
+                     fallback_rows, s.heads, s.len, half, s.rounds, ib);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

@@ -1,0 +1,50 @@
+// lsh_device.h -- types and helpers shared by the gfx950 kernels of liblsh.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsh {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kHeadDim = 64;   // d
+constexpr int kChunk = 64;     // m
+constexpr int kWave = 64;      // CDNA wavefront
+
+// 16-byte global/LDS load and store through uint4.
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// bf16 halves of a packed dword -> fp32 (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 pair -> packed bf16 pair, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a = (a + 0x7fffu + ((a >> 16) & 1u)) >> 16;
+  b = (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
+  return a | b;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Index read from caller memory, forced into [0, n) so that no input can make
+// a kernel access memory outside its buffers.
+__device__ __forceinline__ int clamp_index(int i, int n) { return min(max(i, 0), n - 1); }
+
+}  // namespace lsh

@@ -1,0 +1,176 @@
+// sort.hip -- stable counting sort of every (batch, head, round) segment by
+// bucket id (Reformer study note, section "Sorting and Chunking": tokens are
+// sorted by hash bucket so each bucket becomes contiguous).  Because positions
+// enter in increasing order and the scatter is stable, the result is the
+// order of the unique key (bucket, original position).
+//
+// Four launches per call:
+//   count    one workgroup per (segment, tile): LDS histogram of the tile
+//   scan_t   one thread per (segment, bucket): exclusive prefix over tiles
+//   scan_b   one workgroup per segment: exclusive prefix over bucket totals
+//   scatter  one wave per (segment, tile): walks the tile in order, 64 keys
+//            at a time; equal keys inside a batch are ranked with ballots
+//            (match over the key bits), so the scatter is stable.
+// Workspace: cnt[S][tiles][B] (counts, then tile prefixes) and base[S][B].
+#include "lsh_device.h"
+#include "lsh_launch.h"
+
+namespace lsh {
+
+int sort_tile(const Shape& s) {
+  // tiles of at least max(2048, B) tokens keep the count table no larger
+  // than the keys themselves
+  int t = 2048;
+  while (t < s.buckets) t <<= 1;
+  return t;
+}
+
+static int64_t sort_tiles(const Shape& s) {
+  const int t = sort_tile(s);
+  return (s.len + t - 1) / t;
+}
+
+size_t sort_workspace_bytes(const Shape& s) {
+  const int64_t S = s.segments();
+  const int64_t T = sort_tiles(s);
+  const size_t cnt = (size_t)S * T * s.buckets * sizeof(int32_t);
+  const size_t base = (size_t)S * s.buckets * sizeof(int32_t);
+  return ((cnt + 255) & ~(size_t)255) + base;
+}
+
+__device__ __forceinline__ int clamp_bucket(int k, int nb) {
+  return k < 0 ? 0 : (k >= nb ? nb - 1 : k);
+}
+
+__global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ buckets,
+                                                        int32_t* __restrict__ cnt, int L, int nb,
+                                                        int tile, int ntiles) {
+  extern __shared__ int32_t hist[];
+  const int64_t seg = blockIdx.x / ntiles;
+  const int t = blockIdx.x % ntiles;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int lo = t * tile;
+  const int hi = min(L, lo + tile);
+  const int32_t* bk = buckets + seg * L;
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x)
+    atomicAdd(&hist[clamp_bucket(bk[i], nb)], 1);
+  __syncthreads();
+  int32_t* out = cnt + (seg * ntiles + t) * (int64_t)nb;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) out[i] = hist[i];
+}
+
+// cnt[seg][t][bin] -> exclusive prefix over t; totals[seg][bin] = sum over t.
+__global__ __launch_bounds__(256) void sort_scan_tiles_kernel(int32_t* __restrict__ cnt,
+                                                             int32_t* __restrict__ totals, int nb,
+                                                             int ntiles, int64_t nbins_total) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= nbins_total) return;
+  const int64_t seg = g / nb;
+  const int bin = (int)(g % nb);
+  int32_t* c = cnt + seg * ntiles * (int64_t)nb + bin;
+  int32_t run = 0;
+  for (int t = 0; t < ntiles; ++t) {
+    const int32_t v = c[(int64_t)t * nb];
+    c[(int64_t)t * nb] = run;
+    run += v;
+  }
+  totals[g] = run;
+}
+
+// totals[seg][bin] -> exclusive prefix over bins (in place).
+__global__ __launch_bounds__(1024) void sort_scan_bins_kernel(int32_t* __restrict__ totals,
+                                                             int nb) {
+  __shared__ int32_t part[1024];
+  int32_t* t = totals + (int64_t)blockIdx.x * nb;
+  const int per = (nb + 1023) / 1024;
+  const int lo = threadIdx.x * per;
+  const int hi = min(nb, lo + per);
+  int32_t s = 0;
+  for (int i = lo; i < hi; ++i) s += t[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - s;
+  for (int i = lo; i < hi; ++i) {
+    const int32_t v = t[i];
+    t[i] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(64) void sort_scatter_kernel(
+    const int32_t* __restrict__ buckets, const int32_t* __restrict__ cnt,
+    const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int L, int nb, int nbits, int tile, int ntiles) {
+  extern __shared__ int32_t run[];
+  const int lane = lane_id();
+  const int64_t seg = blockIdx.x / ntiles;
+  const int t = blockIdx.x % ntiles;
+  const int32_t* pre = cnt + (seg * ntiles + t) * (int64_t)nb;
+  const int32_t* bs = base + seg * nb;
+  for (int i = lane; i < nb; i += kWave) run[i] = bs[i] + pre[i];
+  __builtin_amdgcn_wave_barrier();
+
+  const int lo = t * tile;
+  const int hi = min(L, lo + tile);
+  const int32_t* bk = buckets + seg * L;
+  int32_t* pm = perm + seg * L;
+  int32_t* ip = inv_perm + seg * L;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = lo; i0 < hi; i0 += kWave) {
+    const int i = i0 + lane;
+    const bool valid = i < hi;
+    const int key = valid ? clamp_bucket(bk[i], nb) : 0;
+    // lanes holding the same key: intersect the ballots of every key bit
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      peers &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(peers & below);
+    const int n = __popcll(peers);
+    const int32_t start = valid ? run[key] : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == n - 1) run[key] = start + n;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      const int32_t slot = start + rank;
+      pm[slot] = i;
+      ip[i] = slot;
+    }
+  }
+}
+
+hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, int32_t* inv_perm,
+                       void* workspace, hipStream_t stream) {
+  const int64_t S = s.segments();
+  const int tile = sort_tile(s);
+  const int ntiles = (int)sort_tiles(s);
+  const int nb = s.buckets;
+  int nbits = 0;
+  while ((1 << nbits) < nb) ++nbits;
+  int32_t* cnt = static_cast<int32_t*>(workspace);
+  const size_t cnt_bytes = ((size_t)S * ntiles * nb * sizeof(int32_t) + 255) & ~(size_t)255;
+  int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cnt_bytes);
+  const size_t lds = (size_t)nb * sizeof(int32_t);
+
+  hipLaunchKernelGGL(sort_count_kernel, dim3((unsigned)(S * ntiles)), dim3(256), lds, stream,
+                     buckets, cnt, s.len, nb, tile, ntiles);
+  const int64_t nbins = S * nb;
+  hipLaunchKernelGGL(sort_scan_tiles_kernel, dim3((unsigned)((nbins + 255) / 256)), dim3(256), 0,
+                     stream, cnt, base, nb, ntiles, nbins);
+  hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base, nb);
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)(S * ntiles)), dim3(64), lds, stream,
+                     buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

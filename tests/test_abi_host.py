@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every entry point include/lsh.h declares, and
+reject every invalid argument on the host with the documented status before
+any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lsh_sparse_attention_hash_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "lsh.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsh_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = B.library()
+    assert lib.lsh_version() == 10000
+    for st, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape"),
+                     (3, b"workspace too small"), (4, b"HIP launch failure")):
+        assert lib.lsh_status_string(st) == text
+
+
+def cfg(**kw):
+    """A valid configuration with the given fields overwritten verbatim."""
+    c = B.make_config(batch=1, heads=2, seq_len=256, n_buckets=8, n_rounds=2, causal=1,
+                      self_mask=1, dtype="bf16")
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def call_hash(c, qk=FAKE, rot=FAKE, out=FAKE):
+    return B.library().lsh_hash(ctypes.byref(c), qk, rot, out, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=32), B.LSH_ERR_UNSUPPORTED),
+    (dict(chunk_len=128), B.LSH_ERR_UNSUPPORTED),
+    (dict(n_buckets=7), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(n_buckets=0), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(n_buckets=32768), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(n_rounds=0), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=100), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=-64), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(batch=1024, heads=1024, seq_len=4096, n_rounds=1), B.LSH_ERR_INVALID_ARGUMENT),
+])
+def test_invalid_config_rejected_by_every_call(kw, status):
+    c = cfg(**kw)
+    lib = B.library()
+    assert call_hash(c) == status
+    assert lib.lsh_sort(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == status
+    assert lib.lsh_chunk_attend(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.lsh_unsort_combine(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.lsh_sort_workspace_bytes(ctypes.byref(c)) == 0
+    assert lib.lsh_last_error()
+
+
+def test_null_and_misaligned_pointers_rejected():
+    c = cfg()
+    assert call_hash(c, qk=None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert b"qk" in B.library().lsh_last_error()
+    assert call_hash(c, rot=None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert call_hash(c, out=ctypes.c_void_p(0x10004)) == B.LSH_ERR_INVALID_ARGUMENT
+    assert b"aligned" in B.library().lsh_last_error()
+    lib = B.library()
+    assert lib.lsh_hash(ctypes.byref(c), FAKE, FAKE, FAKE, ctypes.c_void_p(0x10002), None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    assert lib.lsh_chunk_attend(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    assert lib.lsh_unsort_combine(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, None, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    assert lib.lsh_hash(None, FAKE, FAKE, FAKE, None, None) == B.LSH_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_too_small():
+    c = cfg()
+    need = B.lsh_sort_workspace_bytes(c)
+    assert need > 0
+    lib = B.library()
+    assert lib.lsh_sort(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+        B.LSH_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_bytes_cover_the_count_tables():
+    for L, nb, R in ((1024, 16, 1), (4096, 64, 2), (65536, 1024, 8), (524288, 8192, 2),
+                     (2048, 16384, 1)):
+        c = cfg(seq_len=L, n_buckets=nb, n_rounds=R, heads=4)
+        tile = 2048
+        while tile < nb:
+            tile *= 2
+        tiles = -(-L // tile)
+        S = 4 * R
+        assert B.lsh_sort_workspace_bytes(c) >= 4 * S * nb * (tiles + 1)
+
+
+def test_empty_problems_are_no_ops():
+    lib = B.library()
+    for kw in (dict(batch=0), dict(heads=0), dict(seq_len=0)):
+        c = cfg(**kw)
+        assert call_hash(c, qk=None, rot=None, out=None) == B.LSH_OK
+        assert lib.lsh_sort(ctypes.byref(c), None, None, None, None, 0, None) == B.LSH_OK
+        assert lib.lsh_chunk_attend(ctypes.byref(c), None, None, None, None, None, None, None) == 0
+        assert lib.lsh_unsort_combine(ctypes.byref(c), None, None, None, None, None, None) == 0
+        assert lib.lsh_sort_workspace_bytes(ctypes.byref(c)) == 0
+    assert lib.lsh_last_error() == b""
+
+
+def test_b1_needs_no_rotation():
+    c = cfg(n_buckets=1)
+    # rot may be NULL when B == 1; qk still required
+    assert call_hash(c, qk=None, rot=None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert b"qk" in B.library().lsh_last_error()

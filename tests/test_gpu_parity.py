@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar (from the method's contract): bucket ids, perm and inv_perm bit-exact;
+o_rounds, lse and y within max abs error 1e-5 for fp32 inputs and 2e-2 for
+bf16 inputs; lse = -inf exactly where the oracle's is.
+
+Small and medium problems are compared element by element in full.  The two
+largest workloads run at full size in the launch configuration the benchmark
+times; there the oracle checks a seeded sample of rows of every step (the
+integer steps are also checked in full where the oracle can afford it), each
+step fed with the GPU's own (already verified) inputs.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from lsh_sparse_attention_hash_amd import synth
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lsh_sparse_attention_hash_amd import binding
+    return binding
+
+
+def run_gpu(B, w, inputs):
+    cfg = B.config_for(w)
+    qk = B.to_device(inputs["qk"], w.dtype)
+    v = B.to_device(inputs["v"], w.dtype)
+    rot = B.to_device(inputs["rot"], w.dtype)
+    f = B.Forward(cfg)
+    f.run(qk, v, rot)
+    torch.cuda.synchronize()
+    return f
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def assert_close_lse(got, want, tol, what):
+    ninf_g, ninf_w = np.isneginf(got), np.isneginf(want)
+    assert np.array_equal(ninf_g, ninf_w), f"{what}: -inf pattern differs"
+    fin = ~ninf_w
+    err = np.abs(got[fin] - want[fin]).max(initial=0.0)
+    assert err <= tol, f"{what}: max abs err {err}"
+
+
+def assert_close(got, want, tol, what):
+    err = np.abs(np.asarray(got, np.float64) - want).max(initial=0.0)
+    assert err <= tol, f"{what}: max abs err {err} > {tol}"
+    return err
+
+
+def full_parity(B, w):
+    say(f"[parity] {w}")
+    inp = synth.make_inputs(w)
+    f = run_gpu(B, w, inp)
+    qk = synth.to_f64(inp["qk"], w.dtype)
+    v = synth.to_f64(inp["v"], w.dtype)
+    rot = synth.to_f64(inp["rot"], w.dtype)
+    ref = oracle.forward(qk, v, rot, w.n_buckets, w.n_rounds, w.chunk_len, w.causal, w.self_mask)
+    tol = TOL[w.dtype]
+    assert np.array_equal(host(f.buckets), ref["buckets"]), "buckets differ"
+    assert np.array_equal(host(f.perm), ref["perm"]), "perm differs"
+    assert np.array_equal(host(f.inv_perm), ref["inv_perm"]), "inv_perm differs"
+    assert_close_lse(host(f.lse), ref["lse"], tol, "lse")
+    assert_close(host(f.o_rounds), ref["o_rounds"], tol, "o_rounds")
+    err = assert_close(host(f.y), ref["y"], tol, "y")
+    # the combine step alone, on the GPU's own per-round outputs
+    y2 = oracle.combine(host(f.o_rounds), host(f.lse), host(f.inv_perm), v)
+    assert_close(host(f.y), y2, 1e-5, "combine on identical inputs")
+    say(f"[parity] {w.name}: y max abs err {err:.3g}, fallback rows {int(host(f.fallback_rows)[0])}")
+    return f
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "medium"])
+def test_workload_full_parity(B, name):
+    full_parity(B, synth.WORKLOADS[name])
+
+
+EDGE = {
+    # ragged hash tile (L = 37 chunks), padded direction tile (B/2 = 19), not causal
+    "ragged_noncausal": synth.Workload("ragged", 3, 2, 64 * 37, 64, 38, 3, 64, False, False,
+                                       "bf16", 11),
+    "ragged_self": synth.Workload("ragged_self", 1, 3, 64 * 37, 64, 38, 2, 64, False, True,
+                                  "bf16", 12),
+    "single_chunk": synth.Workload("single", 2, 2, 64, 64, 4, 2, 64, True, True, "bf16", 13),
+    "no_hashing": synth.Workload("b1", 1, 2, 64 * 9, 64, 1, 2, 64, True, True, "bf16", 14),
+    "two_buckets": synth.Workload("b2", 1, 2, 64 * 9, 64, 2, 3, 64, False, True, "bf16", 15),
+    "max_buckets": synth.Workload("bmax", 1, 1, 2048, 64, 16384, 1, 64, True, True, "bf16", 16),
+    "f32_causal_rounds": synth.Workload("f32r", 2, 2, 64 * 7, 64, 8, 3, 64, True, False,
+                                        "f32", 17),
+    "clusters": synth.Workload("clusters", 1, 2, 4096, 64, 64, 2, 64, True, True, "bf16", 18,
+                               n_clusters=4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_case_parity(B, name):
+    full_parity(B, EDGE[name])
+
+
+def test_empty_problem_is_a_no_op(B):
+    w = synth.Workload("empty", 1, 2, 0, 64, 8, 2, 64, True, True, "bf16", 19)
+    cfg = B.config_for(w)
+    z = torch.zeros(0, device="cuda")
+    lib = B.library()
+    import ctypes
+    assert lib.lsh_hash(ctypes.byref(cfg), None, None, None, None, None) == 0
+    assert lib.lsh_sort(ctypes.byref(cfg), None, None, None, None, 0, None) == 0
+    del z
+
+
+def test_repeat_runs_are_bitwise_identical(B):
+    w = synth.WORKLOADS["small"]
+    inp = synth.make_inputs(w)
+    a = run_gpu(B, w, inp)
+    outs = [host(t).copy() for t in (a.buckets, a.perm, a.inv_perm, a.o_rounds, a.lse, a.y)]
+    for _ in range(3):
+        b = run_gpu(B, w, inp)
+        for x, t in zip(outs, (b.buckets, b.perm, b.inv_perm, b.o_rounds, b.lse, b.y)):
+            assert np.array_equal(x, host(t))
+
+
+def test_hash_matches_exactly_on_skewed_and_tied_inputs(B):
+    """Integer-valued bf16 inputs produce exact ties; zero rows tie everywhere."""
+    w = synth.Workload("ties", 1, 2, 1024, 64, 64, 2, 64, True, True, "bf16", 20)
+    g = np.random.default_rng(21)
+    qk = g.integers(-2, 3, size=(1, 2, 1024, 64)).astype(np.float32)
+    qk[0, 0, :10] = 0.0
+    rot = g.integers(-1, 2, size=(2, 2, 32, 64)).astype(np.float32)
+    inp = {"qk": synth.bf16_bits(qk), "v": synth.bf16_bits(g.standard_normal(qk.shape)),
+           "rot": synth.bf16_bits(rot)}
+    f = run_gpu(B, w, inp)
+    ref = oracle.hash(synth.to_f64(inp["qk"], "bf16"), synth.to_f64(inp["rot"], "bf16"), 64, 2)
+    assert np.array_equal(host(f.buckets), ref)
+    assert int(host(f.fallback_rows)[0]) > 0   # ties can only be settled by the fp64 path
+
+
+# --------------------------------------------------------------- full size
+def sampled_parity(B, w, n_hash, n_rows, seed):
+    say(f"[parity-full] {w}")
+    inp = synth.make_inputs(w)
+    f = run_gpu(B, w, inp)
+    tol = TOL[w.dtype]
+    g = np.random.default_rng(seed)
+    qk = synth.to_f64(inp["qk"], w.dtype)
+    rot = synth.to_f64(inp["rot"], w.dtype)
+    bk = host(f.buckets)
+    idx = g.integers(0, bk.size, n_hash)
+    ref_b = oracle.hash_rows(qk, rot, w.n_buckets, w.n_rounds, idx)
+    assert np.array_equal(bk.ravel()[idx], ref_b), "sampled buckets differ"
+    say(f"[parity-full] {w.name}: {n_hash} sampled buckets exact")
+    perm, inv = oracle.sort(bk)
+    assert np.array_equal(host(f.perm), perm), "perm differs"
+    assert np.array_equal(host(f.inv_perm), inv), "inv_perm differs"
+    say(f"[parity-full] {w.name}: perm / inv_perm exact")
+    v = synth.to_f64(inp["v"], w.dtype)
+    rows = g.integers(0, bk.size, n_rows)
+    o_ref, lse_ref = oracle.attend_rows(qk, v, bk, perm, w.n_buckets, w.chunk_len, w.causal,
+                                        w.self_mask, rows)
+    lse = host(f.lse).ravel()[rows]
+    assert_close_lse(lse, lse_ref, tol, "lse")
+    o = host(f.o_rounds).reshape(-1, w.head_dim)[rows]
+    err_o = assert_close(o, o_ref, tol, "o_rounds")
+    toks = g.integers(0, w.batch * w.heads * w.seq_len, n_rows)
+    y_ref = oracle.combine_rows(host(f.o_rounds), host(f.lse), inv, v, toks)
+    y = host(f.y).reshape(-1, w.head_dim)[toks]
+    assert_close(y, y_ref, 1e-5, "combine rows")
+    say(f"[parity-full] {w.name}: o err {err_o:.3g}, fallback rows {int(host(f.fallback_rows)[0])}")
+
+
+def test_long_full_size_sampled(B):
+    sampled_parity(B, synth.WORKLOADS["long"], n_hash=20000, n_rows=20000, seed=31)
+
+
+def test_verylong_full_size_sampled(B):
+    sampled_parity(B, synth.WORKLOADS["verylong"], n_hash=4000, n_rows=20000, seed=32)
+
+
+def test_long_end_to_end_rows(B):
+    """End to end at full size: y of sampled tokens from the oracle's own
+    hash -> sort -> attend -> combine of the heads they belong to (one head's
+    oracle work is affordable)."""
+    w = synth.WORKLOADS["long"].replace(heads=1)
+    inp = synth.make_inputs(synth.WORKLOADS["long"])
+    inp = {"qk": inp["qk"][:, :1].copy(), "v": inp["v"][:, :1].copy(),
+           "rot": inp["rot"][:1].copy()}
+    f = run_gpu(B, w, inp)
+    qk = synth.to_f64(inp["qk"], w.dtype)
+    v = synth.to_f64(inp["v"], w.dtype)
+    rot = synth.to_f64(inp["rot"], w.dtype)
+    bk = oracle.hash(qk, rot, w.n_buckets, w.n_rounds)
+    assert np.array_equal(host(f.buckets), bk)
+    perm, inv = oracle.sort(bk)
+    o, lse = oracle.attend(qk, v, bk, perm, w.n_buckets, w.chunk_len, w.causal, w.self_mask)
+    toks = np.random.default_rng(33).integers(0, w.seq_len, 4000)
+    y_ref = oracle.combine_rows(o, lse, inv, v, toks)
+    assert_close(host(f.y).reshape(-1, 64)[toks], y_ref, TOL["bf16"], "y")
