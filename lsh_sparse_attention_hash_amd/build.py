@@ -23,6 +23,7 @@ SOURCES = ["api.hip", "hash.hip", "sort.hip", "attend.hip", "combine.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of the generated code on purpose.
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC]
 

@@ -48,25 +48,45 @@ struct AttendLds {
   int32_t kpos[128];   // original position of the key
 };
 
-// Gather sorted chunk c (64 rows of x and v) into LDS half (c & 1).
-__device__ __forceinline__ void stage_chunk_bf16(AttendLds& sm, const uint16_t* xb,
-                                                 const uint16_t* vb, const int32_t* bk,
-                                                 const int32_t* pm, int c, int L) {
+// Staging of one sorted chunk (64 rows of x and v), split in two so the
+// gathers of the next chunk are in flight while the current one is computed:
+// thread t handles the key pair 2*(t/8), 2*(t/8)+1 and the 16-byte column block t%8.
+struct ChunkRegs {
+  int2 pos;                 // original positions of the two keys
+  uint4 xa, xc, va, vc;     // their x and v column blocks
+  int ba, bc;               // their bucket ids
+};
+
+__device__ __forceinline__ int2 load_perm_pair(const int32_t* pm, int c, int L) {
+  int2 p = *reinterpret_cast<const int2*>(pm + (size_t)c * kChunk + 2 * (threadIdx.x >> 3));
+  p.x = clamp_index(p.x, L);
+  p.y = clamp_index(p.y, L);
+  return p;
+}
+
+__device__ __forceinline__ void gather_chunk(ChunkRegs& g, int2 pos, const uint16_t* xb,
+                                             const uint16_t* vb, const int32_t* bk) {
+  const int dblk = threadIdx.x & 7;
+  g.pos = pos;
+  g.xa = load16(xb + (size_t)pos.x * kHeadDim + 8 * dblk);
+  g.xc = load16(xb + (size_t)pos.y * kHeadDim + 8 * dblk);
+  g.va = load16(vb + (size_t)pos.x * kHeadDim + 8 * dblk);
+  g.vc = load16(vb + (size_t)pos.y * kHeadDim + 8 * dblk);
+  g.ba = bk[pos.x];
+  g.bc = bk[pos.y];
+}
+
+// Write a gathered chunk c into LDS half (c & 1): x rows, V transposed, and
+// per-key scale, bucket and position.
+__device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, int c) {
   const int tid = threadIdx.x;
   const int p = tid >> 3;          // key pair 0..31
   const int dblk = tid & 7;        // 16-byte column block
   const int row = 64 * (c & 1) + 2 * p;
-  int2 pos = *reinterpret_cast<const int2*>(pm + (size_t)c * kChunk + 2 * p);
-  pos.x = clamp_index(pos.x, L);
-  pos.y = clamp_index(pos.y, L);
-  const uint4 xa = load16(xb + (size_t)pos.x * kHeadDim + 8 * dblk);
-  const uint4 xc = load16(xb + (size_t)pos.y * kHeadDim + 8 * dblk);
-  const uint4 va = load16(vb + (size_t)pos.x * kHeadDim + 8 * dblk);
-  const uint4 vc = load16(vb + (size_t)pos.y * kHeadDim + 8 * dblk);
-  store16(&sm.xs[row * kXStride + 8 * dblk], xa);
-  store16(&sm.xs[(row + 1) * kXStride + 8 * dblk], xc);
-  const uint32_t wa[4] = {va.x, va.y, va.z, va.w};
-  const uint32_t wc[4] = {vc.x, vc.y, vc.z, vc.w};
+  store16(&sm.xs[row * kXStride + 8 * dblk], g.xa);
+  store16(&sm.xs[(row + 1) * kXStride + 8 * dblk], g.xc);
+  const uint32_t wa[4] = {g.va.x, g.va.y, g.va.z, g.va.w};
+  const uint32_t wc[4] = {g.vc.x, g.vc.y, g.vc.z, g.vc.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const uint32_t even = (wa[e] & 0xffffu) | (wc[e] << 16);
@@ -74,8 +94,8 @@ __device__ __forceinline__ void stage_chunk_bf16(AttendLds& sm, const uint16_t* 
     *reinterpret_cast<uint32_t*>(&sm.vt[(8 * dblk + 2 * e) * kVStride + row]) = even;
     *reinterpret_cast<uint32_t*>(&sm.vt[(8 * dblk + 2 * e + 1) * kVStride + row]) = odd;
   }
-  const uint32_t ua[4] = {xa.x, xa.y, xa.z, xa.w};
-  const uint32_t uc[4] = {xc.x, xc.y, xc.z, xc.w};
+  const uint32_t ua[4] = {g.xa.x, g.xa.y, g.xa.z, g.xa.w};
+  const uint32_t uc[4] = {g.xc.x, g.xc.y, g.xc.z, g.xc.w};
   float sa = 0.f, sc = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -92,10 +112,10 @@ __device__ __forceinline__ void stage_chunk_bf16(AttendLds& sm, const uint16_t* 
   if (dblk == 0) {
     sm.kinv[row] = kLog2e / (fmaxf(sqrtf(sa), kNormEps) * 8.0f);
     sm.kinv[row + 1] = kLog2e / (fmaxf(sqrtf(sc), kNormEps) * 8.0f);
-    sm.kbk[row] = bk[pos.x];
-    sm.kbk[row + 1] = bk[pos.y];
-    sm.kpos[row] = pos.x;
-    sm.kpos[row + 1] = pos.y;
+    sm.kbk[row] = g.ba;
+    sm.kbk[row + 1] = g.bc;
+    sm.kpos[row] = g.pos.x;
+    sm.kpos[row + 1] = g.pos.y;
   }
 }
 
@@ -217,9 +237,20 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   const uint16_t* vb = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.L * kHeadDim;
   const int32_t* bk = a.buckets + seg * a.L;
   const int32_t* pm = a.perm + seg * a.L;
-  if (c0 > 0) stage_chunk_bf16(sm, xb, vb, bk, pm, c0 - 1, a.L);
+  ChunkRegs g;
+  if (c0 > 0) {
+    gather_chunk(g, load_perm_pair(pm, c0 - 1, a.L), xb, vb, bk);
+    commit_chunk(sm, g, c0 - 1);
+  }
+  gather_chunk(g, load_perm_pair(pm, c0, a.L), xb, vb, bk);
+  int2 next = make_int2(0, 0);
+  if (c0 + 1 < c1) next = load_perm_pair(pm, c0 + 1, a.L);
   for (int c = c0; c < c1; ++c) {
-    stage_chunk_bf16(sm, xb, vb, bk, pm, c, a.L);
+    commit_chunk(sm, g, c);
+    if (c + 1 < c1) {
+      gather_chunk(g, next, xb, vb, bk);          // chunk c+1, in flight during compute
+      if (c + 2 < c1) next = load_perm_pair(pm, c + 2, a.L);
+    }
     __syncthreads();
     attend_chunk_bf16(sm, a, seg, c);
     __syncthreads();

@@ -26,7 +26,9 @@ __device__ __forceinline__ float4 load_v4<float>(const float* row, int c4) {
   return *reinterpret_cast<const float4*>(row + c4);
 }
 
-template <typename T>
+// RMAX >= rounds: every round's slot, lse and output row are requested before
+// any is used, so a token's R row gathers are in flight together.
+template <typename T, int RMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_rounds,
                                                       const float* __restrict__ lse,
                                                       const int32_t* __restrict__ inv_perm,
@@ -39,11 +41,64 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int i = (int)(tok % L);
   const int64_t seg0 = bh * rounds;
 
+  int64_t row[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    if (r < rounds) row[r] = (seg0 + r) * L + clamp_index(inv_perm[(seg0 + r) * L + i], L);
+  float l[RMAX];
+  float4 o[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    if (r < rounds) {
+      l[r] = lse[row[r]];
+      o[r] = *reinterpret_cast<const float4*>(o_rounds + row[r] * kHeadDim + c4);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    if (r < rounds) mx = fmaxf(mx, l[r]);
+  float4 out;
+  if (mx == -INFINITY) {
+    out = load_v4<T>(v + tok * kHeadDim, c4);
+  } else {
+    float ws = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      if (r < rounds) {
+        const float w = expf(l[r] - mx);
+        ws += w;
+        acc.x = fmaf(w, o[r].x, acc.x);
+        acc.y = fmaf(w, o[r].y, acc.y);
+        acc.z = fmaf(w, o[r].z, acc.z);
+        acc.w = fmaf(w, o[r].w, acc.w);
+      }
+    }
+    const float inv = 1.0f / ws;
+    out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  *reinterpret_cast<float4*>(y + tok * kHeadDim + c4) = out;
+}
+
+// Any number of rounds: a running softmax over the rounds, one round at a time.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_many_kernel(const float* __restrict__ o_rounds,
+                                                           const float* __restrict__ lse,
+                                                           const int32_t* __restrict__ inv_perm,
+                                                           const T* __restrict__ v,
+                                                           float* __restrict__ y, int rounds,
+                                                           int L, int64_t total) {
+  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (tok >= total) return;
+  const int c4 = (threadIdx.x & 15) * 4;
+  const int64_t bh = tok / L;
+  const int i = (int)(tok % L);
+  const int64_t seg0 = bh * rounds;
   float mx = -INFINITY;
   for (int r = 0; r < rounds; ++r) {
     const int64_t seg = seg0 + r;
-    const int slot = clamp_index(inv_perm[seg * L + i], L);
-    mx = fmaxf(mx, lse[seg * L + slot]);
+    mx = fmaxf(mx, lse[seg * L + clamp_index(inv_perm[seg * L + i], L)]);
   }
   float4 out;
   if (mx == -INFINITY) {
@@ -68,16 +123,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<float4*>(y + tok * kHeadDim + c4) = out;
 }
 
+template <typename T>
+static void launch_combine_t(const Shape& s, const float* o_rounds, const float* lse,
+                             const int32_t* inv_perm, const T* v, float* y, hipStream_t stream) {
+  const int64_t total = s.token_heads();
+  const dim3 grid((unsigned)((total + 15) / 16)), block(256);
+  if (s.rounds <= 1)
+    hipLaunchKernelGGL((combine_kernel<T, 1>), grid, block, 0, stream, o_rounds, lse, inv_perm, v,
+                       y, s.rounds, s.len, total);
+  else if (s.rounds <= 2)
+    hipLaunchKernelGGL((combine_kernel<T, 2>), grid, block, 0, stream, o_rounds, lse, inv_perm, v,
+                       y, s.rounds, s.len, total);
+  else if (s.rounds <= 4)
+    hipLaunchKernelGGL((combine_kernel<T, 4>), grid, block, 0, stream, o_rounds, lse, inv_perm, v,
+                       y, s.rounds, s.len, total);
+  else if (s.rounds <= 8)
+    hipLaunchKernelGGL((combine_kernel<T, 8>), grid, block, 0, stream, o_rounds, lse, inv_perm, v,
+                       y, s.rounds, s.len, total);
+  else if (s.rounds <= 16)
+    hipLaunchKernelGGL((combine_kernel<T, 16>), grid, block, 0, stream, o_rounds, lse, inv_perm,
+                       v, y, s.rounds, s.len, total);
+  else
+    hipLaunchKernelGGL(combine_many_kernel<T>, grid, block, 0, stream, o_rounds, lse, inv_perm, v,
+                       y, s.rounds, s.len, total);
+}
+
 hipError_t launch_combine(const Shape& s, const float* o_rounds, const float* lse,
                           const int32_t* inv_perm, const void* v, float* y, hipStream_t stream) {
-  const int64_t total = s.token_heads();
-  const dim3 grid((unsigned)((total + 15) / 16));
   if (s.bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, stream, o_rounds, lse,
-                       inv_perm, static_cast<const uint16_t*>(v), y, s.rounds, s.len, total);
+    launch_combine_t(s, o_rounds, lse, inv_perm, static_cast<const uint16_t*>(v), y, stream);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream, o_rounds, lse, inv_perm,
-                       static_cast<const float*>(v), y, s.rounds, s.len, total);
+    launch_combine_t(s, o_rounds, lse, inv_perm, static_cast<const float*>(v), y, stream);
   return hipGetLastError();
 }
 

@@ -69,11 +69,34 @@ __device__ int exact_bucket(const double* x, const T* rot_hr, int half) {
 }
 
 // ---------------------------------------------------------------------------
+// Keys: the fp32 score with its 5 low mantissa bits replaced by the direction's
+// offset inside its 32-direction tile (the lane-half bit 4 of that offset is
+// added after the halves merge).  Magnitude keys |key| order like |score| up to
+// that truncation; the tile of the running maximum is tracked per lane.
+constexpr uint32_t kKeyMask = ~31u;
+
+__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* rhr, int half, int st,
+                                           uint4 (&buf)[4], bool load) {
+  // 128 rows x 8 chunks of 16 B = 1024 chunks, 4 per thread
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = threadIdx.x + 256 * q;
+    const int row = c >> 3, col = (c & 7) * 8;
+    const int j = st * kStageRows + row;
+    if (load) {
+      buf[q] = make_uint4(0, 0, 0, 0);
+      if (j < half) buf[q] = load16(rhr + (size_t)j * kHeadDim + col);
+    } else {
+      store16(&dst[row * kRowStride + col], buf[q]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void hash_bf16_kernel(
     const uint16_t* __restrict__ qk, const uint16_t* __restrict__ rot,
     int32_t* __restrict__ buckets, uint32_t* __restrict__ fallback_rows, int heads, int L,
-    int half, int rounds, int ib) {
-  __shared__ __attribute__((aligned(16))) uint16_t rs[kStageRows * kRowStride];
+    int half, int rounds) {
+  __shared__ __attribute__((aligned(16))) uint16_t rs[2][kStageRows * kRowStride];
   __shared__ float gram_part[kHashWaves];
   __shared__ double xfb[kHashWaves][kHeadDim];
 
@@ -107,39 +130,37 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
     xnorm[nb] = sqrtf(ss);
   }
 
-  const uint32_t idxmask = (1u << ib) - 1u;
-  const uint32_t keymask = ~idxmask;
   const int nstages = (half + kStageRows - 1) / kStageRows;
+  const int ntiles = (half + 31) / 32;
 
   for (int r = 0; r < rounds; ++r) {
     const uint16_t* rhr = rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim;
-    float m1[2] = {0.f, 0.f}, m2[2] = {0.f, 0.f}, smax[2] = {-INFINITY, -INFINITY};
+    float m1[2] = {0.f, 0.f}, m2[2] = {0.f, 0.f};
+    int smax[2] = {INT_MIN, INT_MIN};
+    int wt[2] = {0, 0};
     float gmax = 0.f;
 
+    uint4 buf[4];
+    stage_rows(nullptr, rhr, half, 0, buf, true);
+    __syncthreads();   // previous round's readers of rs[0] are done
+    stage_rows(rs[0], rhr, half, 0, buf, false);
+    __syncthreads();
     for (int st = 0; st < nstages; ++st) {
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = threadIdx.x + 256 * q;
-        const int row = c >> 3, col = (c & 7) * 8;
-        const int j = st * kStageRows + row;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (j < half) u = load16(rhr + (size_t)j * kHeadDim + col);
-        store16(&rs[row * kRowStride + col], u);
-      }
-      __syncthreads();
+      const uint16_t* cur = rs[st & 1];
+      const bool more = st + 1 < nstages;
+      if (more) stage_rows(nullptr, rhr, half, st + 1, buf, true);   // in flight during compute
 
 #pragma unroll
       for (int t = 0; t < kStageRows / 32; ++t) {
-        const int jt = st * kStageRows + t * 32;
-        if (jt >= half) break;
-        // A operand (R^T, direction x k): lane holds R[k = 8*(lane/32)+16*ks..][j = jt + lane%32].
+        const int tile = st * (kStageRows / 32) + t;
+        if (tile >= ntiles) break;
+        // A operand (R^T, direction x k): lane holds R[k = 8*(lane/32)+16*ks..][j = 32*tile + lane%32].
         bf16x8 a[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          a[ks] = as_bf16x8(load16(&rs[(t * 32 + (lane & 31)) * kRowStride + 8 * (lane >> 5) + 16 * ks]));
+          a[ks] = as_bf16x8(load16(&cur[(t * 32 + (lane & 31)) * kRowStride + 8 * (lane >> 5) + 16 * ks]));
 
-        if (((st * 4 + t) & (kHashWaves - 1)) == wave) {
+        if ((tile & (kHashWaves - 1)) == wave) {
           // Gram block R_tile^T R_tile: its largest entry is the largest squared
           // direction norm of the tile (off-diagonal entries never exceed it).
           f32x16 g = {};
@@ -156,21 +177,26 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], xf[nb][ks], acc, 0, 0, 0);
-          // Output layout: register i of lane l is direction jt + 8*(i/4) + 4*(l/32) + i%4
-          // for token l%32.  The key carries jt + 8*(i/4) + i%4; the lane-half bit (4)
-          // is restored after the two halves merge.
+          // Output layout: register i of lane l is direction 32*tile + 8*(i/4) + 4*(l/32) + i%4
+          // of token l%32.
+          const float before = m1[nb];
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            const uint32_t ja = (uint32_t)(jt + 8 * (i >> 2) + (i & 3));
-            const float ka = __uint_as_float((__float_as_uint(acc[i]) & keymask) | ja);
-            const float kb = __uint_as_float((__float_as_uint(acc[i + 1]) & keymask) | (ja + 1));
-            smax[nb] = fmaxf(smax[nb], fmaxf(ka, kb));
-            const float aa = fabsf(ka), ab = fabsf(kb);
+            const uint32_t off = 8 * (i >> 2) + (i & 3);
+            const uint32_t ka = (__float_as_uint(acc[i]) & kKeyMask) | off;
+            const uint32_t kb = (__float_as_uint(acc[i + 1]) & kKeyMask) | (off + 1);
+            smax[nb] = max(smax[nb], max((int)ka, (int)kb));
+            const float aa = fabsf(__uint_as_float(ka)), ab = fabsf(__uint_as_float(kb));
             const float n1 = fmaxf(m1[nb], fmaxf(aa, ab));
             m2[nb] = fmaxf(m2[nb], __builtin_amdgcn_fmed3f(m1[nb], aa, ab));
             m1[nb] = n1;
           }
+          wt[nb] = (__float_as_uint(m1[nb]) != __float_as_uint(before)) ? tile : wt[nb];
         }
+      }
+      if (more) {
+        stage_rows(rs[(st + 1) & 1], rhr, half, st + 1, buf, false);
+        __syncthreads();
       }
     }
 
@@ -187,18 +213,20 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
     int32_t* bout = buckets + (bh * rounds + r) * (size_t)L;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
+      // A positive winner is also the largest signed key, bit for bit.
+      const int own_pos = smax[nb] == (int)__float_as_uint(m1[nb]);
+      const uint32_t own_j = 32u * wt[nb] + (__float_as_uint(m1[nb]) & 31u) + 4u * (lane >> 5);
       const float pm1 = __shfl_xor(m1[nb], 32);
       const float pm2 = __shfl_xor(m2[nb], 32);
-      const int own_pos = __float_as_uint(smax[nb]) == __float_as_uint(m1[nb]);
       const int other_pos = __shfl_xor(own_pos, 32);
+      const uint32_t other_j = __shfl_xor(own_j, 32);
       const bool other = pm1 > m1[nb];
       const float w1 = other ? pm1 : m1[nb];
       const float w2 = fmaxf(fminf(m1[nb], pm1), fmaxf(m2[nb], pm2));
-      const int half_id = (other ? (lane ^ 32) : lane) >> 5;
-      const uint32_t jstar = (__float_as_uint(w1) & idxmask) | ((uint32_t)half_id << 2);
+      const uint32_t jstar = other ? other_j : own_j;
       const bool pos = other ? other_pos : own_pos;
-      const float lower1 = __uint_as_float(__float_as_uint(w1) & keymask);
-      const float upper2 = __uint_as_float((__float_as_uint(w2) & keymask) + (1u << ib));
+      const float lower1 = __uint_as_float(__float_as_uint(w1) & kKeyMask);
+      const float upper2 = __uint_as_float((__float_as_uint(w2) & kKeyMask) + 32u);
       // |fp32 MFMA score - exact| <= 64 * 2^-23 * sum_k |x_k R_kj| <= 64 * 2^-23 |x| |R_j|;
       // doubled to cover the fp64 rounding of the definition, plus flush-to-zero slack.
       const float E = xnorm[nb] * rcol * (64.0f * 0x1p-22f * 1.01f) +
@@ -267,13 +295,11 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
                        buckets, s.heads, s.len, half, s.rounds, rows);
     return hipGetLastError();
   }
-  int ib = 5;
-  while ((1 << ib) < half) ++ib;
   const dim3 grid((unsigned)((s.len + kHashTokWG - 1) / kHashTokWG), (unsigned)s.heads,
                   (unsigned)s.batch);
   hipLaunchKernelGGL(hash_bf16_kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
-                     fallback_rows, s.heads, s.len, half, s.rounds, ib);
+                     fallback_rows, s.heads, s.len, half, s.rounds);
   return hipGetLastError();
 }
 
