@@ -40,9 +40,16 @@ struct AttendArgs {
 };
 
 // ------------------------------------------------------------------- bf16
+// V^T rows hold the 128 window keys as 64 dwords (two bf16 keys each) plus 4
+// dwords of padding; the dword column is XOR-swizzled by 8 * ((d >> 4) & 3),
+// which keeps 4-key groups contiguous and 8-byte aligned while making both the
+// transposing writes and the MFMA operand reads free of LDS bank conflicts.
+constexpr int kVRowDw = kVStride / 2;   // 68
+__device__ __forceinline__ int vt_col(int d, int kdw) { return kdw ^ (8 * ((d >> 4) & 3)); }
+
 struct AttendLds {
   uint16_t xs[128 * kXStride];
-  uint16_t vt[kHeadDim * kVStride];
+  uint32_t vt[kHeadDim * kVRowDw];
   float kinv[128];     // log2(e) / (max(|x_j|, eps) * sqrt(d))
   int32_t kbk[128];    // bucket of the key
   int32_t kpos[128];   // original position of the key
@@ -91,8 +98,9 @@ __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, 
   for (int e = 0; e < 4; ++e) {
     const uint32_t even = (wa[e] & 0xffffu) | (wc[e] << 16);
     const uint32_t odd = (wa[e] >> 16) | (wc[e] & 0xffff0000u);
-    *reinterpret_cast<uint32_t*>(&sm.vt[(8 * dblk + 2 * e) * kVStride + row]) = even;
-    *reinterpret_cast<uint32_t*>(&sm.vt[(8 * dblk + 2 * e + 1) * kVStride + row]) = odd;
+    const int d0 = 8 * dblk + 2 * e;
+    sm.vt[d0 * kVRowDw + vt_col(d0, row >> 1)] = even;
+    sm.vt[(d0 + 1) * kVRowDw + vt_col(d0 + 1, row >> 1)] = odd;
   }
   const uint32_t ua[4] = {g.xa.x, g.xa.y, g.xa.z, g.xa.w};
   const uint32_t uc[4] = {g.xc.x, g.xc.y, g.xc.z, g.xc.w};
@@ -110,8 +118,9 @@ __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, 
     sc += __shfl_xor(sc, off);
   }
   if (dblk == 0) {
-    sm.kinv[row] = kLog2e / (fmaxf(sqrtf(sa), kNormEps) * 8.0f);
-    sm.kinv[row + 1] = kLog2e / (fmaxf(sqrtf(sc), kNormEps) * 8.0f);
+    // log2(e) / (max(|x|, eps) * sqrt(d)) with sqrt(d) = 8
+    sm.kinv[row] = (kLog2e / 8.0f) * __builtin_amdgcn_rsqf(fmaxf(sa, kNormEps * kNormEps));
+    sm.kinv[row + 1] = (kLog2e / 8.0f) * __builtin_amdgcn_rsqf(fmaxf(sc, kNormEps * kNormEps));
     sm.kbk[row] = g.ba;
     sm.kbk[row + 1] = g.bc;
     sm.kpos[row] = g.pos.x;
@@ -119,6 +128,7 @@ __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, 
   }
 }
 
+template <bool CAUSAL, bool SELF>
 __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArgs& a, int64_t seg,
                                                   int c) {
   const int lane = lane_id();
@@ -127,7 +137,7 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
   const int ql = lane & 15;         // query column of this lane
   const int hq = c & 1, hp = hq ^ 1;
   const int qrow = 64 * hq + 16 * wave + ql;
-  const int tfirst = (c == 0) ? 4 : 0;   // chunk 0 has no predecessor
+  const bool first = c == 0;        // chunk 0 has no predecessor (uniform)
 
   // B operand: Q^T (d x query), lane holds x_q[8*g + 32*ks .. +7]
   bf16x8 qf[2];
@@ -140,7 +150,7 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
   float s[8][4];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    if (t < tfirst) {
+    if (first && t < 4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[t][i] = -INFINITY;
       continue;
@@ -155,14 +165,21 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
     const int row4 = (16 * t + 4 * g + 64 * hp) & 127;
     const float4 kv = *reinterpret_cast<const float4*>(&sm.kinv[row4]);
     const int4 kb = *reinterpret_cast<const int4*>(&sm.kbk[row4]);
-    const int4 kp = *reinterpret_cast<const int4*>(&sm.kpos[row4]);
     const float kva[4] = {kv.x, kv.y, kv.z, kv.w};
     const int kba[4] = {kb.x, kb.y, kb.z, kb.w};
-    const int kpa[4] = {kp.x, kp.y, kp.z, kp.w};
+    int kpa[4] = {0, 0, 0, 0};
+    if (CAUSAL || SELF) {
+      const int4 kp = *reinterpret_cast<const int4*>(&sm.kpos[row4]);
+      kpa[0] = kp.x; kpa[1] = kp.y; kpa[2] = kp.z; kpa[3] = kp.w;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = kba[i] == qb && (!a.causal || kpa[i] <= qp) && (!a.self_mask || kpa[i] != qp);
-      s[t][i] = ok ? acc[i] * kva[i] : -INFINITY;
+      bool ok = kba[i] == qb;
+      if (CAUSAL && SELF) ok = ok && kpa[i] < qp;
+      if (CAUSAL && !SELF) ok = ok && kpa[i] <= qp;
+      if (!CAUSAL && SELF) ok = ok && kpa[i] != qp;
+      const float sc = acc[i] * kva[i];
+      s[t][i] = ok ? sc : -INFINITY;
     }
   }
 
@@ -175,45 +192,47 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float msafe = (mx == -INFINITY) ? 0.f : mx;
 
-  // probabilities rounded to bf16 (the PV operand); the denominator sums the
-  // same rounded values so the weights of a row add up to one
+  // probabilities (<= 1) rounded to bf16: the B operand of the PV product
   uint32_t pw[8][2];
-  float sum = 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
-      const uint32_t w = pack_bf16x2(exp2f(s[t][i] - msafe), exp2f(s[t][i + 1] - msafe));
-      pw[t][i >> 1] = w;
-      sum += bf16lo(w) + bf16hi(w);
+      const bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(s[t][i] - msafe),
+                         (__bf16)__builtin_amdgcn_exp2f(s[t][i + 1] - msafe)};
+      pw[t][i >> 1] = __builtin_bit_cast(uint32_t, pr);
     }
   }
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
 
-  const int kfirst = (c == 0) ? 2 : 0;
-  f32x4 oacc[4];
+  // O^T = V^T P^T; a fifth tile of ones yields the row sums of the rounded P,
+  // so every output row is a weighted mean with weights adding up to one.
+  const int kfirst = first ? 2 : 0;
+  f32x4 oacc[5];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 5; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u,
+                                                            0x3f803f80u));
 #pragma unroll
   for (int k2 = 0; k2 < 4; ++k2) {
     if (k2 < kfirst) continue;
     // MFMA contraction index 8g + j <-> window key 32*k2 + 16*(j/4) + 4g + j%4
     const bf16x8 pb = __builtin_bit_cast(
         bf16x8, make_uint4(pw[2 * k2][0], pw[2 * k2][1], pw[2 * k2 + 1][0], pw[2 * k2 + 1][1]));
-    const int c0 = (32 * k2 + 4 * g + 64 * hp) & 127;
-    const int c1 = (32 * k2 + 16 + 4 * g + 64 * hp) & 127;
+    const int c0 = ((32 * k2 + 4 * g + 64 * hp) & 127) >> 1;        // key dword column
+    const int c1 = ((32 * k2 + 16 + 4 * g + 64 * hp) & 127) >> 1;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* vrow = &sm.vt[(16 * dt + ql) * kVStride];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + c0);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + c1);
+      const uint32_t* vrow = &sm.vt[(16 * dt + ql) * kVRowDw];
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (c0 ^ (8 * dt)));
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (c1 ^ (8 * dt)));
       const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, oacc[dt], 0, 0, 0);
     }
+    oacc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, oacc[4], 0, 0, 0);
   }
 
-  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  const float sum = oacc[4][0];
+  const float inv = sum > 0.f ? __builtin_amdgcn_rcpf(sum) : 0.f;
   const int64_t slot = (int64_t)c * kChunk + 16 * wave + ql;
   float* orow = a.o + ((int64_t)seg * a.L + slot) * kHeadDim;
 #pragma unroll
@@ -223,13 +242,16 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
     *reinterpret_cast<float4*>(orow + 16 * dt + 4 * g) = val;
   }
   if (g == 0)
-    a.lse[(int64_t)seg * a.L + slot] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
+    a.lse[(int64_t)seg * a.L + slot] =
+        (mx == -INFINITY) ? -INFINITY : (mx + __builtin_amdgcn_logf(sum)) * kLn2;
 }
 
+template <bool CAUSAL, bool SELF>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) AttendLds sm;
-  const int64_t seg = blockIdx.x / a.runs_per_seg;
-  const int run = blockIdx.x % a.runs_per_seg;
+  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t seg = blk / a.runs_per_seg;
+  const int run = (int)(blk % a.runs_per_seg);
   const int c0 = run * a.cpw;
   const int c1 = min(a.nchunks, c0 + a.cpw);
   const int64_t bh = seg / a.rounds;
@@ -252,7 +274,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
       if (c + 2 < c1) next = load_perm_pair(pm, c + 2, a.L);
     }
     __syncthreads();
-    attend_chunk_bf16(sm, a, seg, c);
+    attend_chunk_bf16<CAUSAL, SELF>(sm, a, seg, c);
     __syncthreads();
   }
 }
@@ -355,8 +377,15 @@ hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const in
   cpw = cpw < 1 ? 1 : (cpw > 16 ? 16 : cpw);
   a.cpw = cpw;
   a.runs_per_seg = (a.nchunks + cpw - 1) / cpw;
-  hipLaunchKernelGGL(attend_bf16_kernel, dim3((unsigned)(S * a.runs_per_seg)), dim3(256), 0,
-                     stream, a);
+  const dim3 grid((unsigned)(S * a.runs_per_seg)), block(256);
+  if (a.causal && a.self_mask)
+    hipLaunchKernelGGL((attend_bf16_kernel<true, true>), grid, block, 0, stream, a);
+  else if (a.causal)
+    hipLaunchKernelGGL((attend_bf16_kernel<true, false>), grid, block, 0, stream, a);
+  else if (a.self_mask)
+    hipLaunchKernelGGL((attend_bf16_kernel<false, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attend_bf16_kernel<false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

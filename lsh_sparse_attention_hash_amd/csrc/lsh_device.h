@@ -7,6 +7,7 @@
 namespace lsh {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -46,5 +47,17 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 // Index read from caller memory, forced into [0, n) so that no input can make
 // a kernel access memory outside its buffers.
 __device__ __forceinline__ int clamp_index(int i, int n) { return min(max(i, 0), n - 1); }
+
+// Workgroups are handed to the 8 XCDs of the chip round-robin (hardware block
+// w runs on XCD w % 8).  This maps the hardware id to a logical block index so
+// that each XCD works through one contiguous eighth of the logical range,
+// keeping the data of neighbouring logical blocks in that XCD's own L2.
+// It is a bijection on [0, n).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t w, int64_t n) {
+  const int64_t x = w % kXcds, k = w / kXcds;
+  const int64_t q = n / kXcds, rem = n % kXcds;
+  return x * q + (x < rem ? x : rem) + k;
+}
 
 }  // namespace lsh
