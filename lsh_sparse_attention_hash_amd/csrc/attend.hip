@@ -249,7 +249,7 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
 template <bool CAUSAL, bool SELF>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) AttendLds sm;
-  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t blk = xcd_interleaved_block(blockIdx.x, gridDim.x / a.runs_per_seg, a.runs_per_seg);
   const int64_t seg = blk / a.runs_per_seg;
   const int run = (int)(blk % a.runs_per_seg);
   const int c0 = run * a.cpw;

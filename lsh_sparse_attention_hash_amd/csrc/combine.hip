@@ -34,7 +34,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ inv_perm,
                                                       const T* __restrict__ v, float* __restrict__ y,
                                                       int rounds, int L, int64_t total) {
-  const int64_t tok = xcd_logical_block(blockIdx.x, gridDim.x) * 16 + (threadIdx.x >> 4);
+  // Last tokens first: the per-round rows written last by the attention step
+  // are the likeliest to still sit in the memory-side cache.
+  const int64_t tok = (int64_t)(gridDim.x - 1 - blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (tok >= total) return;
   const int c4 = (threadIdx.x & 15) * 4;
   const int64_t bh = tok / L;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void combine_many_kernel(const float* __restri
                                                            const T* __restrict__ v,
                                                            float* __restrict__ y, int rounds,
                                                            int L, int64_t total) {
-  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t tok = (int64_t)(gridDim.x - 1 - blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (tok >= total) return;
   const int c4 = (threadIdx.x & 15) * 4;
   const int64_t bh = tok / L;

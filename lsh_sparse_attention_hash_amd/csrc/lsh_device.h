@@ -60,4 +60,16 @@ __device__ __forceinline__ int64_t xcd_logical_block(int64_t w, int64_t n) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
+// Groups of `per` consecutive logical blocks ("units"): when the number of
+// units is a multiple of 8, XCD x works through units x, x+8, x+16, ... in
+// order, so at any moment the 8 XCDs hold 8 neighbouring units (for the
+// attention: the 8 hash rounds of one head, whose x and v rows are then hot in
+// the memory-side cache while each XCD's L2 keeps its own round's indices).
+// Otherwise the plain order is used.  A bijection on [0, units * per).
+__device__ __forceinline__ int64_t xcd_interleaved_block(int64_t w, int64_t units, int64_t per) {
+  if (units % kXcds != 0) return w;
+  const int64_t x = w % kXcds, k = w / kXcds;
+  return (x + kXcds * (k / per)) * per + k % per;
+}
+
 }  // namespace lsh

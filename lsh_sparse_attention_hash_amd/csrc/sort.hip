@@ -61,6 +61,7 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
 }
 
 // cnt[seg][t][bin] -> exclusive prefix over t; totals[seg][bin] = sum over t.
+// Loads are issued eight tiles at a time so their latencies overlap.
 __global__ __launch_bounds__(256) void sort_scan_tiles_kernel(int32_t* __restrict__ cnt,
                                                              int32_t* __restrict__ totals, int nb,
                                                              int ntiles, int64_t nbins_total) {
@@ -70,7 +71,18 @@ __global__ __launch_bounds__(256) void sort_scan_tiles_kernel(int32_t* __restric
   const int bin = (int)(g % nb);
   int32_t* c = cnt + seg * ntiles * (int64_t)nb + bin;
   int32_t run = 0;
-  for (int t = 0; t < ntiles; ++t) {
+  int t = 0;
+  for (; t + 8 <= ntiles; t += 8) {
+    int32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c[(int64_t)(t + u) * nb];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c[(int64_t)(t + u) * nb] = run;
+      run += v[u];
+    }
+  }
+  for (; t < ntiles; ++t) {
     const int32_t v = c[(int64_t)t * nb];
     c[(int64_t)t * nb] = run;
     run += v;
@@ -105,46 +117,67 @@ __global__ __launch_bounds__(1024) void sort_scan_bins_kernel(int32_t* __restric
   }
 }
 
+// One wave per (segment, tile).  The tile's keys are first loaded into
+// registers (kScatterBatches loads in flight per lane), then ranked 64 at a
+// time in position order: lanes holding equal keys are found by intersecting
+// the ballots of every key bit, and each key's slot is its bucket's running
+// offset (LDS) plus its rank among the equal keys of lower lanes.
+constexpr int kScatterBatches = 32;   // tile = 32 batches of 64 keys (2048 keys)
+
 __global__ __launch_bounds__(64) void sort_scatter_kernel(
     const int32_t* __restrict__ buckets, const int32_t* __restrict__ cnt,
     const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int L, int nb, int nbits, int tile, int ntiles) {
   extern __shared__ int32_t run[];
   const int lane = lane_id();
-  const int64_t seg = blockIdx.x / ntiles;
-  const int t = blockIdx.x % ntiles;
+  // each XCD scatters whole segments, so a segment's perm lines fill up in one
+  // L2 before they are written back
+  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t seg = blk / ntiles;
+  const int t = (int)(blk % ntiles);
   const int32_t* pre = cnt + (seg * ntiles + t) * (int64_t)nb;
   const int32_t* bs = base + seg * nb;
-  for (int i = lane; i < nb; i += kWave) run[i] = bs[i] + pre[i];
-  __builtin_amdgcn_wave_barrier();
-
   const int lo = t * tile;
   const int hi = min(L, lo + tile);
   const int32_t* bk = buckets + seg * L;
   int32_t* pm = perm + seg * L;
   int32_t* ip = inv_perm + seg * L;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i0 = lo; i0 < hi; i0 += kWave) {
-    const int i = i0 + lane;
-    const bool valid = i < hi;
-    const int key = valid ? clamp_bucket(bk[i], nb) : 0;
-    // lanes holding the same key: intersect the ballots of every key bit
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t ones = __ballot(bit);
-      peers &= bit ? ones : ~ones;
+
+  for (int i = lane; i < nb; i += kWave) run[i] = bs[i] + pre[i];
+
+  for (int c0 = lo; c0 < hi; c0 += kWave * kScatterBatches) {
+    int key[kScatterBatches];
+#pragma unroll
+    for (int b = 0; b < kScatterBatches; ++b) {
+      const int i = c0 + b * kWave + lane;
+      key[b] = i < hi ? clamp_bucket(bk[i], nb) : 0;
     }
-    const int rank = __popcll(peers & below);
-    const int n = __popcll(peers);
-    const int32_t start = valid ? run[key] : 0;
     __builtin_amdgcn_wave_barrier();
-    if (valid && rank == n - 1) run[key] = start + n;
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      const int32_t slot = start + rank;
-      pm[slot] = i;
-      ip[i] = slot;
+#pragma unroll
+    for (int b = 0; b < kScatterBatches; ++b) {
+      const int i0 = c0 + b * kWave;
+      if (i0 >= hi) break;
+      const int i = i0 + lane;
+      const bool valid = i < hi;
+      const int k = key[b];
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (k >> bit) & 1;
+        const uint64_t ones = __ballot(set);
+        peers &= set ? ones : ~ones;
+      }
+      const int rank = __popcll(peers & below);
+      const int n = __popcll(peers);
+      const int32_t start = valid ? run[k] : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (valid && rank == n - 1) run[k] = start + n;
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        const int32_t slot = start + rank;
+        pm[slot] = i;
+        ip[i] = slot;
+      }
     }
   }
 }
