@@ -4,13 +4,14 @@
 //
 // bf16 inputs: x R is contracted on the matrix cores (v_mfma_f32_32x32x16_bf16,
 // exact bf16 products, fp32 accumulation).  The epilogue keeps, per token, the
-// two largest |x R_j| as packed keys (magnitude bits with the direction index
-// in the low mantissa bits) and the largest signed key.  A row is accepted
-// only when the gap between the two best candidates exceeds twice a proven
-// bound on the fp32 accumulation error (plus the fp64 rounding of the defining
-// sum), so that its bucket is provably the one of the fp64 definition.  Other
-// rows are recomputed by one wave in fp64 in the defining order.
-// fp32 inputs are scored in fp64 directly (the same wave routine).
+// two largest |x R_j| as packed keys (magnitude bits with the direction's
+// offset in its tile in the low mantissa bits) and the tile of the largest.
+// A row is accepted only when the gap between the two best candidates exceeds
+// twice a proven bound on the fp32 accumulation error (plus the fp64 rounding
+// of the defining sum), so that its bucket is provably the one of the fp64
+// definition; the winner's sign then comes from an exact-sign dot product.
+// Other rows are marked and recomputed in fp64, in the defining order, by a
+// second kernel.  fp32 inputs are scored in fp64 directly.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -98,7 +99,6 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
     int half, int rounds) {
   __shared__ __attribute__((aligned(16))) uint16_t rs[2][kStageRows * kRowStride];
   __shared__ float gram_part[kHashWaves];
-  __shared__ double xfb[kHashWaves][kHeadDim];
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -136,7 +136,6 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
   for (int r = 0; r < rounds; ++r) {
     const uint16_t* rhr = rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim;
     float m1[2] = {0.f, 0.f}, m2[2] = {0.f, 0.f};
-    int smax[2] = {INT_MIN, INT_MIN};
     int wt[2] = {0, 0};
     float gmax = 0.f;
 
@@ -185,7 +184,6 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
             const uint32_t off = 8 * (i >> 2) + (i & 3);
             const uint32_t ka = (__float_as_uint(acc[i]) & kKeyMask) | off;
             const uint32_t kb = (__float_as_uint(acc[i + 1]) & kKeyMask) | (off + 1);
-            smax[nb] = max(smax[nb], max((int)ka, (int)kb));
             const float aa = fabsf(__uint_as_float(ka)), ab = fabsf(__uint_as_float(kb));
             const float n1 = fmaxf(m1[nb], fmaxf(aa, ab));
             m2[nb] = fmaxf(m2[nb], __builtin_amdgcn_fmed3f(m1[nb], aa, ab));
@@ -213,18 +211,32 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
     int32_t* bout = buckets + (bh * rounds + r) * (size_t)L;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      // A positive winner is also the largest signed key, bit for bit.
-      const int own_pos = smax[nb] == (int)__float_as_uint(m1[nb]);
       const uint32_t own_j = 32u * wt[nb] + (__float_as_uint(m1[nb]) & 31u) + 4u * (lane >> 5);
       const float pm1 = __shfl_xor(m1[nb], 32);
       const float pm2 = __shfl_xor(m2[nb], 32);
-      const int other_pos = __shfl_xor(own_pos, 32);
       const uint32_t other_j = __shfl_xor(own_j, 32);
       const bool other = pm1 > m1[nb];
       const float w1 = other ? pm1 : m1[nb];
       const float w2 = fmaxf(fminf(m1[nb], pm1), fmaxf(m2[nb], pm2));
-      const uint32_t jstar = other ? other_j : own_j;
-      const bool pos = other ? other_pos : own_pos;
+      const uint32_t jstar = other ? other_j : own_j;   // the same in lanes l and l^32
+      // Sign of the winning score x.R_j*: the two lanes of the token each dot
+      // their 32 k-values with the winner's direction row (exact bf16 products,
+      // fp32 sums).  On a certified row |x.R_j*| > 2E exceeds the error of any
+      // fp32 sum of these 64 products, so the computed sign is exact.
+      float part = 0.f;
+      {
+        const uint16_t* jrow = rhr + (size_t)min(jstar, (uint32_t)(half - 1)) * kHeadDim + 8 * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint4 rv = load16(jrow + 16 * ks);
+          const uint4 xv = __builtin_bit_cast(uint4, xf[nb][ks]);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.x), __builtin_bit_cast(bf16x2, rv.x), part, false);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.y), __builtin_bit_cast(bf16x2, rv.y), part, false);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.z), __builtin_bit_cast(bf16x2, rv.z), part, false);
+          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.w), __builtin_bit_cast(bf16x2, rv.w), part, false);
+        }
+      }
+      const bool pos = part + __shfl_xor(part, 32) > 0.f;
       const float lower1 = __uint_as_float(__float_as_uint(w1) & kKeyMask);
       const float upper2 = __uint_as_float((__float_as_uint(w2) & kKeyMask) + 32u);
       // |fp32 MFMA score - exact| <= 64 * 2^-23 * sum_k |x_k R_kj| <= 64 * 2^-23 |x| |R_j|;
@@ -235,21 +247,43 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
       const int bucket = pos ? (int)jstar : (int)jstar + half;
 
       const int tok = tok_wave + nb * 32 + (lane & 31);
-      const bool mine = lane < 32 && tok < L;
-      if (mine && cert) bout[tok] = bucket;
-      uint64_t need = __ballot(mine && !cert);
-      if (fallback_rows && lane == 0 && need) atomicAdd(fallback_rows, (uint32_t)__popcll(need));
-      while (need) {
-        const int q = __ffsll((unsigned long long)need) - 1;
-        need &= need - 1;
-        const int ftok = tok_wave + nb * 32 + q;
-        xfb[wave][lane] = (double)bf16_to_f32(xbase[(size_t)ftok * kHeadDim + lane]);
-        __builtin_amdgcn_wave_barrier();
-        const int bk = exact_bucket<uint16_t>(xfb[wave], rhr, half);
-        if (lane == 0) bout[ftok] = bk;
-        __builtin_amdgcn_wave_barrier();
-      }
+      // rows the fp32 margin cannot settle are marked -1 and settled in fp64
+      // by hash_settle_kernel, so no wave of this block waits on them
+      if (lane < 32 && tok < L) bout[tok] = cert ? bucket : -1;
     }
+  }
+}
+
+// Rows marked -1 by hash_bf16_kernel: one wave per 64 consecutive rows of
+// buckets[b][H][R][L] finds the marked ones and recomputes each in fp64.
+__global__ __launch_bounds__(256) void hash_settle_kernel(
+    const uint16_t* __restrict__ qk, const uint16_t* __restrict__ rot,
+    int32_t* __restrict__ buckets, uint32_t* __restrict__ fallback_rows, int heads, int L,
+    int half, int rounds, int64_t rows) {
+  __shared__ double xs[4][kHeadDim];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * kWave;
+  if (row0 >= rows) return;
+  const int64_t row = row0 + lane;
+  const bool marked = row < rows && buckets[row] < 0;
+  uint64_t need = __ballot(marked);
+  if (fallback_rows && lane == 0 && need) atomicAdd(fallback_rows, (uint32_t)__popcll(need));
+  while (need) {
+    const int q = __ffsll((unsigned long long)need) - 1;
+    need &= need - 1;
+    const int64_t f = row0 + q;   // flat index into buckets[b][H][R][L]
+    const int i = (int)(f % L);
+    const int64_t seg = f / L;
+    const int r = (int)(seg % rounds);
+    const int64_t bh = seg / rounds;
+    const int h = (int)(bh % heads);
+    xs[wave][lane] = (double)bf16_to_f32(qk[(bh * L + i) * kHeadDim + lane]);
+    __builtin_amdgcn_wave_barrier();
+    const int bk = exact_bucket<uint16_t>(xs[wave], rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim,
+                                          half);
+    if (lane == 0) buckets[f] = bk;
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -300,6 +334,9 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
   hipLaunchKernelGGL(hash_bf16_kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
                      fallback_rows, s.heads, s.len, half, s.rounds);
+  hipLaunchKernelGGL(hash_settle_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
+                     fallback_rows, s.heads, s.len, half, s.rounds, rows);
   return hipGetLastError();
 }
 
