@@ -15,7 +15,6 @@ bounded sample of the same workload on this host's cores.
     python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
 """
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -54,33 +53,14 @@ def algorithmic(w):
     }
 
 
-def source_digest(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:12]
-
-
-KERNEL_SOURCES = {
-    "attend": ["lsh_sparse_attention_hash_amd/csrc/attend.hip",
-               "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
-    "hash": ["lsh_sparse_attention_hash_amd/csrc/hash.hip",
-             "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
-    "combine": ["lsh_sparse_attention_hash_amd/csrc/combine.hip",
-                "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
-    "sort": ["lsh_sparse_attention_hash_amd/csrc/sort.hip",
-             "lsh_sparse_attention_hash_amd/csrc/lsh_device.h"],
-}
-
-
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current source of that kernel (else None)."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    from lsh_sparse_attention_hash_amd.rocprof_summary import source_digest
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
-    digest = source_digest(KERNEL_SOURCES[kernel])
+    digest = source_digest(kernel)
     pat = re.compile(r"^\|\s*%s\s*\|\s*%s\s*\|\s*([0-9a-f]+)\s*\|\s*([0-9.eE+]+)\s*\|" %
                      (kernel, workload))
     for line in open(path):
