@@ -10,8 +10,9 @@
 // twice a proven bound on the fp32 accumulation error (plus the fp64 rounding
 // of the defining sum), so that its bucket is provably the one of the fp64
 // definition; the winner's sign then comes from an exact-sign dot product.
-// Other rows are marked and recomputed in fp64, in the defining order, by a
-// second kernel.  fp32 inputs are scored in fp64 directly.
+// Other rows are listed in LDS and recomputed in fp64, in the defining order,
+// by the whole workgroup once its rounds are done.  fp32 inputs are scored in
+// fp64 directly.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -70,6 +71,95 @@ __device__ int exact_bucket(const double* x, const T* rot_hr, int half) {
 }
 
 // ---------------------------------------------------------------------------
+// Rows the fp32 margin cannot certify are settled in fp64 by the whole
+// workgroup: thread t owns directions t, t + 256, ..., and the next
+// direction's row (8 loads of 16 B) is in flight while the current one is
+// accumulated.  Each direction's sum runs k ascending from 0.0 (the products
+// of two bf16 values are exact, so the fused multiply-add rounds exactly like
+// the defining sum).
+constexpr int kSettleCap = 1024;   // listed rows per workgroup before a flush
+
+__device__ __forceinline__ void settle_take(double s, int j, double& best, int& besti) {
+  if (s > best || (s == best && j < besti)) { best = s; besti = j; }
+}
+
+__device__ __forceinline__ double dot_fp64(const uint4 (&r)[8], const double* x) {
+  double acc = 0.0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    asm volatile("" ::: "memory");   // x is read from LDS 8 values at a time
+    const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fma(x[8 * c + 2 * e], (double)bf16lo(w[e]), acc);
+      acc = fma(x[8 * c + 2 * e + 1], (double)bf16hi(w[e]), acc);
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void load_dir(uint4 (&r)[8], const uint16_t* rhr, int j, int half) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    r[c] = j < half ? load16(rhr + (size_t)j * kHeadDim + 8 * c) : make_uint4(0, 0, 0, 0);
+}
+
+struct SettleLds {
+  double xs[kHeadDim];
+  double wbest[kHashWaves];
+  int wbesti[kHashWaves];
+};
+
+// Settles list[0..n): entry (r << 8) | t is token tok0 + t of round r.  Called
+// by all threads of the workgroup; returns after every listed row is written.
+__device__ void settle_rows(const uint32_t* list, int n, const uint16_t* xbh, const uint16_t* rot_h,
+                            int32_t* out_bh, int tok0, int L, int half, SettleLds& sl) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  for (int e = 0; e < n; ++e) {
+    const uint32_t ent = list[e];
+    const int r = (int)(ent >> 8);
+    const int tok = tok0 + (int)(ent & 255u);
+    const uint16_t* rhr = rot_h + (size_t)r * half * kHeadDim;
+    uint4 cur[8];
+    load_dir(cur, rhr, threadIdx.x, half);
+    if (threadIdx.x < kHeadDim)
+      sl.xs[threadIdx.x] = (double)bf16_to_f32(xbh[(size_t)tok * kHeadDim + threadIdx.x]);
+    __syncthreads();
+    double best = -INFINITY;
+    int besti = INT_MAX;
+    for (int j = threadIdx.x; j < half; j += kHashTokWG) {
+      uint4 nxt[8];
+      load_dir(nxt, rhr, j + kHashTokWG, half);
+      const double s = dot_fp64(cur, sl.xs);
+      settle_take(s, j, best, besti);
+      settle_take(-s, j + half, best, besti);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) cur[c] = nxt[c];
+    }
+    // larger value wins, lower index on equal values: a total order, so any
+    // reduction tree finds the first maximum
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const double ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(besti, off);
+      settle_take(ob, oi, best, besti);
+    }
+    if (lane == 0) {
+      sl.wbest[wave] = best;
+      sl.wbesti[wave] = besti;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int w = 1; w < kHashWaves; ++w) settle_take(sl.wbest[w], sl.wbesti[w], best, besti);
+      out_bh[(size_t)r * L + tok] = besti;
+    }
+    __syncthreads();   // xs and wbest are rewritten by the next row
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Keys: the fp32 score with its 5 low mantissa bits replaced by the direction's
 // offset inside its 32-direction tile (the lane-half bit 4 of that offset is
 // added after the halves merge).  Magnitude keys |key| order like |score| up to
@@ -99,6 +189,9 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
     int half, int rounds) {
   __shared__ __attribute__((aligned(16))) uint16_t rs[2][kStageRows * kRowStride];
   __shared__ float gram_part[kHashWaves];
+  __shared__ uint32_t settle_list[kSettleCap];
+  __shared__ int settle_n, settle_over;
+  __shared__ SettleLds settle_lds;
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -106,6 +199,13 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
   const size_t bh = (size_t)blockIdx.z * heads + h;
   const int tok_wave = blockIdx.x * kHashTokWG + wave * kHashTokWave;
   const uint16_t* xbase = qk + bh * (size_t)L * kHeadDim;
+  const uint16_t* rot_h = rot + (size_t)h * rounds * half * kHeadDim;
+  int32_t* out_bh = buckets + bh * rounds * (size_t)L;
+  const int tok0 = blockIdx.x * kHashTokWG;
+  if (threadIdx.x == 0) {
+    settle_n = 0;
+    settle_over = 0;
+  }
 
   // B operand (x^T, k x token): lane holds x[token = lane%32][k = 8*(lane/32) + 16*ks + 0..7].
   bf16x8 xf[2][4];
@@ -247,44 +347,45 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
       const int bucket = pos ? (int)jstar : (int)jstar + half;
 
       const int tok = tok_wave + nb * 32 + (lane & 31);
-      // rows the fp32 margin cannot settle are marked -1 and settled in fp64
-      // by hash_settle_kernel, so no wave of this block waits on them
-      if (lane < 32 && tok < L) bout[tok] = cert ? bucket : -1;
+      // rows the fp32 margin cannot certify are listed and settled in fp64
+      // later, so no wave waits on them inside the round
+      if (lane < 32 && tok < L) {
+        if (cert) {
+          bout[tok] = bucket;
+        } else {
+          const int k = atomicAdd(&settle_n, 1);
+          if (k < kSettleCap) {
+            settle_list[k] = ((uint32_t)r << 8) | (uint32_t)(tok - tok0);
+          } else {   // list full: marked in place, found again below
+            bout[tok] = -1;
+            settle_over = 1;
+          }
+        }
+      }
     }
   }
-}
-
-// Rows marked -1 by hash_bf16_kernel: one wave per 64 consecutive rows of
-// buckets[b][H][R][L] finds the marked ones and recomputes each in fp64.
-__global__ __launch_bounds__(256) void hash_settle_kernel(
-    const uint16_t* __restrict__ qk, const uint16_t* __restrict__ rot,
-    int32_t* __restrict__ buckets, uint32_t* __restrict__ fallback_rows, int heads, int L,
-    int half, int rounds, int64_t rows) {
-  __shared__ double xs[4][kHeadDim];
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * kWave;
-  if (row0 >= rows) return;
-  const int64_t row = row0 + lane;
-  const bool marked = row < rows && buckets[row] < 0;
-  uint64_t need = __ballot(marked);
-  if (fallback_rows && lane == 0 && need) atomicAdd(fallback_rows, (uint32_t)__popcll(need));
-  while (need) {
-    const int q = __ffsll((unsigned long long)need) - 1;
-    need &= need - 1;
-    const int64_t f = row0 + q;   // flat index into buckets[b][H][R][L]
-    const int i = (int)(f % L);
-    const int64_t seg = f / L;
-    const int r = (int)(seg % rounds);
-    const int64_t bh = seg / rounds;
-    const int h = (int)(bh % heads);
-    xs[wave][lane] = (double)bf16_to_f32(qk[(bh * L + i) * kHeadDim + lane]);
-    __builtin_amdgcn_wave_barrier();
-    const int bk = exact_bucket<uint16_t>(xs[wave], rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim,
-                                          half);
-    if (lane == 0) buckets[f] = bk;
-    __builtin_amdgcn_wave_barrier();
+  __syncthreads();
+  const int n = min(settle_n, kSettleCap);
+  if (n) settle_rows(settle_list, n, xbase, rot_h, out_bh, tok0, L, half, settle_lds);
+  uint32_t settled = n;
+  if (settle_over) {
+    // Only when more than kSettleCap rows of this workgroup were uncertain:
+    // collect the rows marked -1 round by round (this workgroup's own
+    // writes, visible after the barrier) and settle them.
+    for (int r = 0; r < rounds; ++r) {
+      if (threadIdx.x == 0) settle_n = 0;
+      __syncthreads();
+      const int tok = tok0 + threadIdx.x;
+      if (tok < L && out_bh[(size_t)r * L + tok] < 0)
+        settle_list[atomicAdd(&settle_n, 1)] = ((uint32_t)r << 8) | threadIdx.x;
+      __syncthreads();
+      const int m = settle_n;
+      if (m) settle_rows(settle_list, m, xbase, rot_h, out_bh, tok0, L, half, settle_lds);
+      settled += m;
+      __syncthreads();   // settle_n is reset for the next round
+    }
   }
+  if (fallback_rows && threadIdx.x == 0 && settled) atomicAdd(fallback_rows, settled);
 }
 
 // fp32 inputs: every row in fp64 (one wave per (token, round) row).
@@ -334,9 +435,6 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
   hipLaunchKernelGGL(hash_bf16_kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
                      fallback_rows, s.heads, s.len, half, s.rounds);
-  hipLaunchKernelGGL(hash_settle_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
-                     fallback_rows, s.heads, s.len, half, s.rounds, rows);
   return hipGetLastError();
 }
 

@@ -153,6 +153,25 @@ def test_hash_matches_exactly_on_skewed_and_tied_inputs(B):
     assert int(host(f.fallback_rows)[0]) > 0   # ties can only be settled by the fp64 path
 
 
+def test_hash_settles_more_uncertain_rows_than_one_list_holds(B):
+    """A workgroup of 256 tokens whose rows are all uncertain (zero vectors
+    tie everywhere) over 8 rounds lists 2048 rows, more than its LDS list
+    holds: the rows that do not fit are found again and settled.  The second
+    workgroup's 64 tokens (L = 320) carry integer ties."""
+    w = synth.Workload("overflow", 1, 1, 320, 64, 32, 8, 64, True, True, "bf16", 22)
+    g = np.random.default_rng(23)
+    qk = g.integers(-1, 2, size=(1, 1, 320, 64)).astype(np.float32)
+    qk[0, 0, :256] = 0.0
+    rot = g.integers(-1, 2, size=(1, 8, 16, 64)).astype(np.float32)
+    inp = {"qk": synth.bf16_bits(qk), "v": synth.bf16_bits(g.standard_normal(qk.shape)),
+           "rot": synth.bf16_bits(rot)}
+    f = run_gpu(B, w, inp)
+    ref = oracle.hash(synth.to_f64(inp["qk"], "bf16"), synth.to_f64(inp["rot"], "bf16"), 32, 8)
+    assert np.array_equal(host(f.buckets), ref)
+    assert (ref[0, 0, :, :256] == 0).all()   # all-zero rows take the first index
+    assert int(host(f.fallback_rows)[0]) >= 256 * 8
+
+
 # --------------------------------------------------------------- full size
 def sampled_parity(B, w, n_hash, n_rows, seed):
     say(f"[parity-full] {w}")
