@@ -72,70 +72,78 @@ __device__ int exact_bucket(const double* x, const T* rot_hr, int half) {
 
 // ---------------------------------------------------------------------------
 // Rows the fp32 margin cannot certify are settled in fp64 by the whole
-// workgroup: thread t owns directions t, t + 256, ..., and the next
-// direction's row (8 loads of 16 B) is in flight while the current one is
-// accumulated.  Each direction's sum runs k ascending from 0.0 (the products
-// of two bf16 values are exact, so the fused multiply-add rounds exactly like
-// the defining sum).
-constexpr int kSettleCap = 1024;   // listed rows per workgroup before a flush
+// workgroup once its rounds are done: thread t owns directions t, t + 256,
+// ... of the row's rotation and loads each as 8 x 16 B.  Each direction's sum
+// runs k ascending from 0.0 (the products of two bf16 values are exact, so
+// the fused multiply-add rounds exactly like the defining sum).
+constexpr int kSettleCap = 1024;   // rows listed per workgroup; the rest are marked in place
 
 __device__ __forceinline__ void settle_take(double s, int j, double& best, int& besti) {
   if (s > best || (s == best && j < besti)) { best = s; besti = j; }
 }
 
-__device__ __forceinline__ double dot_fp64(const uint4 (&r)[8], const double* x) {
+__device__ __forceinline__ double dot_fp64(const uint4 (&r)[8], const uint32_t (&xw)[kHeadDim / 2]) {
   double acc = 0.0;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    asm volatile("" ::: "memory");   // x is read from LDS 8 values at a time
     const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = fma(x[8 * c + 2 * e], (double)bf16lo(w[e]), acc);
-      acc = fma(x[8 * c + 2 * e + 1], (double)bf16hi(w[e]), acc);
+      const uint32_t xv = xw[4 * c + e];
+      acc = fma((double)bf16lo(xv), (double)bf16lo(w[e]), acc);
+      acc = fma((double)bf16hi(xv), (double)bf16hi(w[e]), acc);
     }
   }
   return acc;
 }
 
-__device__ __forceinline__ void load_dir(uint4 (&r)[8], const uint16_t* rhr, int j, int half) {
+__device__ __forceinline__ void load_dir(uint4 (&r)[8], const uint16_t* rhr, int j) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    r[c] = j < half ? load16(rhr + (size_t)j * kHeadDim + 8 * c) : make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < 8; ++c) r[c] = load16(rhr + (size_t)j * kHeadDim + 8 * c);
 }
 
 struct SettleLds {
-  double xs[kHeadDim];
-  double wbest[kHashWaves];
-  int wbesti[kHashWaves];
+  double wbest[2][kHashWaves];   // per-wave winners, double-buffered by row parity
+  int wbesti[2][kHashWaves];
 };
 
-// Settles list[0..n): entry (r << 8) | t is token tok0 + t of round r.  Called
-// by all threads of the workgroup; returns after every listed row is written.
-__device__ void settle_rows(const uint32_t* list, int n, const uint16_t* xbh, const uint16_t* rot_h,
+// Settles list[0..n): entry (r << 8) | t is token tok0 + t of round r, whose
+// x is row t of xsm (bf16, kRowStride apart).  Called by all threads of the
+// workgroup; every listed row is written when it returns.
+__device__ void settle_rows(const uint32_t* list, int n, const uint16_t* xsm, const uint16_t* rot_h,
                             int32_t* out_bh, int tok0, int L, int half, SettleLds& sl) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
+  const int iters = (half + kHashTokWG - 1) / kHashTokWG;
+  const size_t rot_round = (size_t)half * kHeadDim;
   for (int e = 0; e < n; ++e) {
     const uint32_t ent = list[e];
-    const int r = (int)(ent >> 8);
-    const int tok = tok0 + (int)(ent & 255u);
-    const uint16_t* rhr = rot_h + (size_t)r * half * kHeadDim;
-    uint4 cur[8];
-    load_dir(cur, rhr, threadIdx.x, half);
-    if (threadIdx.x < kHeadDim)
-      sl.xs[threadIdx.x] = (double)bf16_to_f32(xbh[(size_t)tok * kHeadDim + threadIdx.x]);
-    __syncthreads();
+    const int t = (int)(ent & 255u);
+    const uint16_t* rhr = rot_h + (size_t)(ent >> 8) * rot_round;
+    uint32_t xw[kHeadDim / 2];   // x as packed bf16 pairs, widened per use
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 u = *reinterpret_cast<const uint4*>(xsm + t * kRowStride + 8 * c);
+      xw[4 * c] = u.x;
+      xw[4 * c + 1] = u.y;
+      xw[4 * c + 2] = u.z;
+      xw[4 * c + 3] = u.w;
+    }
     double best = -INFINITY;
     int besti = INT_MAX;
-    for (int j = threadIdx.x; j < half; j += kHashTokWG) {
-      uint4 nxt[8];
-      load_dir(nxt, rhr, j + kHashTokWG, half);
-      const double s = dot_fp64(cur, sl.xs);
-      settle_take(s, j, best, besti);
-      settle_take(-s, j + half, best, besti);
+    for (int it = 0; it < iters; ++it) {
+      // opaque to the compiler, so the widened x is not hoisted out of the
+      // loop (64 doubles would not fit beside the main loop's registers)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) cur[c] = nxt[c];
+      for (int q = 0; q < kHeadDim / 2; ++q) asm volatile("" : "+v"(xw[q]));
+      const int j = threadIdx.x + it * kHashTokWG;
+      if (j < half) {
+        uint4 rv[8];
+        load_dir(rv, rhr, j);
+        const double s = dot_fp64(rv, xw);
+        settle_take(s, j, best, besti);
+        settle_take(-s, j + half, best, besti);
+      }
     }
     // larger value wins, lower index on equal values: a total order, so any
     // reduction tree finds the first maximum
@@ -146,16 +154,15 @@ __device__ void settle_rows(const uint32_t* list, int n, const uint16_t* xbh, co
       settle_take(ob, oi, best, besti);
     }
     if (lane == 0) {
-      sl.wbest[wave] = best;
-      sl.wbesti[wave] = besti;
+      sl.wbest[e & 1][wave] = best;
+      sl.wbesti[e & 1][wave] = besti;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int w = 1; w < kHashWaves; ++w) settle_take(sl.wbest[w], sl.wbesti[w], best, besti);
-      out_bh[(size_t)r * L + tok] = besti;
+      for (int w = 1; w < kHashWaves; ++w) settle_take(sl.wbest[e & 1][w], sl.wbesti[e & 1][w], best, besti);
+      out_bh[(size_t)(ent >> 8) * L + tok0 + t] = besti;
     }
-    __syncthreads();   // xs and wbest are rewritten by the next row
   }
 }
 
@@ -364,9 +371,19 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
       }
     }
   }
-  __syncthreads();
+  __syncthreads();   // the list is complete and the staging buffer is free
   const int n = min(settle_n, kSettleCap);
-  if (n) settle_rows(settle_list, n, xbase, rot_h, out_bh, tok0, L, half, settle_lds);
+  if (n == 0) return;
+  // the workgroup's x rows (still in registers) into LDS, for the fp64 pass
+  uint16_t* xsm = &rs[0][0];   // 256 rows of kRowStride
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      store16(&xsm[(wave * kHashTokWave + nb * 32 + (lane & 31)) * kRowStride + 8 * (lane >> 5) + 16 * ks],
+              __builtin_bit_cast(uint4, xf[nb][ks]));
+  __syncthreads();
+  settle_rows(settle_list, n, xsm, rot_h, out_bh, tok0, L, half, settle_lds);
   uint32_t settled = n;
   if (settle_over) {
     // Only when more than kSettleCap rows of this workgroup were uncertain:
@@ -380,9 +397,9 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
         settle_list[atomicAdd(&settle_n, 1)] = ((uint32_t)r << 8) | threadIdx.x;
       __syncthreads();
       const int m = settle_n;
-      if (m) settle_rows(settle_list, m, xbase, rot_h, out_bh, tok0, L, half, settle_lds);
+      if (m) settle_rows(settle_list, m, xsm, rot_h, out_bh, tok0, L, half, settle_lds);
       settled += m;
-      __syncthreads();   // settle_n is reset for the next round
+      __syncthreads();   // the list and settle_n are rewritten for the next round
     }
   }
   if (fallback_rows && threadIdx.x == 0 && settled) atomicAdd(fallback_rows, settled);
