@@ -400,3 +400,119 @@ int oracle_lsh_forward(int batch, int heads, int len, int dim, int n_buckets,
   return oracle_lsh_combine(batch, heads, len, dim, rounds, o_rounds, lse,
                             inv_perm, v, y);
 }
+
+/* ------------------------------------------------------- local attention */
+
+/* Local chunked self-attention, the second attention of the method (page 4,
+ * "The Reformer - Pushing the limits of language modeling", sections
+ * "Approach / What changed" and "Takeaways": the sequence is cut into chunks
+ * of length l_c, and each chunk also sees a configurable number of chunks
+ * before and after it).  No hashing and no sorting: the candidates of token i
+ * in chunk c = i / l_c are the positions of chunks max(0, c - before) ..
+ * min(C - 1, c + after), C = L / l_c, filtered by the causal rule (j <= i)
+ * and the self-mask (j != i).  Readings where the page is silent: the score,
+ * the softmax and the empty-set rule are those of the LSH attention above
+ * (Q = K with unit-length keys, 1/sqrt(d), y_i = v_i when no candidate is
+ * left), so before = 1, after = 0 is exactly LSH attention with B = 1, R = 1.
+ *
+ * Layouts: qk, v, y [batch][heads][L][d] double; lse [batch][heads][L]
+ * double (-inf = no candidate), all in original order. */
+static int local_keeps(const shape_t* s, int i, int j) {
+  if (s->causal && j > i) return 0;      /* the future stays hidden */
+  if (s->self_mask && j == i) return 0;  /* a token never attends to itself */
+  return 1;
+}
+
+static void local_one(const shape_t* s, int before, int after,
+                      const double* qk, const double* v, int64_t bh, int i,
+                      double* score, double* y, double* lse) {
+  const int d = s->dim;
+  const double* xs = qk + bh * (int64_t)s->len * d;
+  const double* vs = v + bh * (int64_t)s->len * d;
+  const int nchunks = s->len / s->chunk;
+  const int c = i / s->chunk;
+  const int c_lo = (c - before > 0) ? c - before : 0;
+  const int c_hi = (c + after < nchunks - 1) ? c + after : nchunks - 1;
+  const int lo = c_lo * s->chunk;
+  const int hi = (c_hi + 1) * s->chunk;
+  const double* xi = xs + (int64_t)i * d;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  double mx = -INFINITY;
+  int n = 0;
+  for (int j = lo; j < hi; ++j) {
+    if (!local_keeps(s, i, j)) continue;
+    const double* xj = xs + (int64_t)j * d;
+    double dot = 0.0;
+    for (int k = 0; k < d; ++k) dot = dot + xi[k] * xj[k];
+    double nj = norm2(xj, d);
+    if (nj < ORACLE_NORM_EPS) nj = ORACLE_NORM_EPS;
+    score[j - lo] = dot / nj * inv_sqrt_d;
+    if (score[j - lo] > mx) mx = score[j - lo];
+    ++n;
+  }
+  if (n == 0) {
+    for (int k = 0; k < d; ++k) y[k] = vs[(int64_t)i * d + k];
+    *lse = -INFINITY;
+    return;
+  }
+  double sum = 0.0;
+  for (int j = lo; j < hi; ++j)
+    if (local_keeps(s, i, j)) sum += exp(score[j - lo] - mx);
+  const double lse_i = mx + log(sum);
+  for (int k = 0; k < d; ++k) y[k] = 0.0;
+  for (int j = lo; j < hi; ++j) {
+    if (!local_keeps(s, i, j)) continue;
+    const double p = exp(score[j - lo] - lse_i);
+    const double* vj = vs + (int64_t)j * d;
+    for (int k = 0; k < d; ++k) y[k] += p * vj[k];
+  }
+  *lse = lse_i;
+}
+
+/* idx[n] are flat indices (b*heads + h)*L + i into y rows / lse. */
+int oracle_local_attend_rows(int batch, int heads, int len, int dim, int chunk,
+                             int before, int after, int causal, int self_mask,
+                             const double* qk, const double* v, int64_t n,
+                             const int64_t* idx, double* y, double* lse) {
+  shape_t s;
+  if (make_shape(&s, batch, heads, len, dim, 1, 1, chunk, causal, self_mask))
+    return -1;
+  if (before < 0 || after < 0) return -1;
+  const int64_t total = (int64_t)batch * heads * len;
+  for (int64_t q = 0; q < n; ++q)
+    if (idx[q] < 0 || idx[q] >= total) return -1;
+  /* the window spans at most min(C, before + 1 + after) chunks */
+  const int nchunks = len / chunk;
+  const int64_t span = (int64_t)before + 1 + after;
+  const int64_t wmax = (span < nchunks ? span : nchunks) * (int64_t)chunk;
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    double* score = (double*)malloc(sizeof(double) * (size_t)wmax);
+    if (!score) bad |= 1;
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t q = 0; q < n; ++q) {
+      if (!score) continue;
+      local_one(&s, before, after, qk, v, idx[q] / len, (int)(idx[q] % len),
+                score, y + q * dim, lse + q);
+    }
+    free(score);
+  }
+  return bad ? -1 : 0;
+}
+
+int oracle_local_attend(int batch, int heads, int len, int dim, int chunk,
+                        int before, int after, int causal, int self_mask,
+                        const double* qk, const double* v, double* y,
+                        double* lse) {
+  const int64_t total = (int64_t)batch * heads * len;
+  if (total <= 0) return -1;
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)total);
+  if (!idx) return -1;
+  for (int64_t f = 0; f < total; ++f) idx[f] = f;
+  const int rc = oracle_local_attend_rows(batch, heads, len, dim, chunk, before,
+                                          after, causal, self_mask, qk, v,
+                                          total, idx, y, lse);
+  free(idx);
+  return rc;
+}

@@ -16,6 +16,8 @@ file.  Function map:
                                            Chunking", "Implementation Reading"]
     combine(...)   y                      ["Multiple Hash Rounds"]
     forward(...)   all of the above
+    local_attend() y, lse of local chunked attention (no hashing) [Reformer
+                   overview page, "Approach / What changed", "Takeaways"]
     *_rows(...)    the same on a sample of rows (for full-size parity)
     candidates()   attended positions of one query (window-rule tests)
 """
@@ -61,10 +63,13 @@ def _bind(lib):
     lib.oracle_lsh_combine.argtypes = [_I] * 5 + [_P] * 5
     lib.oracle_lsh_combine_rows.argtypes = [_I] * 5 + [_P] * 4 + [_I64, _P, _P]
     lib.oracle_lsh_forward.argtypes = [_I] * 9 + [_P] * 9
+    lib.oracle_local_attend.argtypes = [_I] * 9 + [_P] * 4
+    lib.oracle_local_attend_rows.argtypes = [_I] * 9 + [_P, _P, _I64, _P, _P, _P]
     for name in ("oracle_lsh_hash", "oracle_lsh_hash_rows", "oracle_lsh_sort",
                  "oracle_lsh_attend", "oracle_lsh_attend_rows",
                  "oracle_lsh_candidates", "oracle_lsh_combine",
-                 "oracle_lsh_combine_rows", "oracle_lsh_forward"):
+                 "oracle_lsh_combine_rows", "oracle_lsh_forward",
+                 "oracle_local_attend", "oracle_local_attend_rows"):
         getattr(lib, name).restype = _I
     return lib
 
@@ -243,3 +248,30 @@ def forward(qk, v, rot, n_buckets: int, n_rounds: int, chunk: int, causal: bool,
                                       _ptr(out["inv_perm"]), _ptr(out["o_rounds"]),
                                       _ptr(out["lse"]), _ptr(out["y"])), "forward")
     return out
+
+
+def local_attend(qk, v, chunk: int, before: int, after: int, causal: bool, self_mask: bool):
+    """(y[b][h][L][d], lse[b][h][L]) of local chunked attention: each chunk
+    sees `before` chunks before it and `after` chunks after it."""
+    qk, v = _f64(qk), _f64(v)
+    b, h, L, d = _dims(qk)
+    y = np.empty((b, h, L, d))
+    lse = np.empty((b, h, L))
+    _check(_load().oracle_local_attend(b, h, L, d, chunk, before, after, int(causal),
+                                       int(self_mask), _ptr(qk), _ptr(v), _ptr(y),
+                                       _ptr(lse)), "local_attend")
+    return y, lse
+
+
+def local_attend_rows(qk, v, chunk: int, before: int, after: int, causal: bool,
+                      self_mask: bool, flat_idx):
+    """(y[n][d], lse[n]) of local attention at flat indices (b*heads + h)*L + i."""
+    qk, v = _f64(qk), _f64(v)
+    b, h, L, d = _dims(qk)
+    idx = _i64(flat_idx).ravel()
+    y = np.empty((idx.shape[0], d))
+    lse = np.empty(idx.shape[0])
+    _check(_load().oracle_local_attend_rows(b, h, L, d, chunk, before, after, int(causal),
+                                            int(self_mask), _ptr(qk), _ptr(v), idx.shape[0],
+                                            _ptr(idx), _ptr(y), _ptr(lse)), "local_attend_rows")
+    return y, lse

@@ -56,6 +56,19 @@ MUTANTS = {
     "self_only_returns_zero": (
         "for (int k = 0; k < d; ++k) y[k] = v[(bh * L + i) * d + k];",
         "for (int k = 0; k < d; ++k) y[k] = 0.0;"),
+    "local_ignores_following_chunks": (
+        "const int c_hi = (c + after < nchunks - 1) ? c + after : nchunks - 1;",
+        "const int c_hi = c;"),
+    "local_one_chunk_too_few_before": (
+        "const int c_lo = (c - before > 0) ? c - before : 0;",
+        "const int c_lo = (c - before > 0) ? c - before + 1 : 0;"),
+    "local_causal_ignored": (
+        "if (s->causal && j > i) return 0;", ";"),
+    "local_self_mask_ignored": (
+        "if (s->self_mask && j == i) return 0;", ";"),
+    "local_empty_row_returns_zero": (
+        "for (int k = 0; k < d; ++k) y[k] = vs[(int64_t)i * d + k];",
+        "for (int k = 0; k < d; ++k) y[k] = 0.0;"),
 }
 
 

@@ -370,3 +370,98 @@ def test_invalid_arguments_raise():
         oracle.forward(x, x, np.zeros((1, 1, 1, 8)), 3, 1, 10, False, False)   # odd B
     with pytest.raises(ValueError):
         oracle.forward(x, x, np.zeros((1, 1, 0, 8)), 1, 1, 64, False, False)   # L % m
+
+
+# ------------------------------------------------ local chunked attention
+# yomu.fyi summary ("The Reformer - Pushing the limits of language modeling"),
+# "Approach / What changed" and "Takeaways": chunks of length l_c that also
+# see a configurable number of preceding and following chunks.
+def local_allowed(L, m, before, after, causal, self_mask):
+    ci = np.arange(L) // m
+    a = (ci[None, :] >= ci[:, None] - before) & (ci[None, :] <= ci[:, None] + after)
+    return a & dense_allowed(L, causal, self_mask)
+
+
+@pytest.mark.parametrize("before,after,causal,self_mask", [
+    (1, 1, False, True), (2, 0, True, True), (0, 2, False, False), (0, 0, True, False),
+    (3, 1, True, True), (1, 4, False, True)])
+def test_local_attention_is_banded_attention(before, after, causal, self_mask):
+    L, d, m = 384, 64, 64
+    x = rand(60, 2, 1, L, d)
+    v = rand(61, 2, 1, L, d)
+    y, lse = oracle.local_attend(x, v, m, before, after, causal, self_mask)
+    allowed = local_allowed(L, m, before, after, causal, self_mask)
+    for b in range(2):
+        yb, lb = np_masked_softmax_attention(x[b, 0], v[b, 0], allowed)
+        np.testing.assert_allclose(y[b, 0], yb, rtol=0, atol=1e-12)
+        assert np.array_equal(np.isneginf(lse[b, 0]), np.isneginf(lb))
+        fin = ~np.isneginf(lb)
+        np.testing.assert_allclose(lse[b, 0][fin], lb[fin], rtol=0, atol=1e-12)
+
+
+def test_local_whole_window_is_dense_attention():
+    """A window wider than the sequence is plain softmax attention (textbook
+    form: softmax(Q K^T / sqrt(d)) V with Q = X, K = unit-length rows of X)."""
+    L, d, m = 256, 64, 64
+    x = rand(62, 1, 1, L, d)
+    v = rand(63, 1, 1, L, d)
+    y, lse = oracle.local_attend(x, v, m, 7, 9, False, False)
+    k = x[0, 0] / np.linalg.norm(x[0, 0], axis=1, keepdims=True)
+    a = x[0, 0] @ k.T / math.sqrt(d)
+    p = np.exp(a - a.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(y[0, 0], (p / p.sum(1, keepdims=True)) @ v[0, 0], rtol=0, atol=1e-12)
+    ref_lse = a.max(1) + np.log(p.sum(1))
+    np.testing.assert_allclose(lse[0, 0], ref_lse, rtol=0, atol=1e-12)
+
+
+def test_local_one_chunk_back_is_lsh_without_hashing():
+    """before = 1, after = 0 is the LSH path with one bucket and one round."""
+    L, d, m = 320, 64, 64
+    x = rand(64, 1, 2, L, d)
+    v = rand(65, 1, 2, L, d)
+    for causal in (False, True):
+        y, lse = oracle.local_attend(x, v, m, 1, 0, causal, True)
+        out = oracle.forward(x, v, np.zeros((2, 1, 0, d)), 1, 1, m, causal, True)
+        np.testing.assert_array_equal(y, out["y"])
+        np.testing.assert_array_equal(lse, out["lse"][:, :, 0])
+
+
+def test_local_single_neighbour_closed_forms():
+    """With chunks of one token and the self-mask, a token sees exactly one
+    other token: y_i is that token's value and lse_i its single score."""
+    L, d = 40, 64
+    x = rand(66, 1, 1, L, d)
+    v = rand(67, 1, 1, L, d)
+    X, V = x[0, 0], v[0, 0]
+
+    def score(i, j):
+        return float(X[i] @ X[j]) / (math.sqrt(float(X[j] @ X[j])) * 8.0)
+
+    y, lse = oracle.local_attend(x, v, 1, 1, 0, True, True)       # previous token only
+    assert np.array_equal(y[0, 0, 0], V[0]) and lse[0, 0, 0] == -np.inf
+    np.testing.assert_array_equal(y[0, 0, 1:], V[:-1])
+    np.testing.assert_allclose(lse[0, 0, 1:], [score(i, i - 1) for i in range(1, L)],
+                               rtol=0, atol=1e-13)
+    y, lse = oracle.local_attend(x, v, 1, 0, 1, False, True)      # next token only
+    np.testing.assert_array_equal(y[0, 0, :-1], V[1:])
+    assert np.array_equal(y[0, 0, -1], V[-1]) and lse[0, 0, -1] == -np.inf
+    y, lse = oracle.local_attend(x, v, 2, 0, 0, False, True)      # chunk partner only
+    partner = np.arange(L) ^ 1
+    np.testing.assert_array_equal(y[0, 0], V[partner])
+    np.testing.assert_allclose(lse[0, 0], [score(i, partner[i]) for i in range(L)],
+                               rtol=0, atol=1e-13)
+
+
+def test_local_rows_match_full_and_bad_arguments_raise():
+    L, d, m = 256, 64, 64
+    x = rand(68, 2, 2, L, d)
+    v = rand(69, 2, 2, L, d)
+    y, lse = oracle.local_attend(x, v, m, 1, 2, True, True)
+    idx = np.random.default_rng(70).integers(0, 4 * L, 300)
+    yr, lr = oracle.local_attend_rows(x, v, m, 1, 2, True, True, idx)
+    np.testing.assert_array_equal(yr, y.reshape(-1, d)[idx])
+    np.testing.assert_array_equal(lr, lse.ravel()[idx])
+    with pytest.raises(ValueError):
+        oracle.local_attend(x, v, m, -1, 0, False, False)
+    with pytest.raises(ValueError):
+        oracle.local_attend(x, v, 100, 1, 0, False, False)   # L % l_c != 0
