@@ -53,6 +53,19 @@ def algorithmic(w):
     }
 
 
+def algorithmic_local(w):
+    """Local attention, one launch: x and v read once, y and lse written; the
+    flops are the score and value products of every query's window."""
+    T = w.batch * w.heads * w.seq_len
+    d = w.head_dim
+    el = 2 if w.dtype == "bf16" else 4
+    C = w.seq_len // w.chunk_len
+    after = 0 if w.causal else w.look_after
+    keys = sum(min(C - 1, c + after) - max(0, c - w.look_before) + 1 for c in range(C)) * w.chunk_len
+    return {"bytes": T * (2 * d * el + 4 * d + 4),
+            "flops": w.batch * w.heads * w.chunk_len * keys * 4 * d}
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current source of that kernel (else None)."""
@@ -95,6 +108,93 @@ def cpu_baseline(w, inputs):
                                      f"; tokens/s scaled by {w.heads // hs}x to all heads")}
 
 
+def copy_calibration(torch):
+    """Plain device copies of known size, after the timed steps: the reference
+    that scales the HBM byte counters of a profiled run."""
+    nbytes = 512 << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 x {nbytes} B device copies")
+
+
+def bench_local(args, w, inputs, binding, torch):
+    """Local chunked attention: one step is one lsh_local_attend call."""
+    qk = binding.to_device(inputs["qk"], w.dtype)
+    v = binding.to_device(inputs["v"], w.dtype)
+    loc = binding.Local(binding.config_for(w), w.look_before, w.look_after)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        loc.run(qk, v)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        loc.run(qk, v)
+        ev[k][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    per = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s); local_attend {per:.4f} ms")
+    if args.copy_calibration:
+        copy_calibration(torch)
+    work = algorithmic_local(w)
+    t = per * 1e-3
+    ach = work["bytes"] / t / 1e9
+    roof = {"kernel": "local_bf16_kernel" if w.dtype == "bf16" else "local_f32_kernel",
+            "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic("local", w.name)}
+    result = {
+        "metric": "local chunked attention fwd tokens/s (all heads) at L=64K; % of HBM roofline",
+        "value": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "head_dim": w.head_dim, "chunk_len": w.chunk_len,
+                   "look_before": w.look_before, "look_after": w.look_after,
+                   "causal": w.causal, "self_mask": w.self_mask},
+        "roofline": roof,
+        "kernels": {"local_attend": {"ms": round(per, 5), "algorithmic_bytes": work["bytes"],
+                                     "GBps": round(ach, 1), "algorithmic_flops": work["flops"],
+                                     "TFLOPs": round(work["flops"] / t / 1e12, 2)}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline_local(w, inputs)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    return result
+
+
+def cpu_baseline_local(w, inputs):
+    """The fp64 oracle's local attention over every head of the workload."""
+    threads = len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    from lsh_sparse_attention_hash_amd import synth
+    from oracle import oracle
+    oracle.build(force=False)
+    qk = synth.to_f64(inputs["qk"], w.dtype)
+    v = synth.to_f64(inputs["v"], w.dtype)
+    t0 = time.perf_counter()
+    oracle.local_attend(qk, v, w.chunk_len, w.look_before, w.look_after, w.causal, w.self_mask)
+    dt = time.perf_counter() - t0
+    return {"value": w.batch * w.seq_len / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"all {w.heads} heads (batch {w.batch}, L={w.seq_len}), full fp64 local "
+                      f"attention"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +225,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     log(f"[bench] workload {w}")
     inputs = synth.make_inputs(w)
+    if w.is_local:
+        print(json.dumps(bench_local(args, w, inputs, binding, torch)), flush=True)
+        return
     qk = binding.to_device(inputs["qk"], w.dtype)
     v = binding.to_device(inputs["v"], w.dtype)
     rot = binding.to_device(inputs["rot"], w.dtype)
@@ -164,13 +267,7 @@ def main():
         + ", ".join(f"{n} {per[n]:.4f}" for n in names))
 
     if args.copy_calibration:
-        nbytes = 512 << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: 3 x {nbytes} B device copies")
+        copy_calibration(torch)
 
     work = algorithmic(w)
     kernels = {}

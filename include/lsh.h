@@ -168,6 +168,35 @@ lsh_status lsh_unsort_combine(const lsh_config* cfg, const float* o_rounds,
                               const float* lse, const int32_t* inv_perm,
                               const void* v, float* y, void* stream);
 
+/*
+ * lsh_local_attend -- local chunked self-attention: the method's attention
+ * without hashing.
+ * Follows: Reformer overview page "The Reformer - Pushing the limits of
+ * language modeling" (yomu.fyi), sections "Approach / What changed" and
+ * "Takeaways": the sequence is cut into chunks of length l_c and each chunk
+ * also attends to a configurable number of chunks before and after it.
+ *
+ *   cfg       batch, heads, seq_len, head_dim, chunk_len, causal, self_mask
+ *             and dtype as above; n_buckets and n_rounds are not used
+ *   n_before  chunks before the query's chunk in its window (>= 0)
+ *   n_after   chunks after it (>= 0; no effect when causal)
+ *   qk, v     [b][H][L][d]   dtype
+ *   y         [b][H][L][d]   fp32 output, original order
+ *   lse       [b][H][L]      fp32 output (-inf where no key is left)
+ *
+ * The keys of query i in chunk c = i / m are the tokens j of chunks
+ * max(0, c - n_before) .. min(L/m - 1, c + n_after) with j <= i if causal and
+ * j != i if self_mask; with s_ij as for lsh_chunk_attend,
+ *   lse_i = log sum_j exp(s_ij),   y_i = sum_j exp(s_ij - lse_i) v_j,
+ * and y_i = v_i, lse_i = -inf when there is no key (self-mask only).
+ * n_before = 1, n_after = 0 is LSH attention with n_buckets = n_rounds = 1.
+ * Windows wider than the sequence are clipped to it.  bf16 inputs use bf16
+ * matrix-core products with fp32 accumulation; fp32 inputs use fp32.
+ */
+lsh_status lsh_local_attend(const lsh_config* cfg, int32_t n_before,
+                            int32_t n_after, const void* qk, const void* v,
+                            float* y, float* lse, void* stream);
+
 /* Static description of a status code. */
 const char* lsh_status_string(lsh_status status);
 

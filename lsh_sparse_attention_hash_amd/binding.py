@@ -26,7 +26,8 @@ LSH_F32 = 0
 LSH_BF16 = 1
 
 EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attend",
-           "lsh_unsort_combine", "lsh_status_string", "lsh_last_error", "lsh_version")
+           "lsh_unsort_combine", "lsh_local_attend", "lsh_status_string", "lsh_last_error",
+           "lsh_version")
 
 
 class LshError(RuntimeError):
@@ -54,7 +55,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsh_sort.argtypes = [cfgp, P, P, P, P, SZ, P]
     lib.lsh_chunk_attend.argtypes = [cfgp, P, P, P, P, P, P, P]
     lib.lsh_unsort_combine.argtypes = [cfgp, P, P, P, P, P, P]
-    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine"):
+    lib.lsh_local_attend.argtypes = [cfgp, I32, I32, P, P, P, P, P]
+    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
+              "lsh_local_attend"):
         getattr(lib, f).restype = I32
     lib.lsh_status_string.argtypes = [I32]
     lib.lsh_status_string.restype = ctypes.c_char_p
@@ -166,6 +169,32 @@ def lsh_unsort_combine(cfg: LshConfig, o_rounds, lse, inv_perm, v, y, stream=Non
     _check("lsh_unsort_combine",
            _lib.lsh_unsort_combine(ctypes.byref(cfg), _ptr(o_rounds), _ptr(lse), _ptr(inv_perm),
                                    _ptr(v), _ptr(y), _stream(stream)))
+
+
+def lsh_local_attend(cfg: LshConfig, n_before: int, n_after: int, qk, v, y, lse, stream=None):
+    b, H, L, d = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim
+    dt = _dtype_of(cfg)
+    _expect(qk, (b, H, L, d), dt, "qk")
+    _expect(v, (b, H, L, d), dt, "v")
+    _expect(y, (b, H, L, d), torch.float32, "y")
+    _expect(lse, (b, H, L), torch.float32, "lse")
+    _check("lsh_local_attend",
+           _lib.lsh_local_attend(ctypes.byref(cfg), int(n_before), int(n_after), _ptr(qk), _ptr(v),
+                                 _ptr(y), _ptr(lse), _stream(stream)))
+
+
+class Local:
+    """Output buffers of local chunked attention for one problem size."""
+
+    def __init__(self, cfg: LshConfig, n_before: int, n_after: int, device="cuda"):
+        b, H, L, d = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim
+        self.cfg, self.n_before, self.n_after = cfg, n_before, n_after
+        self.y = torch.empty((b, H, L, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((b, H, L), dtype=torch.float32, device=device)
+
+    def run(self, qk, v, stream=None):
+        lsh_local_attend(self.cfg, self.n_before, self.n_after, qk, v, self.y, self.lse, stream)
+        return self.y
 
 
 class Forward:

@@ -164,6 +164,29 @@ lsh_status lsh_unsort_combine(const lsh_config* cfg, const float* o_rounds, cons
                   "lsh_unsort_combine");
 }
 
+lsh_status lsh_local_attend(const lsh_config* cfg, int32_t n_before, int32_t n_after,
+                            const void* qk, const void* v, float* y, float* lse, void* stream) {
+  if (!cfg) return fail(LSH_ERR_INVALID_ARGUMENT, "cfg is NULL");
+  // no hashing: the bucket and round fields are not used
+  lsh_config c = *cfg;
+  c.n_buckets = 1;
+  c.n_rounds = 1;
+  lsh::Shape s;
+  bool empty = false;
+  LSH_TRY(check_config(&c, &s, &empty));
+  if (n_before < 0 || n_after < 0)
+    return fail(LSH_ERR_INVALID_ARGUMENT, "n_before %d and n_after %d must be >= 0", n_before,
+                n_after);
+  if (empty) return ok();
+  LSH_TRY(check_ptr(qk, "qk"));
+  LSH_TRY(check_ptr(v, "v"));
+  LSH_TRY(check_ptr(y, "y"));
+  LSH_TRY(check_ptr(lse, "lse"));
+  return launched(lsh::launch_local(s, n_before, n_after, qk, v, y, lse,
+                                    static_cast<hipStream_t>(stream)),
+                  "lsh_local_attend");
+}
+
 const char* lsh_status_string(lsh_status status) {
   switch (status) {
     case LSH_OK: return "ok";

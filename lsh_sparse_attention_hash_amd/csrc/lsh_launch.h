@@ -30,4 +30,7 @@ hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const in
 hipError_t launch_combine(const Shape& s, const float* o_rounds, const float* lse,
                           const int32_t* inv_perm, const void* v, float* y, hipStream_t stream);
 
+hipError_t launch_local(const Shape& s, int before, int after, const void* qk, const void* v,
+                        float* y, float* lse, hipStream_t stream);
+
 }  // namespace lsh

@@ -61,6 +61,14 @@ class Workload:
     seed: int
     n_clusters: int = 0        # 0: qk ~ N(0,1); else Gaussian mixture
     spread: float = 0.3
+    # local chunked attention (no hashing): chunks before / after each chunk in
+    # its window; None for the LSH workloads
+    look_before: "int | None" = None
+    look_after: "int | None" = None
+
+    @property
+    def is_local(self) -> bool:
+        return self.look_before is not None
 
     @property
     def tokens(self) -> int:
@@ -83,6 +91,10 @@ WORKLOADS = {
     "long": Workload("long", 1, 8, 65536, 64, 1024, 8, 64, True, True, "bf16", 4),
     "verylong": Workload("verylong", 1, 4, 524288, 64, 8192, 2, 64, True, True, "bf16", 5,
                          n_clusters=256),
+    # local chunked attention: one chunk of look-back and one of look-ahead
+    # (encoder-style, so not causal), the headline shape otherwise
+    "local_long": Workload("local_long", 1, 8, 65536, 64, 1, 1, 64, False, True, "bf16", 6,
+                           look_before=1, look_after=1),
 }
 
 

@@ -130,3 +130,43 @@ def test_b1_needs_no_rotation():
     # rot may be NULL when B == 1; qk still required
     assert call_hash(c, qk=None, rot=None) == B.LSH_ERR_INVALID_ARGUMENT
     assert b"qk" in B.library().lsh_last_error()
+
+
+def call_local(c, before=1, after=1, qk=FAKE, v=FAKE, y=FAKE, lse=FAKE):
+    return B.library().lsh_local_attend(ctypes.byref(c), before, after, qk, v, y, lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=32), B.LSH_ERR_UNSUPPORTED),
+    (dict(chunk_len=128), B.LSH_ERR_UNSUPPORTED),
+    (dict(seq_len=100), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(self_mask=-1), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(batch=2048, heads=1024, seq_len=1024), B.LSH_ERR_INVALID_ARGUMENT),
+])
+def test_local_attend_rejects_invalid_config(kw, status):
+    assert call_local(cfg(**kw)) == status
+    assert B.library().lsh_last_error()
+
+
+def test_local_attend_ignores_bucket_and_round_fields():
+    # validation stops at the (fake) pointers only if the config itself passed:
+    # a NULL y is reported, not the unused n_buckets / n_rounds
+    c = cfg(n_buckets=7, n_rounds=0)
+    assert call_local(c, y=None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert b"y is NULL" in B.library().lsh_last_error()
+
+
+def test_local_attend_rejects_bad_windows_and_pointers():
+    c = cfg()
+    assert call_local(c, before=-1) == B.LSH_ERR_INVALID_ARGUMENT
+    assert call_local(c, after=-2) == B.LSH_ERR_INVALID_ARGUMENT
+    assert b"n_before" in B.library().lsh_last_error()
+    assert call_local(c, qk=None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert call_local(c, v=ctypes.c_void_p(0x10008)) == B.LSH_ERR_INVALID_ARGUMENT
+    assert call_local(c, lse=None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert B.library().lsh_local_attend(None, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    for kw in (dict(batch=0), dict(heads=0), dict(seq_len=0)):
+        assert call_local(cfg(**kw), qk=None, v=None, y=None, lse=None) == B.LSH_OK
