@@ -37,7 +37,9 @@
  *   - causal masking compares ORIGINAL positions (j <= i);
  *   - self-mask: token i is never its own candidate in any round; if no round
  *     leaves any candidate, y_i = v_i (the token attends only to itself);
- *   - rounds combine as a multiset: a key found in k rounds counts k times.
+ *   - rounds combine as a multiset: a key found in k rounds counts k times
+ *     (oracle_lsh_attend); oracle_lsh_attend_union gives the set reading
+ *     instead, where every key of the union counts once.
  *
  * Layouts (all row-major, all arrays owned by the caller):
  *   qk, v      [batch][heads][L][d]            double
@@ -214,11 +216,32 @@ static double norm2(const double* x, int d) {
   return sqrt(acc);
 }
 
-/* o (length d) and lse of one query row. */
+/* Number of rounds r' in which key j is a candidate of query i (the same
+ * bucket and, in round r', a sorted slot inside the window of i's chunk; the
+ * causal and self rules do not depend on the round). */
+static int rounds_sharing(const shape_t* s, const int32_t* buckets,
+                          const int32_t* inv_perm, int64_t bh, int i, int j) {
+  int count = 0;
+  for (int r = 0; r < s->rounds; ++r) {
+    const int64_t seg = bh * s->rounds + r;
+    const int32_t* bk = buckets + seg * s->len;
+    const int32_t* ip = inv_perm + seg * s->len;
+    if (bk[i] != bk[j]) continue;
+    const int c = ip[i] / s->chunk;
+    const int first = (c > 0) ? (c - 1) * s->chunk : 0;
+    if (ip[j] >= first && ip[j] < (c + 1) * s->chunk) ++count;
+  }
+  return count;
+}
+
+/* o (length d) and lse of one query row.  With inv_perm == NULL the rounds
+ * are a multiset; otherwise (set semantics of the union over rounds) the
+ * score of key j is lowered by log c_ij, c_ij = rounds_sharing(i, j) >= 1, so
+ * that after the round combine every key of the union weighs once. */
 static void attend_one(const shape_t* s, const double* qk, const double* v,
                        const int32_t* buckets, const int32_t* perm,
-                       int64_t seg, int slot, int32_t* cand, double* score,
-                       double* o, double* lse) {
+                       const int32_t* inv_perm, int64_t seg, int slot,
+                       int32_t* cand, double* score, double* o, double* lse) {
   const int d = s->dim;
   const int64_t bh = seg / s->rounds;
   const double* xs = qk + bh * (int64_t)s->len * d;
@@ -237,6 +260,8 @@ static void attend_one(const shape_t* s, const double* qk, const double* v,
     double nj = norm2(xj, d);
     if (nj < ORACLE_NORM_EPS) nj = ORACLE_NORM_EPS;
     score[a] = dot / nj * inv_sqrt_d;
+    if (inv_perm)
+      score[a] -= log((double)rounds_sharing(s, buckets, inv_perm, bh, i, cand[a]));
     if (score[a] > mx) mx = score[a];
   }
   double sum = 0.0;
@@ -250,13 +275,11 @@ static void attend_one(const shape_t* s, const double* qk, const double* v,
   *lse = l;
 }
 
-/* idx[n] are flat indices seg*L + slot into o_rounds rows / lse. */
-int oracle_lsh_attend_rows(int batch, int heads, int len, int dim,
-                           int n_buckets, int rounds, int chunk, int causal,
-                           int self_mask, const double* qk, const double* v,
-                           const int32_t* buckets, const int32_t* perm,
-                           int64_t n, const int64_t* idx, double* o,
-                           double* lse) {
+static int attend_rows(int batch, int heads, int len, int dim, int n_buckets,
+                       int rounds, int chunk, int causal, int self_mask,
+                       const double* qk, const double* v, const int32_t* buckets,
+                       const int32_t* perm, const int32_t* inv_perm, int64_t n,
+                       const int64_t* idx, double* o, double* lse) {
   shape_t s;
   if (make_shape(&s, batch, heads, len, dim, n_buckets, rounds, chunk, causal,
                  self_mask))
@@ -273,13 +296,24 @@ int oracle_lsh_attend_rows(int batch, int heads, int len, int dim,
 #pragma omp for schedule(dynamic, 64)
     for (int64_t q = 0; q < n; ++q) {
       if (!cand || !score) continue;
-      attend_one(&s, qk, v, buckets, perm, idx[q] / len, (int)(idx[q] % len),
-                 cand, score, o + q * dim, lse + q);
+      attend_one(&s, qk, v, buckets, perm, inv_perm, idx[q] / len,
+                 (int)(idx[q] % len), cand, score, o + q * dim, lse + q);
     }
     free(cand);
     free(score);
   }
   return bad ? -1 : 0;
+}
+
+/* idx[n] are flat indices seg*L + slot into o_rounds rows / lse. */
+int oracle_lsh_attend_rows(int batch, int heads, int len, int dim,
+                           int n_buckets, int rounds, int chunk, int causal,
+                           int self_mask, const double* qk, const double* v,
+                           const int32_t* buckets, const int32_t* perm,
+                           int64_t n, const int64_t* idx, double* o,
+                           double* lse) {
+  return attend_rows(batch, heads, len, dim, n_buckets, rounds, chunk, causal,
+                     self_mask, qk, v, buckets, perm, NULL, n, idx, o, lse);
 }
 
 int oracle_lsh_attend(int batch, int heads, int len, int dim, int n_buckets,
@@ -295,6 +329,42 @@ int oracle_lsh_attend(int batch, int heads, int len, int dim, int n_buckets,
                                         rounds, chunk, causal, self_mask, qk,
                                         v, buckets, perm, total, idx, o_rounds,
                                         lse);
+  free(idx);
+  return rc;
+}
+
+/* Set semantics of the union over rounds (Reformer study note, "Multiple
+ * Hash Rounds": N(i) is the union over r of the per-round neighbourhoods, as
+ * a set): per-round o and lse (sorted order, like oracle_lsh_attend) with
+ * every candidate's score lowered by the log of the number of rounds in
+ * which it is a candidate.  oracle_lsh_combine of these is the softmax over
+ * the set union.  inv_perm as returned by oracle_lsh_sort. */
+int oracle_lsh_attend_union_rows(int batch, int heads, int len, int dim,
+                                 int n_buckets, int rounds, int chunk,
+                                 int causal, int self_mask, const double* qk,
+                                 const double* v, const int32_t* buckets,
+                                 const int32_t* perm, const int32_t* inv_perm,
+                                 int64_t n, const int64_t* idx, double* o,
+                                 double* lse) {
+  if (!inv_perm) return -1;
+  return attend_rows(batch, heads, len, dim, n_buckets, rounds, chunk, causal,
+                     self_mask, qk, v, buckets, perm, inv_perm, n, idx, o, lse);
+}
+
+int oracle_lsh_attend_union(int batch, int heads, int len, int dim,
+                            int n_buckets, int rounds, int chunk, int causal,
+                            int self_mask, const double* qk, const double* v,
+                            const int32_t* buckets, const int32_t* perm,
+                            const int32_t* inv_perm, double* o_rounds,
+                            double* lse) {
+  const int64_t total = (int64_t)batch * heads * rounds * len;
+  if (total <= 0) return -1;
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)total);
+  if (!idx) return -1;
+  for (int64_t f = 0; f < total; ++f) idx[f] = f;
+  const int rc = oracle_lsh_attend_union_rows(
+      batch, heads, len, dim, n_buckets, rounds, chunk, causal, self_mask, qk, v,
+      buckets, perm, inv_perm, total, idx, o_rounds, lse);
   free(idx);
   return rc;
 }

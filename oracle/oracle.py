@@ -16,6 +16,8 @@ file.  Function map:
                                            Chunking", "Implementation Reading"]
     combine(...)   y                      ["Multiple Hash Rounds"]
     forward(...)   all of the above
+    attend_union() o_rounds, lse with set semantics of the round union
+                   ["Multiple Hash Rounds"]; forward_union() end to end
     local_attend() y, lse of local chunked attention (no hashing) [Reformer
                    overview page, "Approach / What changed", "Takeaways"]
     *_rows(...)    the same on a sample of rows (for full-size parity)
@@ -63,13 +65,16 @@ def _bind(lib):
     lib.oracle_lsh_combine.argtypes = [_I] * 5 + [_P] * 5
     lib.oracle_lsh_combine_rows.argtypes = [_I] * 5 + [_P] * 4 + [_I64, _P, _P]
     lib.oracle_lsh_forward.argtypes = [_I] * 9 + [_P] * 9
+    lib.oracle_lsh_attend_union.argtypes = [_I] * 9 + [_P] * 7
+    lib.oracle_lsh_attend_union_rows.argtypes = [_I] * 9 + [_P] * 5 + [_I64, _P, _P, _P]
     lib.oracle_local_attend.argtypes = [_I] * 9 + [_P] * 4
     lib.oracle_local_attend_rows.argtypes = [_I] * 9 + [_P, _P, _I64, _P, _P, _P]
     for name in ("oracle_lsh_hash", "oracle_lsh_hash_rows", "oracle_lsh_sort",
                  "oracle_lsh_attend", "oracle_lsh_attend_rows",
                  "oracle_lsh_candidates", "oracle_lsh_combine",
                  "oracle_lsh_combine_rows", "oracle_lsh_forward",
-                 "oracle_local_attend", "oracle_local_attend_rows"):
+                 "oracle_local_attend", "oracle_local_attend_rows",
+                 "oracle_lsh_attend_union", "oracle_lsh_attend_union_rows"):
         getattr(lib, name).restype = _I
     return lib
 
@@ -193,6 +198,38 @@ def attend_rows(qk, v, buckets, perm, n_buckets: int, chunk: int, causal: bool,
     return o, lse
 
 
+def attend_union(qk, v, buckets, perm, inv_perm, n_buckets: int, chunk: int, causal: bool,
+                 self_mask: bool):
+    """Per-round (o_rounds, lse), sorted order, with each candidate's score
+    lowered by the log of the number of rounds that share it; combine() of
+    these is the softmax over the SET union of the rounds' candidates."""
+    qk, v, bk, pm, ip = _f64(qk), _f64(v), _i32(buckets), _i32(perm), _i32(inv_perm)
+    b, h, L, d = _dims(qk)
+    R = bk.shape[2]
+    o = np.empty((b, h, R, L, d))
+    lse = np.empty((b, h, R, L))
+    _check(_load().oracle_lsh_attend_union(b, h, L, d, n_buckets, R, chunk, int(causal),
+                                           int(self_mask), _ptr(qk), _ptr(v), _ptr(bk), _ptr(pm),
+                                           _ptr(ip), _ptr(o), _ptr(lse)), "attend_union")
+    return o, lse
+
+
+def attend_union_rows(qk, v, buckets, perm, inv_perm, n_buckets: int, chunk: int, causal: bool,
+                      self_mask: bool, flat_idx):
+    """attend_union at flat indices seg*L + slot (sorted order)."""
+    qk, v, bk, pm, ip = _f64(qk), _f64(v), _i32(buckets), _i32(perm), _i32(inv_perm)
+    b, h, L, d = _dims(qk)
+    R = bk.shape[2]
+    idx = _i64(flat_idx).ravel()
+    o = np.empty((idx.shape[0], d))
+    lse = np.empty(idx.shape[0])
+    _check(_load().oracle_lsh_attend_union_rows(b, h, L, d, n_buckets, R, chunk, int(causal),
+                                                int(self_mask), _ptr(qk), _ptr(v), _ptr(bk),
+                                                _ptr(pm), _ptr(ip), idx.shape[0], _ptr(idx),
+                                                _ptr(o), _ptr(lse)), "attend_union_rows")
+    return o, lse
+
+
 def candidates(buckets, perm, n_buckets: int, chunk: int, causal: bool, self_mask: bool,
                seg: int, slot: int) -> np.ndarray:
     """Original positions attended by the query at sorted `slot` of segment `seg`."""
@@ -275,3 +312,14 @@ def local_attend_rows(qk, v, chunk: int, before: int, after: int, causal: bool,
                                             int(self_mask), _ptr(qk), _ptr(v), idx.shape[0],
                                             _ptr(idx), _ptr(y), _ptr(lse)), "local_attend_rows")
     return y, lse
+
+
+def forward_union(qk, v, rot, n_buckets: int, n_rounds: int, chunk: int, causal: bool,
+                  self_mask: bool) -> dict:
+    """hash -> sort -> attend_union -> combine: y is the softmax over the set
+    union of the rounds' candidates."""
+    buckets = hash(qk, rot, n_buckets, n_rounds)
+    perm, inv_perm = sort(buckets)
+    o, lse = attend_union(qk, v, buckets, perm, inv_perm, n_buckets, chunk, causal, self_mask)
+    y = combine(o, lse, inv_perm, v)
+    return dict(buckets=buckets, perm=perm, inv_perm=inv_perm, o_rounds=o, lse=lse, y=y)

@@ -56,6 +56,15 @@ MUTANTS = {
     "self_only_returns_zero": (
         "for (int k = 0; k < d; ++k) y[k] = v[(bh * L + i) * d + k];",
         "for (int k = 0; k < d; ++k) y[k] = 0.0;"),
+    "union_without_count_correction": (
+        "      score[a] -= log((double)rounds_sharing(s, buckets, inv_perm, bh, i, cand[a]));",
+        "      score[a] -= 0.0;"),
+    "union_counts_every_round": (
+        "    if (bk[i] != bk[j]) continue;\n    const int c = ip[i] / s->chunk;",
+        "    const int c = ip[i] / s->chunk;"),
+    "union_window_without_predecessor": (
+        "    const int first = (c > 0) ? (c - 1) * s->chunk : 0;",
+        "    const int first = c * s->chunk;"),
     "local_ignores_following_chunks": (
         "const int c_hi = (c + after < nchunks - 1) ? c + after : nchunks - 1;",
         "const int c_hi = c;"),

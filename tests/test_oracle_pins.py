@@ -465,3 +465,86 @@ def test_local_rows_match_full_and_bad_arguments_raise():
         oracle.local_attend(x, v, m, -1, 0, False, False)
     with pytest.raises(ValueError):
         oracle.local_attend(x, v, 100, 1, 0, False, False)   # L % l_c != 0
+
+
+# ------------------------------------------------- set union over rounds
+# Reformer study note, "Multiple Hash Rounds": N(i) is the union over rounds
+# of the per-round neighbourhoods.  The set reading counts every key once.
+def np_round_candidates(buckets, perm, L, m, causal, self_mask):
+    """allowed[r][i][j]: j is a candidate of i in round r (dense, from the
+    definition: same bucket, j's sorted slot in the window of i's chunk)."""
+    R = buckets.shape[0]
+    out = np.zeros((R, L, L), bool)
+    for r in range(R):
+        slot = np.empty(L, int)
+        slot[perm[r]] = np.arange(L)
+        c = slot // m
+        first = np.maximum(c - 1, 0) * m
+        last = (c + 1) * m
+        win = (slot[None, :] >= first[:, None]) & (slot[None, :] < last[:, None])
+        out[r] = win & (buckets[r][:, None] == buckets[r][None, :])
+    return out & dense_allowed(L, causal, self_mask)[None]
+
+
+@pytest.mark.parametrize("causal,self_mask,B,R", [(True, True, 8, 3), (False, True, 4, 4),
+                                                  (True, False, 16, 2), (False, False, 2, 5)])
+def test_union_is_softmax_over_the_set_of_candidates(causal, self_mask, B, R):
+    L, d, m = 256, 64, 64
+    x = rand(80 + R, 1, 2, L, d)
+    v = rand(81 + R, 1, 2, L, d)
+    rot = rand(82 + R, 2, R, B // 2, d)
+    out = oracle.forward_union(x, v, rot, B, R, m, causal, self_mask)
+    multi = oracle.forward(x, v, rot, B, R, m, causal, self_mask)
+    repeats = 0
+    for h in range(2):
+        cand = np_round_candidates(out["buckets"][0, h], out["perm"][0, h], L, m, causal,
+                                   self_mask)
+        repeats += int((cand.sum(0) > 1).sum())
+        y, lse = np_masked_softmax_attention(x[0, h], v[0, h], cand.any(0))
+        np.testing.assert_allclose(out["y"][0, h], y, rtol=0, atol=1e-12)
+    assert repeats > 0                                   # the two readings differ here
+    assert np.abs(out["y"] - multi["y"]).max() > 1e-3
+
+
+def test_union_with_one_round_is_the_multiset_path():
+    L, d, m = 320, 64, 64
+    x = rand(90, 2, 1, L, d)
+    v = rand(91, 2, 1, L, d)
+    rot = rand(92, 1, 1, 8, d)
+    out = oracle.forward_union(x, v, rot, 16, 1, m, True, True)
+    multi = oracle.forward(x, v, rot, 16, 1, m, True, True)
+    np.testing.assert_array_equal(out["o_rounds"], multi["o_rounds"])
+    np.testing.assert_array_equal(out["lse"], multi["lse"])
+
+
+def test_union_of_identical_rounds_is_one_round():
+    """R copies of one rotation: the union is the single round's set, so the
+    per-round outputs equal the one-round outputs and y is one round's."""
+    L, d, m = 256, 64, 64
+    x = rand(93, 1, 1, L, d)
+    v = rand(94, 1, 1, L, d)
+    one = rand(95, 1, 1, 8, d)
+    out = oracle.forward_union(x, v, np.repeat(one, 3, axis=1), 16, 3, m, True, True)
+    ref = oracle.forward(x, v, one, 16, 1, m, True, True)
+    for r in range(3):
+        np.testing.assert_allclose(out["o_rounds"][:, :, r], ref["o_rounds"][:, :, 0],
+                                   rtol=0, atol=1e-13)
+        lse = out["lse"][:, :, r]
+        fin = ~np.isneginf(ref["lse"][:, :, 0])
+        # every key is shared by all 3 rounds: each round's sum is a third of it
+        np.testing.assert_allclose(lse[fin] + math.log(3), ref["lse"][:, :, 0][fin],
+                                   rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["y"], ref["y"], rtol=0, atol=1e-13)
+
+
+def test_union_rows_match_full():
+    L, d, m = 256, 64, 64
+    x = rand(96, 1, 2, L, d)
+    v = rand(97, 1, 2, L, d)
+    rot = rand(98, 2, 3, 4, d)
+    out = oracle.forward_union(x, v, rot, 8, 3, m, True, True)
+    idx = np.random.default_rng(99).integers(0, 2 * 3 * L, 300)
+    o, lse = oracle.attend_union_rows(x, v, out["buckets"], out["perm"], out["inv_perm"], 8, m,
+                                      True, True, idx)
+    np.testing.assert_array_equal(o, out["o_rounds"].reshape(-1, d)[idx])
+    np.testing.assert_array_equal(lse, out["lse"].ravel()[idx])
