@@ -33,14 +33,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic(w):
+def algorithmic(w, union=False):
     """Algorithmic work per launch of each kernel (bytes or flops)."""
     N = w.token_rounds
     T = w.batch * w.heads * w.seq_len
     d = w.head_dim
     el = 2 if w.dtype == "bf16" else 4
     rot = w.heads * w.n_rounds * (w.n_buckets // 2) * d * el
-    return {
+    out = {
         # x read once, rotations read, bucket ids written; contraction flops
         "hash": {"bytes": T * d * el + rot + 4 * N, "flops": N * d * w.n_buckets},
         # keys read twice, perm and inv_perm written
@@ -51,6 +51,12 @@ def algorithmic(w):
         # per token-round: o row, lse and inv_perm read; per token-head: y row written
         "combine": {"bytes": N * (4 * d + 8) + T * 4 * d},
     }
+    if union:
+        # round-key table: built from buckets and inv_perm (8 B per token-round
+        # read, stride keys per token written), then gathered with every key row
+        stride = (w.n_rounds + 3) // 4 * 4
+        out["attend"]["bytes"] += 8 * N + 4 * stride * T + 4 * stride * N
+    return out
 
 
 def algorithmic_local(w):
@@ -83,7 +89,7 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, inputs):
+def cpu_baseline(w, inputs, union=False):
     """The fp64 oracle on a bounded sample of the workload: every head for the
     shapes up to L = 64K (a few seconds on a many-core host), one head of the
     half-million-token shape."""
@@ -97,14 +103,16 @@ def cpu_baseline(w, inputs):
     v = synth.to_f64(inputs["v"][:, :hs], w.dtype)
     rot = synth.to_f64(inputs["rot"][:hs], w.dtype)
     t0 = time.perf_counter()
-    oracle.forward(qk, v, rot, w.n_buckets, w.n_rounds, w.chunk_len, w.causal, w.self_mask)
+    (oracle.forward_union if union else oracle.forward)(qk, v, rot, w.n_buckets, w.n_rounds,
+                                                        w.chunk_len, w.causal, w.self_mask)
     dt = time.perf_counter() - t0
     full_est = dt * w.heads / hs
     return {"value": w.batch * w.seq_len / full_est, "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{hs} of {w.heads} heads (batch {w.batch}, L={w.seq_len}, all "
-                      f"{w.n_rounds} rounds), full fp64 forward (hash, sort, attend, "
-                      f"combine)" + ("" if hs == w.heads else
+                      f"{w.n_rounds} rounds), full fp64 forward (hash, sort, "
+                      f"{'set-union attend' if union else 'attend'}, combine)" +
+                      ("" if hs == w.heads else
                                      f"; tokens/s scaled by {w.heads // hs}x to all heads")}
 
 
@@ -202,6 +210,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--union", action="store_true",
+                    help="set reading of the union over rounds (lsh_chunk_attend_union)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run plain device copies of known size "
                          "(reference for HBM counter scaling)")
@@ -234,8 +244,9 @@ def main():
     f = binding.Forward(binding.config_for(w))
     stream = torch.cuda.current_stream()
 
+    attend = f.attend_union if args.union else f.attend
     for _ in range(args.warmup):
-        f.run(qk, v, rot)
+        f.run(qk, v, rot, union=args.union)
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
@@ -253,7 +264,7 @@ def main():
         e[1].record(stream)
         f.sort()
         e[2].record(stream)
-        f.attend(qk, v)
+        attend(qk, v)
         e[3].record(stream)
         f.combine(v)
         e[4].record(stream)
@@ -269,7 +280,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
 
-    work = algorithmic(w)
+    work = algorithmic(w, args.union)
     kernels = {}
     for n in names:
         t = per[n] * 1e-3
@@ -292,10 +303,11 @@ def main():
         roof = {"kernel": {"attend": "attend_bf16_kernel", "combine": "combine_kernel"}[dom],
                 "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = measured_traffic(dom, w.name)
+    roof["traffic"] = None if args.union else measured_traffic(dom, w.name)
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if not args.union else
+        "LSH-attention fwd tokens/s, set union of rounds (all heads) at L=64K; % of roofline",
         "value": round(w.batch * w.seq_len / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -307,7 +319,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) / Gaussian-mixture inputs, random rotations)",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+        "config": {"workload": w.name + ("+union" if args.union else ""), "batch": w.batch,
+                   "heads": w.heads, "seq_len": w.seq_len,
                    "head_dim": w.head_dim, "n_buckets": w.n_buckets, "n_rounds": w.n_rounds,
                    "chunk_len": w.chunk_len, "causal": w.causal, "self_mask": w.self_mask,
                    "qk": ("gaussian mixture, %d clusters" % w.n_clusters) if w.n_clusters
@@ -319,7 +332,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w, inputs)
+        result["cpu_baseline"] = cpu_baseline(w, inputs, args.union)
         log(f"[bench] cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 

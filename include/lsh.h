@@ -148,6 +148,35 @@ lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk,
                             const int32_t* perm, float* o_rounds, float* lse,
                             void* stream);
 
+/* Bytes of device workspace lsh_chunk_attend_union needs for cfg (0 for an
+ * empty or unsupported problem). */
+size_t lsh_union_workspace_bytes(const lsh_config* cfg);
+
+/*
+ * lsh_chunk_attend_union -- lsh_chunk_attend with the SET reading of the
+ * union over rounds.
+ * Follows: Reformer study note, section "Multiple Hash Rounds" (the
+ * neighbourhood of token i is the union over r of the per-round
+ * neighbourhoods), read as a set: a key found by several rounds counts once.
+ *
+ *   qk, v, buckets, perm, o_rounds, lse   as for lsh_chunk_attend
+ *   inv_perm   [b][H][R][L] int32 (from lsh_sort)
+ *   workspace  device scratch of at least lsh_union_workspace_bytes(cfg)
+ *              bytes (else LSH_ERR_WORKSPACE_TOO_SMALL); contents ignored
+ *
+ * As lsh_chunk_attend, except that the score of key j for query i is
+ * s_ij - log(c_ij), c_ij = the number of rounds in which j is a key of i
+ * (same bucket, j's sorted slot in the window of i's chunk; c_ij >= 1).
+ * lsh_unsort_combine of these outputs is then the softmax of s_ij over the
+ * set union of the rounds' keys.  Supports n_rounds <= 16 and
+ * n_buckets * (seq_len / 64 + 1) < 2^31 (else LSH_ERR_UNSUPPORTED).
+ */
+lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk,
+                                  const void* v, const int32_t* buckets,
+                                  const int32_t* perm, const int32_t* inv_perm,
+                                  float* o_rounds, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /*
  * lsh_unsort_combine -- back to original order and combine the rounds.
  * Follows: Reformer study note, section "Multiple Hash Rounds" (the

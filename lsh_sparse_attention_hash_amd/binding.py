@@ -26,8 +26,8 @@ LSH_F32 = 0
 LSH_BF16 = 1
 
 EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attend",
-           "lsh_unsort_combine", "lsh_local_attend", "lsh_status_string", "lsh_last_error",
-           "lsh_version")
+           "lsh_unsort_combine", "lsh_union_workspace_bytes", "lsh_chunk_attend_union",
+           "lsh_local_attend", "lsh_status_string", "lsh_last_error", "lsh_version")
 
 
 class LshError(RuntimeError):
@@ -56,8 +56,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsh_chunk_attend.argtypes = [cfgp, P, P, P, P, P, P, P]
     lib.lsh_unsort_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.lsh_local_attend.argtypes = [cfgp, I32, I32, P, P, P, P, P]
+    lib.lsh_union_workspace_bytes.argtypes = [cfgp]
+    lib.lsh_union_workspace_bytes.restype = SZ
+    lib.lsh_chunk_attend_union.argtypes = [cfgp, P, P, P, P, P, P, P, P, SZ, P]
     for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
-              "lsh_local_attend"):
+              "lsh_local_attend", "lsh_chunk_attend_union"):
         getattr(lib, f).restype = I32
     lib.lsh_status_string.argtypes = [I32]
     lib.lsh_status_string.restype = ctypes.c_char_p
@@ -159,6 +162,28 @@ def lsh_chunk_attend(cfg: LshConfig, qk, v, buckets, perm, o_rounds, lse, stream
                                  _ptr(o_rounds), _ptr(lse), _stream(stream)))
 
 
+def lsh_union_workspace_bytes(cfg: LshConfig) -> int:
+    return int(_lib.lsh_union_workspace_bytes(ctypes.byref(cfg)))
+
+
+def lsh_chunk_attend_union(cfg: LshConfig, qk, v, buckets, perm, inv_perm, o_rounds, lse,
+                           workspace, stream=None):
+    b, H, L, d, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_rounds
+    dt = _dtype_of(cfg)
+    _expect(qk, (b, H, L, d), dt, "qk")
+    _expect(v, (b, H, L, d), dt, "v")
+    for t, n in ((buckets, "buckets"), (perm, "perm"), (inv_perm, "inv_perm")):
+        _expect(t, (b, H, R, L), torch.int32, n)
+    _expect(o_rounds, (b, H, R, L, d), torch.float32, "o_rounds")
+    _expect(lse, (b, H, R, L), torch.float32, "lse")
+    _check("lsh_chunk_attend_union",
+           _lib.lsh_chunk_attend_union(ctypes.byref(cfg), _ptr(qk), _ptr(v), _ptr(buckets),
+                                       _ptr(perm), _ptr(inv_perm), _ptr(o_rounds), _ptr(lse),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)))
+
+
 def lsh_unsort_combine(cfg: LshConfig, o_rounds, lse, inv_perm, v, y, stream=None):
     b, H, L, d, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_rounds
     _expect(o_rounds, (b, H, R, L, d), torch.float32, "o_rounds")
@@ -219,6 +244,7 @@ class Forward:
         nbytes = max(16, lsh_sort_workspace_bytes(cfg))
         self.workspace = torch.empty(((nbytes + 15) // 16) * 16, dtype=torch.uint8, device=device)
         self.fallback_rows = torch.zeros(1, **i32)
+        self.union_workspace = None   # allocated by the first attend_union
 
     def hash(self, qk, rot, stream=None):
         lsh_hash(self.cfg, qk, rot, self.buckets, self.fallback_rows, stream)
@@ -229,13 +255,28 @@ class Forward:
     def attend(self, qk, v, stream=None):
         lsh_chunk_attend(self.cfg, qk, v, self.buckets, self.perm, self.o_rounds, self.lse, stream)
 
+    def attend_union(self, qk, v, stream=None):
+        """The set reading of the union over rounds (see lsh_chunk_attend_union)."""
+        if self.union_workspace is None:
+            nbytes = lsh_union_workspace_bytes(self.cfg)
+            if nbytes == 0:
+                raise LshError("lsh_union_workspace_bytes", LSH_ERR_UNSUPPORTED,
+                               "shape not supported by the set-union attention")
+            self.union_workspace = torch.empty(((nbytes + 15) // 16) * 16, dtype=torch.uint8,
+                                               device=self.y.device)
+        lsh_chunk_attend_union(self.cfg, qk, v, self.buckets, self.perm, self.inv_perm,
+                               self.o_rounds, self.lse, self.union_workspace, stream)
+
     def combine(self, v, stream=None):
         lsh_unsort_combine(self.cfg, self.o_rounds, self.lse, self.inv_perm, v, self.y, stream)
 
-    def run(self, qk, v, rot, stream=None):
+    def run(self, qk, v, rot, stream=None, union=False):
         self.hash(qk, rot, stream)
         self.sort(stream)
-        self.attend(qk, v, stream)
+        if union:
+            self.attend_union(qk, v, stream)
+        else:
+            self.attend(qk, v, stream)
         self.combine(v, stream)
         return self.y
 

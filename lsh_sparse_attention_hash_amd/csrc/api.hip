@@ -78,6 +78,16 @@ lsh_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// Shapes the set-union attention supports (beyond check_config).
+lsh_status check_union(const lsh::Shape& s) {
+  if (s.rounds > 16)
+    return fail(LSH_ERR_UNSUPPORTED, "set union supports n_rounds <= 16 (got %d)", s.rounds);
+  const long long span = (long long)s.len / lsh::kChunk + 1;
+  if ((long long)s.buckets * span >= (1LL << 31))
+    return fail(LSH_ERR_UNSUPPORTED, "set union needs n_buckets * (seq_len / 64 + 1) < 2^31");
+  return LSH_OK;
+}
+
 #define LSH_TRY(expr)                 \
   do {                                \
     const lsh_status st_ = (expr);    \
@@ -146,6 +156,39 @@ lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk, const void* v
   return launched(lsh::launch_attend(s, qk, v, buckets, perm, o_rounds, lse,
                                      static_cast<hipStream_t>(stream)),
                   "lsh_chunk_attend");
+}
+
+size_t lsh_union_workspace_bytes(const lsh_config* cfg) {
+  lsh::Shape s;
+  bool empty = false;
+  if (check_config(cfg, &s, &empty) != LSH_OK || empty || check_union(s) != LSH_OK) return 0;
+  return lsh::union_workspace_bytes(s);
+}
+
+lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk, const void* v,
+                                  const int32_t* buckets, const int32_t* perm,
+                                  const int32_t* inv_perm, float* o_rounds, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  lsh::Shape s;
+  bool empty = false;
+  LSH_TRY(check_config(cfg, &s, &empty));
+  if (empty) return ok();
+  LSH_TRY(check_union(s));
+  LSH_TRY(check_ptr(qk, "qk"));
+  LSH_TRY(check_ptr(v, "v"));
+  LSH_TRY(check_ptr(buckets, "buckets"));
+  LSH_TRY(check_ptr(perm, "perm"));
+  LSH_TRY(check_ptr(inv_perm, "inv_perm"));
+  LSH_TRY(check_ptr(o_rounds, "o_rounds"));
+  LSH_TRY(check_ptr(lse, "lse"));
+  LSH_TRY(check_ptr(workspace, "workspace"));
+  const size_t need = lsh::union_workspace_bytes(s);
+  if (workspace_bytes < need)
+    return fail(LSH_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed",
+                workspace_bytes, need);
+  return launched(lsh::launch_attend_union(s, qk, v, buckets, perm, inv_perm, o_rounds, lse,
+                                           workspace, static_cast<hipStream_t>(stream)),
+                  "lsh_chunk_attend_union");
 }
 
 lsh_status lsh_unsort_combine(const lsh_config* cfg, const float* o_rounds, const float* lse,

@@ -37,7 +37,13 @@ struct AttendArgs {
   float* o;
   float* lse;
   int rounds, L, nchunks, cpw, runs_per_seg, causal, self_mask;
+  // set union over rounds: per-token round keys bucket * (C + 1) + chunk of
+  // the token's sorted slot, [b][H][L][ukey_stride] (see union_keys_kernel)
+  const int32_t* ukeys;
+  int ukey_stride;
 };
+
+constexpr int kMaxUnionRounds = 16;
 
 // ------------------------------------------------------------------- bf16
 // V^T rows hold the 128 window keys as 64 dwords (two bf16 keys each) plus 4
@@ -62,6 +68,7 @@ struct ChunkRegs {
   int2 pos;                 // original positions of the two keys
   uint4 xa, xc, va, vc;     // their x and v column blocks
   int ba, bc;               // their bucket ids
+  uint4 uk;                 // set union: 4 round keys of key 2*(t/8) + (t%8)/4
 };
 
 __device__ __forceinline__ int2 load_perm_pair(const int32_t* pm, int c, int L) {
@@ -71,9 +78,16 @@ __device__ __forceinline__ int2 load_perm_pair(const int32_t* pm, int c, int L) 
   return p;
 }
 
+template <bool UNION = false>
 __device__ __forceinline__ void gather_chunk(ChunkRegs& g, int2 pos, const uint16_t* xb,
-                                             const uint16_t* vb, const int32_t* bk) {
+                                             const uint16_t* vb, const int32_t* bk,
+                                             const int32_t* uk = nullptr, int ustride = 0) {
   const int dblk = threadIdx.x & 7;
+  if (UNION) {
+    const int blk4 = 4 * (dblk & 3);
+    const int tok = (dblk >> 2) ? pos.y : pos.x;
+    g.uk = blk4 < ustride ? load16(uk + (size_t)tok * ustride + blk4) : make_uint4(0, 0, 0, 0);
+  }
   g.pos = pos;
   g.xa = load16(xb + (size_t)pos.x * kHeadDim + 8 * dblk);
   g.xc = load16(xb + (size_t)pos.y * kHeadDim + 8 * dblk);
@@ -84,12 +98,16 @@ __device__ __forceinline__ void gather_chunk(ChunkRegs& g, int2 pos, const uint1
 }
 
 // Write a gathered chunk c into LDS half (c & 1): x rows, V transposed, and
-// per-key scale, bucket and position.
-__device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, int c) {
+// per-key scale, bucket and position (and the round keys for the set union).
+template <bool UNION = false>
+__device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, int c,
+                                             int32_t* kkey = nullptr) {
   const int tid = threadIdx.x;
   const int p = tid >> 3;          // key pair 0..31
   const int dblk = tid & 7;        // 16-byte column block
   const int row = 64 * (c & 1) + 2 * p;
+  if (UNION)
+    store16(&kkey[(row + (dblk >> 2)) * kMaxUnionRounds + 4 * (dblk & 3)], g.uk);
   store16(&sm.xs[row * kXStride + 8 * dblk], g.xa);
   store16(&sm.xs[(row + 1) * kXStride + 8 * dblk], g.xc);
   const uint32_t wa[4] = {g.va.x, g.va.y, g.va.z, g.va.w};
@@ -128,9 +146,9 @@ __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, 
   }
 }
 
-template <bool CAUSAL, bool SELF>
+template <bool CAUSAL, bool SELF, bool UNION = false>
 __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArgs& a, int64_t seg,
-                                                  int c) {
+                                                  int c, const int32_t* kkey = nullptr) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;          // 16-lane group
@@ -145,6 +163,14 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
   for (int ks = 0; ks < 2; ++ks) qf[ks] = as_bf16x8(load16(&sm.xs[qrow * kXStride + 8 * g + 32 * ks]));
   const int qb = sm.kbk[qrow];
   const int qp = sm.kpos[qrow];
+  int32_t kq[kMaxUnionRounds];   // set union: the query's round keys
+  if (UNION) {
+#pragma unroll
+    for (int q4 = 0; q4 < kMaxUnionRounds; q4 += 4) {
+      const int4 w = *reinterpret_cast<const int4*>(&kkey[qrow * kMaxUnionRounds + q4]);
+      kq[q4] = w.x; kq[q4 + 1] = w.y; kq[q4 + 2] = w.z; kq[q4 + 3] = w.w;
+    }
+  }
 
   // scores, log2-scaled: s[t][i] is key 16t + 4g + i of the window for query ql
   float s[8][4];
@@ -172,14 +198,36 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
       const int4 kp = *reinterpret_cast<const int4*>(&sm.kpos[row4]);
       kpa[0] = kp.x; kpa[1] = kp.y; kpa[2] = kp.z; kpa[3] = kp.w;
     }
+    bool oka[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bool ok = kba[i] == qb;
       if (CAUSAL && SELF) ok = ok && kpa[i] < qp;
       if (CAUSAL && !SELF) ok = ok && kpa[i] <= qp;
       if (!CAUSAL && SELF) ok = ok && kpa[i] != qp;
+      oka[i] = ok;
       const float sc = acc[i] * kva[i];
       s[t][i] = ok ? sc : -INFINITY;
+    }
+    if (UNION && __ballot(oka[0] || oka[1] || oka[2] || oka[3])) {
+      // key j of the union weighs once: its score loses log2 of the number of
+      // rounds in which it is a candidate of this query (same bucket, and its
+      // sorted slot in the query's chunk or the one before: key difference 0 or 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t* kk = &kkey[(row4 + i) * kMaxUnionRounds];
+        int cnt = 0;
+#pragma unroll
+        for (int q4 = 0; q4 < kMaxUnionRounds; q4 += 4) {
+          if (q4 >= a.rounds) break;
+          const int4 w = *reinterpret_cast<const int4*>(kk + q4);
+          const int wk[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            cnt += (q4 + e < a.rounds && (uint32_t)(kq[q4 + e] - wk[e]) <= 1u) ? 1 : 0;
+        }
+        if (oka[i]) s[t][i] -= __builtin_amdgcn_logf((float)cnt);
+      }
     }
   }
 
@@ -246,9 +294,10 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
         (mx == -INFINITY) ? -INFINITY : (mx + __builtin_amdgcn_logf(sum)) * kLn2;
 }
 
-template <bool CAUSAL, bool SELF>
+template <bool CAUSAL, bool SELF, bool UNION = false>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) AttendLds sm;
+  __shared__ __attribute__((aligned(16))) int32_t kkey[UNION ? 128 * kMaxUnionRounds : 4];
   const int64_t blk = xcd_interleaved_block(blockIdx.x, gridDim.x / a.runs_per_seg, a.runs_per_seg);
   const int64_t seg = blk / a.runs_per_seg;
   const int run = (int)(blk % a.runs_per_seg);
@@ -259,22 +308,23 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   const uint16_t* vb = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.L * kHeadDim;
   const int32_t* bk = a.buckets + seg * a.L;
   const int32_t* pm = a.perm + seg * a.L;
+  const int32_t* uk = UNION ? a.ukeys + bh * (int64_t)a.L * a.ukey_stride : nullptr;
   ChunkRegs g;
   if (c0 > 0) {
-    gather_chunk(g, load_perm_pair(pm, c0 - 1, a.L), xb, vb, bk);
-    commit_chunk(sm, g, c0 - 1);
+    gather_chunk<UNION>(g, load_perm_pair(pm, c0 - 1, a.L), xb, vb, bk, uk, a.ukey_stride);
+    commit_chunk<UNION>(sm, g, c0 - 1, kkey);
   }
-  gather_chunk(g, load_perm_pair(pm, c0, a.L), xb, vb, bk);
+  gather_chunk<UNION>(g, load_perm_pair(pm, c0, a.L), xb, vb, bk, uk, a.ukey_stride);
   int2 next = make_int2(0, 0);
   if (c0 + 1 < c1) next = load_perm_pair(pm, c0 + 1, a.L);
   for (int c = c0; c < c1; ++c) {
-    commit_chunk(sm, g, c);
+    commit_chunk<UNION>(sm, g, c, kkey);
     if (c + 1 < c1) {
-      gather_chunk(g, next, xb, vb, bk);          // chunk c+1, in flight during compute
+      gather_chunk<UNION>(g, next, xb, vb, bk, uk, a.ukey_stride);   // chunk c+1, in flight
       if (c + 2 < c1) next = load_perm_pair(pm, c + 2, a.L);
     }
     __syncthreads();
-    attend_chunk_bf16<CAUSAL, SELF>(sm, a, seg, c);
+    attend_chunk_bf16<CAUSAL, SELF, UNION>(sm, a, seg, c, kkey);
     __syncthreads();
   }
 }
@@ -325,7 +375,15 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
       float dot = 0.f;
 #pragma unroll
       for (int k = 0; k < kHeadDim; ++k) dot = fmaf(xq[k], xw[kk][k], dot);
-      const float sc = dot * kinv[kk];
+      float sc = dot * kinv[kk];
+      if (a.ukeys) {
+        // set union over rounds: the key weighs once over all rounds
+        const int32_t* uq = a.ukeys + (bh * a.L + qp) * a.ukey_stride;
+        const int32_t* uj = a.ukeys + (bh * a.L + kpos[kk]) * a.ukey_stride;
+        int cnt = 0;
+        for (int r = 0; r < a.rounds; ++r) cnt += (uint32_t)(uq[r] - uj[r]) <= 1u ? 1 : 0;
+        sc -= logf((float)cnt);
+      }
       if (sc > m) {
         const float f = expf(m - sc);
         l *= f;
@@ -349,9 +407,46 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
   a.lse[seg * a.L + slot] = (m == -INFINITY) ? -INFINITY : m + logf(l);
 }
 
-hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const int32_t* buckets,
-                         const int32_t* perm, float* o_rounds, float* lse, hipStream_t stream) {
+int union_key_stride(const Shape& s) { return (s.rounds + 3) & ~3; }
+
+size_t union_workspace_bytes(const Shape& s) {
+  return (size_t)s.token_heads() * union_key_stride(s) * sizeof(int32_t);
+}
+
+// Round keys of every token for the set union over rounds:
+// key_r(t) = bucket_r(t) * (C + 1) + slot_r(t) / m with C = L / m chunks, so
+// that key j is a candidate of query i in round r exactly when the two share
+// the bucket and j's chunk is i's chunk or the one before, i.e. when
+// key_r(i) - key_r(j) is 0 or 1 (C + 1 > C keeps different buckets apart).
+__global__ __launch_bounds__(256) void union_keys_kernel(const int32_t* __restrict__ buckets,
+                                                        const int32_t* __restrict__ inv_perm,
+                                                        int32_t* __restrict__ keys, int rounds,
+                                                        int stride, int L, int nb, int64_t total) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= total) return;
+  const int64_t bh = g / L;
+  const int pos = (int)(g % L);
+  const int span = L / kChunk + 1;
+  int32_t* out = keys + g * stride;
+  for (int r = 0; r < stride; ++r) {
+    int32_t k = -2;   // padding, never compared
+    if (r < rounds) {
+      const int64_t f = (bh * rounds + r) * L + pos;
+      const int b = min(max(buckets[f], 0), nb - 1);
+      k = b * span + clamp_index(inv_perm[f], L) / kChunk;
+    }
+    out[r] = k;
+  }
+}
+
+template <bool UNION>
+static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void* v,
+                                     const int32_t* buckets, const int32_t* perm,
+                                     const int32_t* ukeys, float* o_rounds, float* lse,
+                                     hipStream_t stream) {
   AttendArgs a;
+  a.ukeys = ukeys;
+  a.ukey_stride = UNION ? union_key_stride(s) : 0;
   a.qk = qk;
   a.v = v;
   a.buckets = buckets;
@@ -379,14 +474,31 @@ hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const in
   a.runs_per_seg = (a.nchunks + cpw - 1) / cpw;
   const dim3 grid((unsigned)(S * a.runs_per_seg)), block(256);
   if (a.causal && a.self_mask)
-    hipLaunchKernelGGL((attend_bf16_kernel<true, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<true, true, UNION>), grid, block, 0, stream, a);
   else if (a.causal)
-    hipLaunchKernelGGL((attend_bf16_kernel<true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<true, false, UNION>), grid, block, 0, stream, a);
   else if (a.self_mask)
-    hipLaunchKernelGGL((attend_bf16_kernel<false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<false, true, UNION>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attend_bf16_kernel<false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<false, false, UNION>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const int32_t* buckets,
+                         const int32_t* perm, float* o_rounds, float* lse, hipStream_t stream) {
+  return launch_attend_impl<false>(s, qk, v, buckets, perm, nullptr, o_rounds, lse, stream);
+}
+
+hipError_t launch_attend_union(const Shape& s, const void* qk, const void* v,
+                               const int32_t* buckets, const int32_t* perm,
+                               const int32_t* inv_perm, float* o_rounds, float* lse,
+                               void* workspace, hipStream_t stream) {
+  int32_t* keys = static_cast<int32_t*>(workspace);
+  const int64_t total = s.token_heads();
+  hipLaunchKernelGGL(union_keys_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, buckets, inv_perm, keys, s.rounds, union_key_stride(s), s.len,
+                     s.buckets, total);
+  return launch_attend_impl<true>(s, qk, v, buckets, perm, keys, o_rounds, lse, stream);
 }
 
 }  // namespace lsh

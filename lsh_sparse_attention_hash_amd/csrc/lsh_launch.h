@@ -27,6 +27,14 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
 hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, float* o_rounds, float* lse, hipStream_t stream);
 
+// Set union over rounds: workspace = per-token round keys (see attend.hip).
+int union_key_stride(const Shape& s);
+size_t union_workspace_bytes(const Shape& s);
+hipError_t launch_attend_union(const Shape& s, const void* qk, const void* v,
+                               const int32_t* buckets, const int32_t* perm,
+                               const int32_t* inv_perm, float* o_rounds, float* lse,
+                               void* workspace, hipStream_t stream);
+
 hipError_t launch_combine(const Shape& s, const float* o_rounds, const float* lse,
                           const int32_t* inv_perm, const void* v, float* y, hipStream_t stream);
 

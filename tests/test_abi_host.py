@@ -170,3 +170,24 @@ def test_local_attend_rejects_bad_windows_and_pointers():
         B.LSH_ERR_INVALID_ARGUMENT
     for kw in (dict(batch=0), dict(heads=0), dict(seq_len=0)):
         assert call_local(cfg(**kw), qk=None, v=None, y=None, lse=None) == B.LSH_OK
+
+
+def test_union_attend_limits_and_workspace():
+    lib = B.library()
+    c = cfg()
+    need = B.lsh_union_workspace_bytes(c)
+    assert need == 1 * 2 * 256 * 4 * 4          # rounds padded to 4 keys per token
+    args = [FAKE] * 7
+    assert lib.lsh_chunk_attend_union(ctypes.byref(c), *args, FAKE, need - 1, None) == \
+        B.LSH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.lsh_chunk_attend_union(ctypes.byref(c), *args[:6], None, FAKE, need, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT                # NULL lse
+    c17 = cfg(n_rounds=17)
+    assert B.lsh_union_workspace_bytes(c17) == 0
+    assert lib.lsh_chunk_attend_union(ctypes.byref(c17), *args, FAKE, 1 << 30, None) == \
+        B.LSH_ERR_UNSUPPORTED
+    big = cfg(seq_len=1 << 23, n_buckets=16384, n_rounds=1, heads=1)
+    assert lib.lsh_chunk_attend_union(ctypes.byref(big), *args, FAKE, 1 << 40, None) == \
+        B.LSH_ERR_UNSUPPORTED
+    empty = cfg(seq_len=0)
+    assert lib.lsh_chunk_attend_union(ctypes.byref(empty), *([None] * 8), 0, None) == B.LSH_OK
