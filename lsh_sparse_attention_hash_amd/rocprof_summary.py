@@ -31,7 +31,7 @@ KERNEL_SOURCES = {
 }
 # kernel name prefix (as rocprofv3 prints it) -> step
 STEP_OF = [("lsh::hash", "hash"), ("lsh::sort", "sort"), ("lsh::attend", "attend"),
-           ("lsh::combine", "combine"), ("lsh::local", "local")]
+           ("lsh::union_keys", "attend"), ("lsh::combine", "combine"), ("lsh::local", "local")]
 COPY_BYTES = 512 << 20
 
 
