@@ -586,3 +586,26 @@ int oracle_local_attend(int batch, int heads, int len, int dim, int chunk,
   free(idx);
   return rc;
 }
+
+/* ------------------------------------------------------ dense linear maps */
+
+/* out[m][n] = sum_{k=0}^{K-1} a[m][k] * w[n][k] (+ bias[n]), summed in fp64
+ * with k ascending from 0.0; w is stored as [N][K] (one row per output
+ * feature).  Each output row depends on its own input row only, so any split
+ * of the rows into chunks gives the same values (Reformer study note,
+ * "Chunked Feed-Forward Computation": the feed-forward map is token-wise). */
+int oracle_linear(int64_t rows, int n_out, int n_in, const double* a,
+                  const double* w, const double* bias, double* out) {
+  if (rows < 0 || n_out < 1 || n_in < 1) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < rows; ++m) {
+    const double* am = a + m * (int64_t)n_in;
+    for (int n = 0; n < n_out; ++n) {
+      const double* wn = w + (int64_t)n * n_in;
+      double acc = 0.0;
+      for (int k = 0; k < n_in; ++k) acc = acc + am[k] * wn[k];
+      out[m * (int64_t)n_out + n] = bias ? acc + bias[n] : acc;
+    }
+  }
+  return 0;
+}

@@ -18,6 +18,8 @@ file.  Function map:
     forward(...)   all of the above
     attend_union() o_rounds, lse with set semantics of the round union
                    ["Multiple Hash Rounds"]; forward_union() end to end
+    linear()       x W^T + b, token by token            ["Chunked Feed-Forward
+                                                          Computation"]
     local_attend() y, lse of local chunked attention (no hashing) [Reformer
                    overview page, "Approach / What changed", "Takeaways"]
     *_rows(...)    the same on a sample of rows (for full-size parity)
@@ -67,6 +69,7 @@ def _bind(lib):
     lib.oracle_lsh_forward.argtypes = [_I] * 9 + [_P] * 9
     lib.oracle_lsh_attend_union.argtypes = [_I] * 9 + [_P] * 7
     lib.oracle_lsh_attend_union_rows.argtypes = [_I] * 9 + [_P] * 5 + [_I64, _P, _P, _P]
+    lib.oracle_linear.argtypes = [_I64, _I, _I, _P, _P, _P, _P]
     lib.oracle_local_attend.argtypes = [_I] * 9 + [_P] * 4
     lib.oracle_local_attend_rows.argtypes = [_I] * 9 + [_P, _P, _I64, _P, _P, _P]
     for name in ("oracle_lsh_hash", "oracle_lsh_hash_rows", "oracle_lsh_sort",
@@ -74,7 +77,8 @@ def _bind(lib):
                  "oracle_lsh_candidates", "oracle_lsh_combine",
                  "oracle_lsh_combine_rows", "oracle_lsh_forward",
                  "oracle_local_attend", "oracle_local_attend_rows",
-                 "oracle_lsh_attend_union", "oracle_lsh_attend_union_rows"):
+                 "oracle_lsh_attend_union", "oracle_lsh_attend_union_rows",
+                 "oracle_linear"):
         getattr(lib, name).restype = _I
     return lib
 
@@ -323,3 +327,17 @@ def forward_union(qk, v, rot, n_buckets: int, n_rounds: int, chunk: int, causal:
     o, lse = attend_union(qk, v, buckets, perm, inv_perm, n_buckets, chunk, causal, self_mask)
     y = combine(o, lse, inv_perm, v)
     return dict(buckets=buckets, perm=perm, inv_perm=inv_perm, o_rounds=o, lse=lse, y=y)
+
+
+def linear(a, w, bias=None) -> np.ndarray:
+    """a[..., K] @ w[N, K]^T (+ bias[N]) in fp64, each output row from its own
+    input row only."""
+    a = _f64(a)
+    w = _f64(w)
+    N, K = w.shape
+    rows = a.size // K
+    out = np.empty(a.shape[:-1] + (N,))
+    b = None if bias is None else _f64(bias)
+    _check(_load().oracle_linear(rows, N, K, _ptr(a), _ptr(w), None if b is None else _ptr(b),
+                                 _ptr(out)), "linear")
+    return out

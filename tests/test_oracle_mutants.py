@@ -96,3 +96,43 @@ def test_pins_catch_mutant(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
+LAYER_SRC = os.path.join(ROOT, "oracle", "layer.py")
+LAYER_MUTANTS = {
+    "inverse_adds_attention": (
+        "    x1 = y1 - attention(x2, w, cfg)", "    x1 = y1 + attention(x2, w, cfg)"),
+    "inverse_ffn_of_x2": (
+        "    x2 = y2 - ffn(y1, w, cfg.get(\"ffn_chunk\"))",
+        "    x2 = y2 - ffn(y2, w, cfg.get(\"ffn_chunk\"))"),
+    "forward_ffn_of_x1": (
+        "    y2 = x2 + ffn(y1, w, cfg.get(\"ffn_chunk\"))",
+        "    y2 = x2 + ffn(x1, w, cfg.get(\"ffn_chunk\"))"),
+    "ffn_without_relu": (
+        "h = bf16_round(np.maximum(oracle.linear(xb, w[\"w_1\"], w[\"b_1\"]), 0.0))",
+        "h = bf16_round(oracle.linear(xb, w[\"w_1\"], w[\"b_1\"]))"),
+    "ffn_without_first_bias": (
+        "oracle.linear(xb, w[\"w_1\"], w[\"b_1\"])", "oracle.linear(xb, w[\"w_1\"])"),
+    "ffn_hidden_not_rounded": (
+        "h = bf16_round(np.maximum(", "h = (np.maximum("),
+    "heads_interleaved": (
+        "return np.ascontiguousarray(t.reshape(b, L, heads, HEAD_DIM).transpose(0, 2, 1, 3))",
+        "return np.ascontiguousarray(t.reshape(b, L, HEAD_DIM, heads).transpose(0, 3, 1, 2))"),
+    "round_ties_away": (
+        "return np.ldexp(np.rint(m * 256.0) / 256.0, e)",
+        "return np.ldexp(np.trunc(m * 256.0 + np.copysign(0.5, m)) / 256.0, e)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYER_MUTANTS))
+def test_layer_pins_catch_mutant(name, tmp_path):
+    old, new = LAYER_MUTANTS[name]
+    src = open(LAYER_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / "layer_mutant.py"
+    path.write_text(src.replace(old, new))
+    env = dict(os.environ, LSH_ORACLE_LAYER=str(path), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_layer_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
