@@ -226,6 +226,100 @@ lsh_status lsh_local_attend(const lsh_config* cfg, int32_t n_before,
                             int32_t n_after, const void* qk, const void* v,
                             float* y, float* lse, void* stream);
 
+/* ------------------------------------------------------------------------
+ * One reversible Reformer layer around the LSH attention.
+ * Follows: Reformer study note, sections "Reversible Residual Layers" (the
+ * hidden state is split into (x1, x2); y1 = x1 + F(x2), y2 = x2 + G(y1); the
+ * inverse x2 = y2 - G(y1), x1 = y1 - F(x2)) and "Chunked Feed-Forward
+ * Computation" (G(x) = W2 s(W1 x + b1) + b2 token by token, evaluated over
+ * chunks of tokens with the same result).  Here s = ReLU and
+ *   F(x) = concat_h(LSHAttn_h(qk_h, v_h)) W_o^T,
+ *   qk = bf16(bf16(x) W_qk^T), v = bf16(bf16(x) W_v^T) split into heads of 64
+ *   features (head h = features 64h .. 64h+63),
+ * with LSHAttn the four calls above (bf16, head_dim = chunk_len = 64).
+ * Precision: the inputs of every dense map are rounded to bf16 (nearest,
+ * ties to even), products are exact and summed in fp32; qk, v and the hidden
+ * activation of G are stored in bf16; the residual stream x1, x2, y1, y2 is
+ * fp32 [batch][seq_len][d_model].  Weights are bf16, one row per output
+ * feature ([out][in]); biases fp32.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch, seq_len;
+  int32_t d_model;    /* multiple of 64; heads H = d_model / 64 */
+  int32_t d_ff;       /* hidden width of G, multiple of 64 */
+  int32_t n_buckets, n_rounds, causal, self_mask;   /* of the LSH attention */
+  int32_t ffn_chunk;  /* tokens per chunk of G (0 = all tokens at once) */
+} lsh_layer_config;
+
+typedef struct {
+  const void* w_qk;   /* [d_model][d_model] bf16 */
+  const void* w_v;    /* [d_model][d_model] bf16 */
+  const void* w_o;    /* [d_model][d_model] bf16 */
+  const void* rot;    /* [H][R][B/2][64] bf16 (may be NULL if B == 1) */
+  const void* w_1;    /* [d_ff][d_model] bf16 */
+  const float* b_1;   /* [d_ff] */
+  const void* w_2;    /* [d_model][d_ff] bf16 */
+  const float* b_2;   /* [d_model] */
+} lsh_layer_weights;
+
+/*
+ * lsh_project_qkv -- the two input maps of F.
+ *   x   [b][L][d_model] fp32
+ *   qk, v  [b][H][L][64] bf16 outputs (the layout lsh_hash and
+ *       lsh_chunk_attend read): qk = bf16(bf16(x) W_qk^T) and likewise v.
+ */
+lsh_status lsh_project_qkv(const lsh_layer_config* cfg, const float* x,
+                           const void* w_qk, const void* w_v, void* qk, void* v,
+                           void* stream);
+
+/*
+ * lsh_project_out -- the output map of F and its residual add:
+ *   out = resid +/- concat_h(bf16(y_att_h)) W_o^T   (minus when subtract = 1)
+ *   y_att  [b][H][L][64] fp32 (from lsh_unsort_combine)
+ *   resid, out  [b][L][d_model] fp32; out may be the same buffer as resid.
+ */
+lsh_status lsh_project_out(const lsh_layer_config* cfg, const float* y_att,
+                           const void* w_o, const float* resid, int32_t subtract,
+                           float* out, void* stream);
+
+/* Bytes of device workspace lsh_ffn needs: one chunk of hidden activations. */
+size_t lsh_ffn_workspace_bytes(const lsh_layer_config* cfg);
+
+/*
+ * lsh_ffn -- G and its residual add, chunk by chunk of cfg->ffn_chunk tokens:
+ *   out = resid +/- (bf16(ReLU(bf16(x) W_1^T + b_1)) W_2^T + b_2)
+ *   x, resid, out  [b][L][d_model] fp32; out may be the same buffer as resid
+ *   but must not overlap x.  The result does not depend on ffn_chunk.
+ */
+lsh_status lsh_ffn(const lsh_layer_config* cfg, const float* x, const void* w_1,
+                   const float* b_1, const void* w_2, const float* b_2,
+                   const float* resid, int32_t subtract, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace the reversible layer needs (qk, v, the LSH
+ * attention's intermediates, the per-head outputs and one FFN chunk). */
+size_t lsh_layer_workspace_bytes(const lsh_layer_config* cfg);
+
+/*
+ * lsh_reversible_forward -- (y1, y2) = (x1 + F(x2), x2 + G(y1)).
+ * lsh_reversible_inverse -- (x1, x2) = (y1 - F(x2), y2 - G(y1)), x2 first.
+ * All four tensors [b][L][d_model] fp32; outputs must not overlap inputs.
+ * The inverse recomputes F and G from its inputs; it returns the forward's
+ * inputs up to the rounding of the fp32 residual adds (and exactly the same
+ * F wherever bf16(x2) comes back bit for bit, which then gives the same
+ * buckets).
+ */
+lsh_status lsh_reversible_forward(const lsh_layer_config* cfg,
+                                  const lsh_layer_weights* weights,
+                                  const float* x1, const float* x2, float* y1,
+                                  float* y2, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+lsh_status lsh_reversible_inverse(const lsh_layer_config* cfg,
+                                  const lsh_layer_weights* weights,
+                                  const float* y1, const float* y2, float* x1,
+                                  float* x2, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* lsh_status_string(lsh_status status);
 

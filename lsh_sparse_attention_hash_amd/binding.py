@@ -27,7 +27,9 @@ LSH_BF16 = 1
 
 EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attend",
            "lsh_unsort_combine", "lsh_union_workspace_bytes", "lsh_chunk_attend_union",
-           "lsh_local_attend", "lsh_status_string", "lsh_last_error", "lsh_version")
+           "lsh_local_attend", "lsh_project_qkv", "lsh_project_out", "lsh_ffn_workspace_bytes",
+           "lsh_ffn", "lsh_layer_workspace_bytes", "lsh_reversible_forward",
+           "lsh_reversible_inverse", "lsh_status_string", "lsh_last_error", "lsh_version")
 
 
 class LshError(RuntimeError):
@@ -40,6 +42,17 @@ class LshConfig(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "heads", "seq_len", "head_dim", "n_buckets", "n_rounds", "chunk_len",
         "causal", "self_mask", "dtype")]
+
+
+class LshLayerConfig(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "seq_len", "d_model", "d_ff", "n_buckets", "n_rounds", "causal", "self_mask",
+        "ffn_chunk")]
+
+
+class LshLayerWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "w_qk", "w_v", "w_o", "rot", "w_1", "b_1", "w_2", "b_2")]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -59,8 +72,20 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsh_union_workspace_bytes.argtypes = [cfgp]
     lib.lsh_union_workspace_bytes.restype = SZ
     lib.lsh_chunk_attend_union.argtypes = [cfgp, P, P, P, P, P, P, P, P, SZ, P]
+    lcp = ctypes.POINTER(LshLayerConfig)
+    lwp = ctypes.POINTER(LshLayerWeights)
+    lib.lsh_project_qkv.argtypes = [lcp, P, P, P, P, P, P]
+    lib.lsh_project_out.argtypes = [lcp, P, P, P, I32, P, P]
+    lib.lsh_ffn_workspace_bytes.argtypes = [lcp]
+    lib.lsh_ffn_workspace_bytes.restype = SZ
+    lib.lsh_ffn.argtypes = [lcp, P, P, P, P, P, P, I32, P, P, SZ, P]
+    lib.lsh_layer_workspace_bytes.argtypes = [lcp]
+    lib.lsh_layer_workspace_bytes.restype = SZ
+    lib.lsh_reversible_forward.argtypes = [lcp, lwp, P, P, P, P, P, SZ, P]
+    lib.lsh_reversible_inverse.argtypes = [lcp, lwp, P, P, P, P, P, SZ, P]
     for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
-              "lsh_local_attend", "lsh_chunk_attend_union"):
+              "lsh_local_attend", "lsh_chunk_attend_union", "lsh_project_qkv", "lsh_project_out",
+              "lsh_ffn", "lsh_reversible_forward", "lsh_reversible_inverse"):
         getattr(lib, f).restype = I32
     lib.lsh_status_string.argtypes = [I32]
     lib.lsh_status_string.restype = ctypes.c_char_p
@@ -279,6 +304,119 @@ class Forward:
             self.attend(qk, v, stream)
         self.combine(v, stream)
         return self.y
+
+
+# ----------------------------------------------------------------- layer
+def make_layer_config(w) -> LshLayerConfig:
+    """LshLayerConfig of a synth.LayerWorkload."""
+    return LshLayerConfig(w.batch, w.seq_len, w.d_model, w.d_ff, w.n_buckets, w.n_rounds,
+                          int(bool(w.causal)), int(bool(w.self_mask)), w.ffn_chunk)
+
+
+def attention_config(lc: LshLayerConfig) -> LshConfig:
+    """The LshConfig of the layer's attention (bf16, d_model / 64 heads)."""
+    return make_config(lc.batch, lc.d_model // 64, lc.seq_len, lc.n_buckets, lc.n_rounds,
+                       lc.causal, lc.self_mask, "bf16")
+
+
+def _layer_shapes(lc):
+    b, L, D, F, H = lc.batch, lc.seq_len, lc.d_model, lc.d_ff, lc.d_model // 64
+    return dict(stream=(b, L, D), heads=(b, H, L, 64))
+
+
+def lsh_project_qkv(lc: LshLayerConfig, x, w_qk, w_v, qk, v, stream=None):
+    sh = _layer_shapes(lc)
+    D = lc.d_model
+    _expect(x, sh["stream"], torch.float32, "x")
+    _expect(w_qk, (D, D), torch.bfloat16, "w_qk")
+    _expect(w_v, (D, D), torch.bfloat16, "w_v")
+    _expect(qk, sh["heads"], torch.bfloat16, "qk")
+    _expect(v, sh["heads"], torch.bfloat16, "v")
+    _check("lsh_project_qkv", _lib.lsh_project_qkv(ctypes.byref(lc), _ptr(x), _ptr(w_qk),
+                                                   _ptr(w_v), _ptr(qk), _ptr(v), _stream(stream)))
+
+
+def lsh_project_out(lc: LshLayerConfig, y_att, w_o, resid, subtract, out, stream=None):
+    sh = _layer_shapes(lc)
+    _expect(y_att, sh["heads"], torch.float32, "y_att")
+    _expect(w_o, (lc.d_model, lc.d_model), torch.bfloat16, "w_o")
+    _expect(resid, sh["stream"], torch.float32, "resid")
+    _expect(out, sh["stream"], torch.float32, "out")
+    _check("lsh_project_out", _lib.lsh_project_out(ctypes.byref(lc), _ptr(y_att), _ptr(w_o),
+                                                   _ptr(resid), int(bool(subtract)), _ptr(out),
+                                                   _stream(stream)))
+
+
+def lsh_ffn_workspace_bytes(lc: LshLayerConfig) -> int:
+    return int(_lib.lsh_ffn_workspace_bytes(ctypes.byref(lc)))
+
+
+def lsh_ffn(lc: LshLayerConfig, x, w_1, b_1, w_2, b_2, resid, subtract, out, workspace,
+            stream=None):
+    sh = _layer_shapes(lc)
+    D, F = lc.d_model, lc.d_ff
+    for t, n in ((x, "x"), (resid, "resid"), (out, "out")):
+        _expect(t, sh["stream"], torch.float32, n)
+    _expect(w_1, (F, D), torch.bfloat16, "w_1")
+    _expect(b_1, (F,), torch.float32, "b_1")
+    _expect(w_2, (D, F), torch.bfloat16, "w_2")
+    _expect(b_2, (D,), torch.float32, "b_2")
+    _check("lsh_ffn", _lib.lsh_ffn(ctypes.byref(lc), _ptr(x), _ptr(w_1), _ptr(b_1), _ptr(w_2),
+                                   _ptr(b_2), _ptr(resid), int(bool(subtract)), _ptr(out),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
+
+
+def lsh_layer_workspace_bytes(lc: LshLayerConfig) -> int:
+    return int(_lib.lsh_layer_workspace_bytes(ctypes.byref(lc)))
+
+
+class Layer:
+    """Weights (device tensors), workspace and the calls of one reversible
+    layer.  ``weights`` maps w_qk, w_v, w_o, rot, w_1, w_2 (bf16) and b_1,
+    b_2 (fp32) to device tensors of the shapes in include/lsh.h."""
+
+    def __init__(self, lc: LshLayerConfig, weights: dict, device="cuda"):
+        self.cfg = lc
+        self.w = weights
+        D, F, H = lc.d_model, lc.d_ff, lc.d_model // 64
+        for name, shape in (("w_qk", (D, D)), ("w_v", (D, D)), ("w_o", (D, D)),
+                            ("w_1", (F, D)), ("w_2", (D, F))):
+            _expect(weights[name], shape, torch.bfloat16, name)
+        if lc.n_buckets > 1:
+            _expect(weights["rot"], (H, lc.n_rounds, lc.n_buckets // 2, 64), torch.bfloat16, "rot")
+        _expect(weights["b_1"], (F,), torch.float32, "b_1")
+        _expect(weights["b_2"], (D,), torch.float32, "b_2")
+        self.cw = LshLayerWeights(*[None if (k == "rot" and lc.n_buckets == 1)
+                                    else weights[k].data_ptr()
+                                    for k in ("w_qk", "w_v", "w_o", "rot", "w_1", "b_1", "w_2",
+                                              "b_2")])
+        nbytes = max(16, lsh_layer_workspace_bytes(lc))
+        self.workspace = torch.empty(((nbytes + 15) // 16) * 16, dtype=torch.uint8, device=device)
+
+    def _run(self, fn, name, a, b, c, d, stream):
+        sh = _layer_shapes(self.cfg)["stream"]
+        for t, n in ((a, "in1"), (b, "in2"), (c, "out1"), (d, "out2")):
+            _expect(t, sh, torch.float32, n)
+        _check(name, fn(ctypes.byref(self.cfg), ctypes.byref(self.cw), _ptr(a), _ptr(b), _ptr(c),
+                        _ptr(d), _ptr(self.workspace),
+                        self.workspace.numel() * self.workspace.element_size(), _stream(stream)))
+
+    def forward(self, x1, x2, y1, y2, stream=None):
+        self._run(_lib.lsh_reversible_forward, "lsh_reversible_forward", x1, x2, y1, y2, stream)
+
+    def inverse(self, y1, y2, x1, x2, stream=None):
+        self._run(_lib.lsh_reversible_inverse, "lsh_reversible_inverse", y1, y2, x1, x2, stream)
+
+
+def layer_weights_to_device(inputs: dict, device="cuda") -> dict:
+    """synth.make_layer_inputs weights -> device tensors (bf16 / fp32)."""
+    out = {}
+    for k in ("w_qk", "w_v", "w_o", "rot", "w_1", "w_2"):
+        out[k] = to_device(inputs[k], "bf16", device)
+    for k in ("b_1", "b_2"):
+        out[k] = to_device(inputs[k], "f32", device)
+    return out
 
 
 def to_device(stored, dtype: str, device="cuda"):

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "liblsh.so")
-SOURCES = ["api.hip", "hash.hip", "sort.hip", "attend.hip", "combine.hip", "local.hip"]
+SOURCES = ["api.hip", "hash.hip", "sort.hip", "attend.hip", "combine.hip", "local.hip", "gemm.hip",
+           "layer.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of the generated code on purpose.
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

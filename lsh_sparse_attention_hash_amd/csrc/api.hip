@@ -94,6 +94,40 @@ lsh_status check_union(const lsh::Shape& s) {
     if (st_ != LSH_OK) return st_;    \
   } while (0)
 
+// Validates a layer configuration; fills the layer shape and the shape of its
+// attention (bf16, head_dim = chunk_len = 64).  *empty: no tokens.
+lsh_status check_layer(const lsh_layer_config* cfg, lsh::LayerShape* ls, lsh::Shape* as,
+                       bool* empty) {
+  if (!cfg) return fail(LSH_ERR_INVALID_ARGUMENT, "cfg is NULL");
+  const lsh_layer_config& c = *cfg;
+  if (c.d_model < lsh::kHeadDim || c.d_model % lsh::kHeadDim)
+    return fail(LSH_ERR_UNSUPPORTED, "d_model %d must be a positive multiple of 64", c.d_model);
+  if (c.d_ff < 64 || c.d_ff % 64)
+    return fail(LSH_ERR_UNSUPPORTED, "d_ff %d must be a positive multiple of 64", c.d_ff);
+  if (c.ffn_chunk < 0) return fail(LSH_ERR_INVALID_ARGUMENT, "ffn_chunk %d < 0", c.ffn_chunk);
+  lsh_config a;
+  a.batch = c.batch;
+  a.heads = c.d_model / lsh::kHeadDim;
+  a.seq_len = c.seq_len;
+  a.head_dim = lsh::kHeadDim;
+  a.n_buckets = c.n_buckets;
+  a.n_rounds = c.n_rounds;
+  a.chunk_len = lsh::kChunk;
+  a.causal = c.causal;
+  a.self_mask = c.self_mask;
+  a.dtype = LSH_BF16;
+  LSH_TRY(check_config(&a, as, empty));
+  const long long rows = (long long)c.batch * c.seq_len;
+  if (rows * (c.d_model > c.d_ff ? c.d_model : c.d_ff) >= (1LL << 40))
+    return fail(LSH_ERR_INVALID_ARGUMENT, "batch*seq_len*max(d_model, d_ff) too large");
+  ls->batch = c.batch;
+  ls->len = c.seq_len;
+  ls->d_model = c.d_model;
+  ls->d_ff = c.d_ff;
+  ls->ffn_chunk = c.ffn_chunk;
+  return LSH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,6 +262,144 @@ lsh_status lsh_local_attend(const lsh_config* cfg, int32_t n_before, int32_t n_a
   return launched(lsh::launch_local(s, n_before, n_after, qk, v, y, lse,
                                     static_cast<hipStream_t>(stream)),
                   "lsh_local_attend");
+}
+
+lsh_status lsh_project_qkv(const lsh_layer_config* cfg, const float* x, const void* w_qk,
+                           const void* w_v, void* qk, void* v, void* stream) {
+  lsh::LayerShape ls;
+  lsh::Shape as;
+  bool empty = false;
+  LSH_TRY(check_layer(cfg, &ls, &as, &empty));
+  if (empty) return ok();
+  LSH_TRY(check_ptr(x, "x"));
+  LSH_TRY(check_ptr(w_qk, "w_qk"));
+  LSH_TRY(check_ptr(w_v, "w_v"));
+  LSH_TRY(check_ptr(qk, "qk"));
+  LSH_TRY(check_ptr(v, "v"));
+  return launched(lsh::launch_project_qkv(ls, x, static_cast<const uint16_t*>(w_qk),
+                                          static_cast<const uint16_t*>(w_v),
+                                          static_cast<uint16_t*>(qk), static_cast<uint16_t*>(v),
+                                          static_cast<hipStream_t>(stream)),
+                  "lsh_project_qkv");
+}
+
+lsh_status lsh_project_out(const lsh_layer_config* cfg, const float* y_att, const void* w_o,
+                           const float* resid, int32_t subtract, float* out, void* stream) {
+  lsh::LayerShape ls;
+  lsh::Shape as;
+  bool empty = false;
+  LSH_TRY(check_layer(cfg, &ls, &as, &empty));
+  if (subtract != 0 && subtract != 1)
+    return fail(LSH_ERR_INVALID_ARGUMENT, "subtract must be 0 or 1");
+  if (empty) return ok();
+  LSH_TRY(check_ptr(y_att, "y_att"));
+  LSH_TRY(check_ptr(w_o, "w_o"));
+  LSH_TRY(check_ptr(resid, "resid"));
+  LSH_TRY(check_ptr(out, "out"));
+  return launched(lsh::launch_project_out(ls, y_att, static_cast<const uint16_t*>(w_o), resid,
+                                          subtract ? -1.f : 1.f, out,
+                                          static_cast<hipStream_t>(stream)),
+                  "lsh_project_out");
+}
+
+size_t lsh_ffn_workspace_bytes(const lsh_layer_config* cfg) {
+  lsh::LayerShape ls;
+  lsh::Shape as;
+  bool empty = false;
+  if (check_layer(cfg, &ls, &as, &empty) != LSH_OK || empty) return 0;
+  return lsh::ffn_workspace_bytes(ls);
+}
+
+lsh_status lsh_ffn(const lsh_layer_config* cfg, const float* x, const void* w_1, const float* b_1,
+                   const void* w_2, const float* b_2, const float* resid, int32_t subtract,
+                   float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  lsh::LayerShape ls;
+  lsh::Shape as;
+  bool empty = false;
+  LSH_TRY(check_layer(cfg, &ls, &as, &empty));
+  if (subtract != 0 && subtract != 1)
+    return fail(LSH_ERR_INVALID_ARGUMENT, "subtract must be 0 or 1");
+  if (empty) return ok();
+  LSH_TRY(check_ptr(x, "x"));
+  LSH_TRY(check_ptr(w_1, "w_1"));
+  LSH_TRY(check_ptr(b_1, "b_1"));
+  LSH_TRY(check_ptr(w_2, "w_2"));
+  LSH_TRY(check_ptr(b_2, "b_2"));
+  LSH_TRY(check_ptr(resid, "resid"));
+  LSH_TRY(check_ptr(out, "out"));
+  LSH_TRY(check_ptr(workspace, "workspace"));
+  const size_t need = lsh::ffn_workspace_bytes(ls);
+  if (workspace_bytes < need)
+    return fail(LSH_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed",
+                workspace_bytes, need);
+  return launched(lsh::launch_ffn(ls, x, static_cast<const uint16_t*>(w_1), b_1,
+                                  static_cast<const uint16_t*>(w_2), b_2, resid,
+                                  subtract ? -1.f : 1.f, out, static_cast<uint16_t*>(workspace),
+                                  static_cast<hipStream_t>(stream)),
+                  "lsh_ffn");
+}
+
+size_t lsh_layer_workspace_bytes(const lsh_layer_config* cfg) {
+  lsh::LayerShape ls;
+  lsh::Shape as;
+  bool empty = false;
+  if (check_layer(cfg, &ls, &as, &empty) != LSH_OK || empty) return 0;
+  return lsh::layer_workspace_bytes(ls, as);
+}
+
+static lsh_status reversible(const char* name, bool inverse, const lsh_layer_config* cfg,
+                             const lsh_layer_weights* w, const float* in1, const float* in2,
+                             float* out1, float* out2, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  lsh::LayerShape ls;
+  lsh::Shape as;
+  bool empty = false;
+  LSH_TRY(check_layer(cfg, &ls, &as, &empty));
+  if (empty) return ok();
+  if (!w) return fail(LSH_ERR_INVALID_ARGUMENT, "weights is NULL");
+  LSH_TRY(check_ptr(w->w_qk, "w_qk"));
+  LSH_TRY(check_ptr(w->w_v, "w_v"));
+  LSH_TRY(check_ptr(w->w_o, "w_o"));
+  if (as.buckets > 1) LSH_TRY(check_ptr(w->rot, "rot"));
+  LSH_TRY(check_ptr(w->w_1, "w_1"));
+  LSH_TRY(check_ptr(w->b_1, "b_1"));
+  LSH_TRY(check_ptr(w->w_2, "w_2"));
+  LSH_TRY(check_ptr(w->b_2, "b_2"));
+  LSH_TRY(check_ptr(in1, "first input"));
+  LSH_TRY(check_ptr(in2, "second input"));
+  LSH_TRY(check_ptr(out1, "first output"));
+  LSH_TRY(check_ptr(out2, "second output"));
+  LSH_TRY(check_ptr(workspace, "workspace"));
+  const size_t need = lsh::layer_workspace_bytes(ls, as);
+  if (workspace_bytes < need)
+    return fail(LSH_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed",
+                workspace_bytes, need);
+  lsh::LayerWeights lw;
+  lw.w_qk = static_cast<const uint16_t*>(w->w_qk);
+  lw.w_v = static_cast<const uint16_t*>(w->w_v);
+  lw.w_o = static_cast<const uint16_t*>(w->w_o);
+  lw.rot = static_cast<const uint16_t*>(w->rot);
+  lw.w_1 = static_cast<const uint16_t*>(w->w_1);
+  lw.b_1 = w->b_1;
+  lw.w_2 = static_cast<const uint16_t*>(w->w_2);
+  lw.b_2 = w->b_2;
+  return launched(lsh::launch_reversible(ls, as, lw, inverse, in1, in2, out1, out2, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                  name);
+}
+
+lsh_status lsh_reversible_forward(const lsh_layer_config* cfg, const lsh_layer_weights* w,
+                                  const float* x1, const float* x2, float* y1, float* y2,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return reversible("lsh_reversible_forward", false, cfg, w, x1, x2, y1, y2, workspace,
+                    workspace_bytes, stream);
+}
+
+lsh_status lsh_reversible_inverse(const lsh_layer_config* cfg, const lsh_layer_weights* w,
+                                  const float* y1, const float* y2, float* x1, float* x2,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return reversible("lsh_reversible_inverse", true, cfg, w, y1, y2, x1, x2, workspace,
+                    workspace_bytes, stream);
 }
 
 const char* lsh_status_string(lsh_status status) {

@@ -1,0 +1,305 @@
+// gemm.hip -- the dense maps of the reversible layer (Reformer study note,
+// "Reversible Residual Layers": y1 = x1 + F(x2), y2 = x2 + G(y1); "Chunked
+// Feed-Forward Computation": G(x) = W2 ReLU(W1 x + b1) + b2 token by token):
+// C[m][n] = sum_k A[m][k] W[n][k] on v_mfma_f32_32x32x16_bf16 with fused
+// epilogues.
+//
+// A is bf16 or fp32 (rounded to bf16, nearest-even, as it is staged), in rows
+// [M][lda] or, for the attention output, as heads [b][H][L][64] read as the
+// concatenation [b*L][H*64].  W is bf16, one row per output feature ([N][K]),
+// so both operands are K-contiguous: every MFMA fragment is one 16-byte load.
+//
+// Tiles: 128 x 128 outputs per workgroup (4 waves, 64 x 64 each as 2 x 2
+// MFMA blocks), K in steps of 64.  Both operand tiles go through LDS (rows
+// padded to 144 B so the fragment reads are conflict-free), double-buffered:
+// the next K-tile's global loads are in flight in registers while the current
+// one is multiplied, one barrier per K-tile.  Each output element is the same
+// K-ordered sum whatever tile or chunk of rows it falls in, so results do not
+// depend on how the rows are split.
+#include "lsh_device.h"
+#include "lsh_launch.h"
+
+namespace lsh {
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kTS = 72;   // bf16 per staged row (64 + 8 pad)
+
+enum ALayout { kAF32Rows = 0, kABf16Rows = 1, kAF32Heads = 2 };
+enum Epilogue { kEpiQkv = 0, kEpiResidual = 1, kEpiReluBf16 = 2 };
+
+struct GemmArgs {
+  const void* a;
+  int64_t lda;          // rows layouts: element (m, k) at a[m * lda + k]
+  int heads, L;         // heads layout: (m, k) at a[((m / L * heads + k / 64) * L + m % L) * 64 + k % 64]
+  const uint16_t* w0;   // output features n < n0
+  const uint16_t* w1;   // output features n >= n0 (row n - n0)
+  int n0;
+  int M, N, K;
+  void* out0;           // qkv: qk; residual: out (fp32 [M][N]); relu: bf16 [M][N]
+  void* out1;           // qkv: v
+  const float* bias;    // [N] or null
+  const float* resid;   // residual: fp32 [M][N] (may equal out0)
+  float sign;           // residual: out = resid + sign * (acc + bias)
+};
+
+__device__ __forceinline__ uint32_t gemm_pack2(float a, float b) {
+  const bf16x2 p = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// One K-tile of A (128 rows x 64 k) in registers.
+template <int AL>
+struct GemmATile {
+  uint4 r[AL == kABf16Rows ? 4 : 8];
+};
+
+template <int AL>
+__device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g, int m0, int k0) {
+  if (AL == kABf16Rows) {
+    const uint16_t* a = static_cast<const uint16_t*>(g.a);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      const int row = idx >> 3, c8 = (idx & 7) * 8;
+      const int m = m0 + row;
+      t.r[q] = m < g.M ? load16(a + (int64_t)m * g.lda + k0 + c8) : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    const float* a = static_cast<const float*>(g.a);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      const int row = idx >> 4, c4 = (idx & 15) * 4;
+      const int m = m0 + row;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (m < g.M) {
+        const float* src;
+        if (AL == kAF32Rows) {
+          src = a + (int64_t)m * g.lda + k0 + c4;
+        } else {   // heads: K-tile k0 / 64 is head k0 / 64
+          const int bi = m / g.L, l = m - bi * g.L;
+          src = a + (((int64_t)bi * g.heads + k0 / kHeadDim) * g.L + l) * kHeadDim + c4;
+        }
+        u = load16(src);
+      }
+      t.r[q] = u;
+    }
+  }
+}
+
+template <int AL>
+__device__ __forceinline__ void gemm_store_a(uint16_t* as, const GemmATile<AL>& t) {
+  if (AL == kABf16Rows) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      store16(&as[(idx >> 3) * kTS + (idx & 7) * 8], t.r[q]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      const uint4 u = t.r[q];
+      const uint2 p = make_uint2(gemm_pack2(__uint_as_float(u.x), __uint_as_float(u.y)),
+                                 gemm_pack2(__uint_as_float(u.z), __uint_as_float(u.w)));
+      *reinterpret_cast<uint2*>(&as[(idx >> 4) * kTS + (idx & 15) * 4]) = p;
+    }
+  }
+}
+
+__device__ __forceinline__ void gemm_load_w(uint4 (&t)[4], const GemmArgs& g, int n_base, int k0) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = threadIdx.x + 256 * q;
+    const int n = n_base + (idx >> 3), c8 = (idx & 7) * 8;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (n < g.N) {
+      const uint16_t* row = n < g.n0 ? g.w0 + (int64_t)n * g.K : g.w1 + (int64_t)(n - g.n0) * g.K;
+      u = load16(row + k0 + c8);
+    }
+    t[q] = u;
+  }
+}
+
+__device__ __forceinline__ void gemm_store_w(uint16_t* ws, const uint4 (&t)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = threadIdx.x + 256 * q;
+    store16(&ws[(idx >> 3) * kTS + (idx & 7) * 8], t[q]);
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void gemm_emit(const GemmArgs& g, int m, int n, float acc) {
+  if (m >= g.M || n >= g.N) return;
+  if (EPI == kEpiQkv) {
+    // feature n of qk (n < n0) or v: head n / 64, column n % 64, [b][H][L][64]
+    const int nn = n < g.n0 ? n : n - g.n0;
+    uint16_t* out = static_cast<uint16_t*>(n < g.n0 ? g.out0 : g.out1);
+    const int bi = m / g.L, l = m - bi * g.L;
+    const int64_t at = (((int64_t)bi * g.heads + nn / kHeadDim) * g.L + l) * kHeadDim + nn % kHeadDim;
+    out[at] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+  } else if (EPI == kEpiResidual) {
+    const int64_t at = (int64_t)m * g.N + n;
+    const float v = acc + (g.bias ? g.bias[n] : 0.f);
+    static_cast<float*>(g.out0)[at] = g.resid[at] + g.sign * v;
+  } else {
+    const int64_t at = (int64_t)m * g.N + n;
+    static_cast<uint16_t*>(g.out0)[at] =
+        __builtin_bit_cast(uint16_t, (__bf16)fmaxf(acc + (g.bias ? g.bias[n] : 0.f), 0.f));
+  }
+}
+
+template <int AL, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[2][kBM * kTS];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kBN * kTS];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int ntn = (g.N + kBN - 1) / kBN;
+  // each XCD takes a contiguous range of row tiles, so its A rows stay in its L2
+  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int m0 = (int)(blk / ntn) * kBM;
+  const int n_base = (int)(blk % ntn) * kBN;
+  const int nkt = g.K / kBK;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  GemmATile<AL> ta;
+  uint4 tw[4];
+  gemm_load_a<AL>(ta, g, m0, 0);
+  gemm_load_w(tw, g, n_base, 0);
+  gemm_store_a<AL>(as[0], ta);
+  gemm_store_w(ws[0], tw);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bool more = kt + 1 < nkt;
+    if (more) {   // next K-tile in flight during the products
+      gemm_load_a<AL>(ta, g, m0, (kt + 1) * kBK);
+      gemm_load_w(tw, g, n_base, (kt + 1) * kBK);
+    }
+    const uint16_t* a_s = as[kt & 1];
+    const uint16_t* w_s = ws[kt & 1];
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int kc = 16 * ks + 8 * (lane >> 5);
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = as_bf16x8(load16(&a_s[(wm * 64 + i * 32 + (lane & 31)) * kTS + kc]));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = as_bf16x8(load16(&w_s[(wn * 64 + j * 32 + (lane & 31)) * kTS + kc]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      gemm_store_a<AL>(as[(kt + 1) & 1], ta);
+      gemm_store_w(ws[(kt + 1) & 1], tw);
+    }
+    __syncthreads();
+  }
+
+  // register r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int n = n_base + wn * 64 + j * 32 + (lane & 31);
+        gemm_emit<EPI>(g, m, n, acc[i][j][r]);
+      }
+}
+
+template <int AL, int EPI>
+hipError_t gemm_launch(const GemmArgs& g, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<AL, EPI>), dim3((unsigned)tiles), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+static GemmArgs gemm_args(int M, int N, int K) {
+  GemmArgs g = {};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.n0 = N;
+  g.sign = 1.f;
+  return g;
+}
+
+hipError_t launch_project_qkv(const LayerShape& s, const float* x, const uint16_t* w_qk,
+                              const uint16_t* w_v, uint16_t* qk, uint16_t* v,
+                              hipStream_t stream) {
+  GemmArgs g = gemm_args(s.batch * s.len, 2 * s.d_model, s.d_model);
+  g.a = x;
+  g.lda = s.d_model;
+  g.heads = s.d_model / kHeadDim;
+  g.L = s.len;
+  g.w0 = w_qk;
+  g.w1 = w_v;
+  g.n0 = s.d_model;
+  g.out0 = qk;
+  g.out1 = v;
+  return gemm_launch<kAF32Rows, kEpiQkv>(g, stream);
+}
+
+hipError_t launch_project_out(const LayerShape& s, const float* y_att, const uint16_t* w_o,
+                              const float* resid, float sign, float* out, hipStream_t stream) {
+  GemmArgs g = gemm_args(s.batch * s.len, s.d_model, s.d_model);
+  g.a = y_att;
+  g.heads = s.d_model / kHeadDim;
+  g.L = s.len;
+  g.w0 = g.w1 = w_o;
+  g.out0 = out;
+  g.resid = resid;
+  g.sign = sign;
+  return gemm_launch<kAF32Heads, kEpiResidual>(g, stream);
+}
+
+hipError_t launch_ffn(const LayerShape& s, const float* x, const uint16_t* w_1, const float* b_1,
+                      const uint16_t* w_2, const float* b_2, const float* resid, float sign,
+                      float* out, uint16_t* hidden, hipStream_t stream) {
+  const int64_t rows = (int64_t)s.batch * s.len;
+  const int64_t chunk = s.ffn_chunk > 0 ? s.ffn_chunk : rows;
+  for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+    const int m = (int)(rows - r0 < chunk ? rows - r0 : chunk);
+    // hidden = bf16(ReLU(x W1^T + b1)) for this chunk of tokens
+    GemmArgs g1 = gemm_args(m, s.d_ff, s.d_model);
+    g1.a = x + r0 * s.d_model;
+    g1.lda = s.d_model;
+    g1.w0 = g1.w1 = w_1;
+    g1.bias = b_1;
+    g1.out0 = hidden;
+    hipError_t e = gemm_launch<kAF32Rows, kEpiReluBf16>(g1, stream);
+    if (e != hipSuccess) return e;
+    // out = resid + sign * (hidden W2^T + b2)
+    GemmArgs g2 = gemm_args(m, s.d_model, s.d_ff);
+    g2.a = hidden;
+    g2.lda = s.d_ff;
+    g2.w0 = g2.w1 = w_2;
+    g2.bias = b_2;
+    g2.out0 = out + r0 * s.d_model;
+    g2.resid = resid + r0 * s.d_model;
+    g2.sign = sign;
+    e = gemm_launch<kABf16Rows, kEpiResidual>(g2, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace lsh

@@ -41,4 +41,35 @@ hipError_t launch_combine(const Shape& s, const float* o_rounds, const float* ls
 hipError_t launch_local(const Shape& s, int before, int after, const void* qk, const void* v,
                         float* y, float* lse, hipStream_t stream);
 
+// ------------------------------------------------ reversible layer (gemm.hip, layer.hip)
+struct LayerShape {
+  int batch, len, d_model, d_ff, ffn_chunk;   // heads = d_model / 64; ffn_chunk 0 = all rows
+  int64_t rows() const { return (int64_t)batch * len; }
+  int64_t chunk_rows() const { return ffn_chunk > 0 && ffn_chunk < rows() ? ffn_chunk : rows(); }
+};
+
+struct LayerWeights {
+  const uint16_t *w_qk, *w_v, *w_o, *rot, *w_1, *w_2;
+  const float *b_1, *b_2;
+};
+
+// qk, v [b][H][L][64] bf16 = bf16(bf16(x) W^T) for x fp32 [b*L][d_model]
+hipError_t launch_project_qkv(const LayerShape& s, const float* x, const uint16_t* w_qk,
+                              const uint16_t* w_v, uint16_t* qk, uint16_t* v, hipStream_t stream);
+// out = resid + sign * (concat_heads(bf16(y_att)) W_o^T); out may equal resid
+hipError_t launch_project_out(const LayerShape& s, const float* y_att, const uint16_t* w_o,
+                              const float* resid, float sign, float* out, hipStream_t stream);
+// out = resid + sign * (bf16(ReLU(bf16(x) W1^T + b1)) W2^T + b2), chunk by chunk of rows;
+// hidden: chunk_rows() x d_ff bf16 scratch
+hipError_t launch_ffn(const LayerShape& s, const float* x, const uint16_t* w_1, const float* b_1,
+                      const uint16_t* w_2, const float* b_2, const float* resid, float sign,
+                      float* out, uint16_t* hidden, hipStream_t stream);
+
+size_t ffn_workspace_bytes(const LayerShape& s);
+size_t layer_workspace_bytes(const LayerShape& ls, const Shape& as);
+// forward: (y1, y2) = (x1 + F(x2), x2 + G(y1)); inverse: (x1, x2) from (y1, y2)
+hipError_t launch_reversible(const LayerShape& ls, const Shape& as, const LayerWeights& w,
+                             bool inverse, const float* in1, const float* in2, float* out1,
+                             float* out2, void* workspace, hipStream_t stream);
+
 }  // namespace lsh

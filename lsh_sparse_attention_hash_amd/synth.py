@@ -128,3 +128,57 @@ def make_inputs(w: Workload) -> dict:
     rot = normal(w.seed, 2, (w.heads, w.n_rounds, half, w.head_dim))
     return {"qk": _storage(qk, w.dtype), "v": _storage(v, w.dtype),
             "rot": _storage(rot, w.dtype)}
+
+
+# ---------------------------------------------------------------- layer
+@dataclasses.dataclass(frozen=True)
+class LayerWorkload:
+    """One reversible layer: residual stream [batch][seq_len][d_model] fp32,
+    heads = d_model / 64, LSH attention with n_buckets / n_rounds, FFN hidden
+    width d_ff evaluated ffn_chunk tokens at a time (0 = all)."""
+    name: str
+    batch: int
+    seq_len: int
+    d_model: int
+    d_ff: int
+    n_buckets: int
+    n_rounds: int
+    causal: bool
+    self_mask: bool
+    ffn_chunk: int
+    seed: int
+
+    @property
+    def heads(self) -> int:
+        return self.d_model // 64
+
+
+LAYER_WORKLOADS = {
+    # the headline attention shape inside one layer: 8 heads of 64 features,
+    # a 4x feed-forward expansion evaluated 8,192 tokens at a time
+    "layer_long": LayerWorkload("layer_long", 1, 65536, 512, 2048, 1024, 8, True, True, 8192, 8),
+}
+
+
+def make_layer_inputs(w: LayerWorkload) -> dict:
+    """Seeded inputs of one layer: x1, x2 fp32 ~ N(0, 1); weights bf16 bit
+    patterns ~ N(0, 1/fan_in) stored [out][in]; biases fp32 ~ N(0, 0.1^2);
+    rotations bf16 ~ N(0, 1) [H][R][B/2][64].  Streams 10..19 of the seed."""
+    D, F, H = w.d_model, w.d_ff, w.heads
+    shape = (w.batch, w.seq_len, D)
+
+    def wmat(stream, n_out, n_in):
+        return bf16_bits(normal(w.seed, stream, (n_out, n_in)) / np.float32(np.sqrt(n_in)))
+
+    return {
+        "x1": normal(w.seed, 10, shape),
+        "x2": normal(w.seed, 11, shape),
+        "w_qk": wmat(12, D, D),
+        "w_v": wmat(13, D, D),
+        "w_o": wmat(14, D, D),
+        "rot": bf16_bits(normal(w.seed, 15, (H, w.n_rounds, w.n_buckets // 2, 64))),
+        "w_1": wmat(16, F, D),
+        "b_1": normal(w.seed, 17, (F,)) * np.float32(0.1),
+        "w_2": wmat(18, D, F),
+        "b_2": normal(w.seed, 19, (D,)) * np.float32(0.1),
+    }

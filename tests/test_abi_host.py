@@ -191,3 +191,58 @@ def test_union_attend_limits_and_workspace():
         B.LSH_ERR_UNSUPPORTED
     empty = cfg(seq_len=0)
     assert lib.lsh_chunk_attend_union(ctypes.byref(empty), *([None] * 8), 0, None) == B.LSH_OK
+
+
+def layer_cfg(**kw):
+    c = B.LshLayerConfig(1, 256, 128, 256, 8, 2, 1, 1, 0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=100), B.LSH_ERR_UNSUPPORTED),
+    (dict(d_model=0), B.LSH_ERR_UNSUPPORTED),
+    (dict(d_ff=96), B.LSH_ERR_UNSUPPORTED),
+    (dict(ffn_chunk=-1), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=100), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(n_buckets=7), B.LSH_ERR_INVALID_ARGUMENT),
+    (dict(causal=3), B.LSH_ERR_INVALID_ARGUMENT),
+])
+def test_layer_calls_reject_invalid_config(kw, status):
+    lib = B.library()
+    c = layer_cfg(**kw)
+    w = B.LshLayerWeights(*([0x10000] * 8))
+    assert lib.lsh_project_qkv(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.lsh_project_out(ctypes.byref(c), FAKE, FAKE, FAKE, 0, FAKE, None) == status
+    assert lib.lsh_ffn(ctypes.byref(c), *([FAKE] * 6), 0, FAKE, FAKE, 1 << 40, None) == status
+    assert lib.lsh_reversible_forward(ctypes.byref(c), ctypes.byref(w), *([FAKE] * 5), 1 << 40,
+                                      None) == status
+    assert lib.lsh_layer_workspace_bytes(ctypes.byref(c)) == 0
+    assert lib.lsh_ffn_workspace_bytes(ctypes.byref(c)) == 0
+
+
+def test_layer_calls_check_pointers_workspace_and_flags():
+    lib = B.library()
+    c = layer_cfg()
+    w = B.LshLayerWeights(*([0x10000] * 8))
+    need = B.lsh_layer_workspace_bytes(c)
+    assert need > 0
+    assert lib.lsh_reversible_inverse(ctypes.byref(c), ctypes.byref(w), *([FAKE] * 5), need - 1,
+                                      None) == B.LSH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.lsh_reversible_forward(ctypes.byref(c), None, *([FAKE] * 5), need, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    w_bad = B.LshLayerWeights(*([0x10000] * 4 + [0x10004] + [0x10000] * 3))
+    assert lib.lsh_reversible_forward(ctypes.byref(c), ctypes.byref(w_bad), *([FAKE] * 5), need,
+                                      None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert b"w_1" in lib.lsh_last_error()
+    assert B.lsh_ffn_workspace_bytes(c) == 256 * 256 * 2
+    assert B.lsh_ffn_workspace_bytes(layer_cfg(ffn_chunk=100)) == 100 * 256 * 2
+    assert lib.lsh_ffn(ctypes.byref(c), *([FAKE] * 6), 0, FAKE, FAKE, 256 * 256 * 2 - 1, None) == \
+        B.LSH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.lsh_project_out(ctypes.byref(c), FAKE, FAKE, FAKE, 2, FAKE, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    assert lib.lsh_project_qkv(ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    e = layer_cfg(seq_len=0)
+    assert lib.lsh_reversible_forward(ctypes.byref(e), None, *([None] * 5), 0, None) == B.LSH_OK
