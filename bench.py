@@ -116,6 +116,109 @@ def cpu_baseline(w, inputs, union=False):
                                      f"; tokens/s scaled by {w.heads // hs}x to all heads")}
 
 
+def bench_layer(args, binding, torch, synth):
+    """One reversible layer: one step is lsh_reversible_forward (qk/v maps,
+    the four LSH calls, output map, chunked FFN).  The same calls are then
+    timed one by one for the per-kernel roofline."""
+    w = synth.LAYER_WORKLOADS[args.workload]
+    log(f"[bench] layer workload {w}")
+    inp = synth.make_layer_inputs(w)
+    lc = binding.make_layer_config(w)
+    wd = binding.layer_weights_to_device(inp)
+    x1 = torch.from_numpy(inp["x1"]).cuda()
+    x2 = torch.from_numpy(inp["x2"]).cuda()
+    y1, y2 = torch.empty_like(x1), torch.empty_like(x2)
+    layer = binding.Layer(lc, wd)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        layer.forward(x1, x2, y1, y2)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        layer.forward(x1, x2, y1, y2)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    log(f"[bench] {args.steps} layer steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
+
+    # the same work call by call
+    H, L, b, D, F = w.heads, w.seq_len, w.batch, w.d_model, w.d_ff
+    qk = torch.empty((b, H, L, 64), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(qk)
+    att = binding.Forward(binding.attention_config(lc))
+    ffn_ws = torch.empty(max(16, binding.lsh_ffn_workspace_bytes(lc)), dtype=torch.uint8,
+                         device="cuda")
+    calls = {
+        "project_qkv": lambda: binding.lsh_project_qkv(lc, x2, wd["w_qk"], wd["w_v"], qk, v),
+        "hash": lambda: att.hash(qk, wd["rot"]),
+        "sort": lambda: att.sort(),
+        "attend": lambda: att.attend(qk, v),
+        "combine": lambda: att.combine(v),
+        "project_out": lambda: binding.lsh_project_out(lc, att.y, wd["w_o"], x1, 0, y1),
+        "ffn": lambda: binding.lsh_ffn(lc, y1, wd["w_1"], wd["b_1"], wd["w_2"], wd["b_2"], x2, 0,
+                                       y2, ffn_ws),
+    }
+    for f in calls.values():
+        f()
+    torch.cuda.synchronize()
+    per = {}
+    for name, f in calls.items():
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            f()
+        e.record(stream)
+        torch.cuda.synchronize()
+        per[name] = a.elapsed_time(e) / args.steps
+    M = b * L
+    aw = synth.Workload(w.name, b, H, L, 64, w.n_buckets, w.n_rounds, 64, w.causal, w.self_mask,
+                        "bf16", w.seed)
+    work = algorithmic(aw)
+    work["project_qkv"] = {"flops": 2 * M * 2 * D * D, "bytes": M * D * 4 + 2 * D * D * 2 + 2 * M * D * 2}
+    work["project_out"] = {"flops": 2 * M * D * D, "bytes": M * D * 4 * 3 + D * D * 2}
+    work["ffn"] = {"flops": 2 * 2 * M * D * F, "bytes": M * D * 4 * 3 + 2 * D * F * 2}
+    kernels = {}
+    for n, t_ms in per.items():
+        t = t_ms * 1e-3
+        kb = {"ms": round(t_ms, 5), "algorithmic_bytes": work[n]["bytes"],
+              "GBps": round(work[n]["bytes"] / t / 1e9, 1)}
+        if "flops" in work[n]:
+            kb["algorithmic_flops"] = work[n]["flops"]
+            kb["TFLOPs"] = round(work[n]["flops"] / t / 1e12, 2)
+        kernels[n] = kb
+    log("[bench] per call ms: " + ", ".join(f"{n} {t:.4f}" for n, t in per.items()))
+    gemms = ("project_qkv", "project_out", "ffn")
+    dom = max(per, key=lambda n: per[n])
+    t = per[dom] * 1e-3
+    if dom in gemms or dom == "hash":
+        ach = work[dom]["flops"] / t / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        ach = work[dom]["bytes"] / t / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    return {
+        "metric": "reversible LSH layer fwd tokens/s (qk/v maps, LSH attention, output map, "
+                  "chunked FFN) at L=64K; % of roofline",
+        "value": round(M / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) stream, N(0,1/fan_in) bf16 weights, random rotations)",
+        "config": {"workload": w.name, "batch": b, "seq_len": L, "d_model": D, "heads": H,
+                   "d_ff": F, "n_buckets": w.n_buckets, "n_rounds": w.n_rounds,
+                   "causal": w.causal, "self_mask": w.self_mask, "ffn_chunk": w.ffn_chunk},
+        "roofline": roof, "kernels": kernels,
+        "gemm_TFLOPs": round(sum(work[n]["flops"] for n in gemms) /
+                             (sum(per[n] for n in gemms) * 1e-3) / 1e12, 2),
+        "cpu_baseline": None,
+    }
+
+
 def copy_calibration(torch):
     """Plain device copies of known size, after the timed steps: the reference
     that scales the HBM byte counters of a profiled run."""
@@ -232,6 +335,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
+    if args.workload in synth.LAYER_WORKLOADS:
+        print(json.dumps(bench_layer(args, binding, torch, synth)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     log(f"[bench] workload {w}")
     inputs = synth.make_inputs(w)
