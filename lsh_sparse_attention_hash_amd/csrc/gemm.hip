@@ -10,19 +10,20 @@
 // so both operands are K-contiguous: every MFMA fragment is one 16-byte load.
 //
 // Tiles: 128 x 128 outputs per workgroup (4 waves, 64 x 64 each as 2 x 2
-// MFMA blocks), K in steps of 64.  Both operand tiles go through LDS (rows
-// padded to 144 B so the fragment reads are conflict-free), double-buffered:
-// the next K-tile's global loads are in flight in registers while the current
-// one is multiplied, one barrier per K-tile.  Each output element is the same
-// K-ordered sum whatever tile or chunk of rows it falls in, so results do not
-// depend on how the rows are split.
+// MFMA blocks), K in steps of 32.  Both operand tiles go through LDS (rows
+// padded to 80 B), double-buffered: the next K-tile's global loads are in
+// flight in registers while the current one is multiplied, one barrier per
+// K-tile.  At most 128 VGPRs and 40 KB of LDS per workgroup let four
+// workgroups share a CU, so one waits on memory while the others multiply.
+// Each output element is the same K-ordered sum whatever tile or chunk of
+// rows it falls in, so results do not depend on how the rows are split.
 #include "lsh_device.h"
 #include "lsh_launch.h"
 
 namespace lsh {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kTS = 72;   // bf16 per staged row (64 + 8 pad)
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kTS = 40;   // bf16 per staged row (32 + 8 pad: 80 B)
 
 enum ALayout { kAF32Rows = 0, kABf16Rows = 1, kAF32Heads = 2 };
 enum Epilogue { kEpiQkv = 0, kEpiResidual = 1, kEpiReluBf16 = 2 };
@@ -47,42 +48,60 @@ __device__ __forceinline__ uint32_t gemm_pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// One K-tile of A (128 rows x 64 k) in registers.
+// One K-tile of A (128 rows x 32 k) in registers.
 template <int AL>
 struct GemmATile {
-  uint4 r[AL == kABf16Rows ? 4 : 8];
+  uint4 r[AL == kABf16Rows ? 2 : 4];
+};
+
+// Element offset of (row m, k = 0) of A for the rows this thread stages, or
+// -1 past the last row.  Heads layout: k = 64h + j lies at
+// ((b * H + h) * L + l) * 64 + j, i.e. row offset (b * H * L + l) * 64 plus
+// h * L * 64 + j.
+template <int AL>
+struct GemmARows {
+  int64_t off[AL == kABf16Rows ? 2 : 4];
 };
 
 template <int AL>
-__device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g, int m0, int k0) {
+__device__ __forceinline__ void gemm_a_rows(GemmARows<AL>& ar, const GemmArgs& g, int m0) {
+#pragma unroll
+  for (int q = 0; q < (AL == kABf16Rows ? 2 : 4); ++q) {
+    const int idx = threadIdx.x + 256 * q;
+    const int m = m0 + (AL == kABf16Rows ? idx >> 2 : idx >> 3);
+    int64_t o = -1;
+    if (m < g.M) {
+      if (AL == kAF32Heads) {
+        const int bi = m / g.L, l = m - bi * g.L;
+        o = ((int64_t)bi * g.heads * g.L + l) * kHeadDim;
+      } else {
+        o = (int64_t)m * g.lda;
+      }
+    }
+    ar.off[q] = o;
+  }
+}
+
+template <int AL>
+__device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g,
+                                            const GemmARows<AL>& ar, int k0) {
   if (AL == kABf16Rows) {
     const uint16_t* a = static_cast<const uint16_t*>(g.a);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = threadIdx.x + 256 * q;
-      const int row = idx >> 3, c8 = (idx & 7) * 8;
-      const int m = m0 + row;
-      t.r[q] = m < g.M ? load16(a + (int64_t)m * g.lda + k0 + c8) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      const int c8 = ((threadIdx.x + 256 * q) & 3) * 8;
+      t.r[q] = ar.off[q] >= 0 ? load16(a + ar.off[q] + k0 + c8) : make_uint4(0, 0, 0, 0);
     }
   } else {
     const float* a = static_cast<const float*>(g.a);
+    // heads: the K-tile at k0 lies in head k0 / 64
+    const int64_t kofs = AL == kAF32Heads
+                             ? (int64_t)(k0 / kHeadDim) * g.L * kHeadDim + k0 % kHeadDim
+                             : k0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = threadIdx.x + 256 * q;
-      const int row = idx >> 4, c4 = (idx & 15) * 4;
-      const int m = m0 + row;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (m < g.M) {
-        const float* src;
-        if (AL == kAF32Rows) {
-          src = a + (int64_t)m * g.lda + k0 + c4;
-        } else {   // heads: K-tile k0 / 64 is head k0 / 64
-          const int bi = m / g.L, l = m - bi * g.L;
-          src = a + (((int64_t)bi * g.heads + k0 / kHeadDim) * g.L + l) * kHeadDim + c4;
-        }
-        u = load16(src);
-      }
-      t.r[q] = u;
+    for (int q = 0; q < 4; ++q) {
+      const int c4 = ((threadIdx.x + 256 * q) & 7) * 4;
+      t.r[q] = ar.off[q] >= 0 ? load16(a + ar.off[q] + kofs + c4) : make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -91,27 +110,27 @@ template <int AL>
 __device__ __forceinline__ void gemm_store_a(uint16_t* as, const GemmATile<AL>& t) {
   if (AL == kABf16Rows) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const int idx = threadIdx.x + 256 * q;
-      store16(&as[(idx >> 3) * kTS + (idx & 7) * 8], t.r[q]);
+      store16(&as[(idx >> 2) * kTS + (idx & 3) * 8], t.r[q]);
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int idx = threadIdx.x + 256 * q;
       const uint4 u = t.r[q];
       const uint2 p = make_uint2(gemm_pack2(__uint_as_float(u.x), __uint_as_float(u.y)),
                                  gemm_pack2(__uint_as_float(u.z), __uint_as_float(u.w)));
-      *reinterpret_cast<uint2*>(&as[(idx >> 4) * kTS + (idx & 15) * 4]) = p;
+      *reinterpret_cast<uint2*>(&as[(idx >> 3) * kTS + (idx & 7) * 4]) = p;
     }
   }
 }
 
-__device__ __forceinline__ void gemm_load_w(uint4 (&t)[4], const GemmArgs& g, int n_base, int k0) {
+__device__ __forceinline__ void gemm_load_w(uint4 (&t)[2], const GemmArgs& g, int n_base, int k0) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     const int idx = threadIdx.x + 256 * q;
-    const int n = n_base + (idx >> 3), c8 = (idx & 7) * 8;
+    const int n = n_base + (idx >> 2), c8 = (idx & 3) * 8;
     uint4 u = make_uint4(0, 0, 0, 0);
     if (n < g.N) {
       const uint16_t* row = n < g.n0 ? g.w0 + (int64_t)n * g.K : g.w1 + (int64_t)(n - g.n0) * g.K;
@@ -121,11 +140,11 @@ __device__ __forceinline__ void gemm_load_w(uint4 (&t)[4], const GemmArgs& g, in
   }
 }
 
-__device__ __forceinline__ void gemm_store_w(uint16_t* ws, const uint4 (&t)[4]) {
+__device__ __forceinline__ void gemm_store_w(uint16_t* ws, const uint4 (&t)[2]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     const int idx = threadIdx.x + 256 * q;
-    store16(&ws[(idx >> 3) * kTS + (idx & 7) * 8], t[q]);
+    store16(&ws[(idx >> 2) * kTS + (idx & 3) * 8], t[q]);
   }
 }
 
@@ -150,8 +169,9 @@ __device__ __forceinline__ void gemm_emit(const GemmArgs& g, int m, int n, float
   }
 }
 
+// at most 128 VGPRs: four workgroups per CU hide each other's load latency
 template <int AL, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t as[2][kBM * kTS];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][kBN * kTS];
   const int lane = lane_id();
@@ -172,9 +192,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  GemmARows<AL> ar;
+  gemm_a_rows<AL>(ar, g, m0);
   GemmATile<AL> ta;
-  uint4 tw[4];
-  gemm_load_a<AL>(ta, g, m0, 0);
+  uint4 tw[2];
+  gemm_load_a<AL>(ta, g, ar, 0);
   gemm_load_w(tw, g, n_base, 0);
   gemm_store_a<AL>(as[0], ta);
   gemm_store_w(ws[0], tw);
@@ -183,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   for (int kt = 0; kt < nkt; ++kt) {
     const bool more = kt + 1 < nkt;
     if (more) {   // next K-tile in flight during the products
-      gemm_load_a<AL>(ta, g, m0, (kt + 1) * kBK);
+      gemm_load_a<AL>(ta, g, ar, (kt + 1) * kBK);
       gemm_load_w(tw, g, n_base, (kt + 1) * kBK);
     }
     const uint16_t* a_s = as[kt & 1];

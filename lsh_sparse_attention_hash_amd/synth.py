@@ -155,8 +155,8 @@ class LayerWorkload:
 
 LAYER_WORKLOADS = {
     # the headline attention shape inside one layer: 8 heads of 64 features,
-    # a 4x feed-forward expansion evaluated 8,192 tokens at a time
-    "layer_long": LayerWorkload("layer_long", 1, 65536, 512, 2048, 1024, 8, True, True, 8192, 8),
+    # a 4x feed-forward expansion evaluated 32,768 tokens at a time
+    "layer_long": LayerWorkload("layer_long", 1, 65536, 512, 2048, 1024, 8, True, True, 32768, 8),
 }
 
 

@@ -197,7 +197,7 @@ def test_inverse_reconstructs_the_inputs(B, runs, name):
 
 def test_layer_long_full_size_sampled(B):
     """The headline attention shape inside one layer (8 x 64 features,
-    65,536 tokens, d_ff 2,048, FFN in chunks of 8,192): the one-call layer
+    65,536 tokens, d_ff 2,048, FFN in chunks of 32,768): the one-call layer
     equals its calls, buckets and rows are sampled against the oracle."""
     w = synth.LAYER_WORKLOADS["layer_long"]
     r = Run(B, w)
