@@ -170,7 +170,10 @@ __device__ __forceinline__ void attend_keys(const LocalLds& sm, const bf16x8 (&q
   }
 }
 
-template <bool CAUSAL, bool SELF>
+// NPRE = 1: any window, the next key chunk in flight during the current one.
+// NPRE = 3: windows of at most three chunks, all of them requested at once, so
+// the workgroup waits on memory once instead of once per chunk.
+template <bool CAUSAL, bool SELF, int NPRE>
 __global__ __launch_bounds__(256) void local_bf16_kernel(LocalArgs a) {
   __shared__ __attribute__((aligned(16))) LocalLds sm;
   const int lane = lane_id();
@@ -196,14 +199,29 @@ __global__ __launch_bounds__(256) void local_bf16_kernel(LocalArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 5; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  KeyRegs kr;
-  gather_keys(kr, xb, vb, k0);
-  for (int kc = k0; kc <= k1; ++kc) {
-    commit_keys(sm, kr);
-    if (kc < k1) gather_keys(kr, xb, vb, kc + 1);   // in flight during the compute
-    __syncthreads();
-    attend_keys<CAUSAL, SELF>(sm, qf, st, kc == c, qi);
-    __syncthreads();
+  if (NPRE == 1) {
+    KeyRegs kr;
+    gather_keys(kr, xb, vb, k0);
+    for (int kc = k0; kc <= k1; ++kc) {
+      commit_keys(sm, kr);
+      if (kc < k1) gather_keys(kr, xb, vb, kc + 1);   // in flight during the compute
+      __syncthreads();
+      attend_keys<CAUSAL, SELF>(sm, qf, st, kc == c, qi);
+      __syncthreads();
+    }
+  } else {
+    KeyRegs kr[NPRE];
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i)
+      if (k0 + i <= k1) gather_keys(kr[i], xb, vb, k0 + i);
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      if (k0 + i > k1) break;
+      commit_keys(sm, kr[i]);
+      __syncthreads();
+      attend_keys<CAUSAL, SELF>(sm, qf, st, k0 + i == c, qi);
+      __syncthreads();
+    }
   }
 
   const float sum = st.o[4][0];
@@ -299,6 +317,20 @@ __global__ __launch_bounds__(64) void local_f32_kernel(LocalArgs a, int causal, 
   a.lse[bh * a.L + qp] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+template <int NPRE>
+static hipError_t launch_local_bf16(const Shape& s, const LocalArgs& a, unsigned grid,
+                                    hipStream_t stream) {
+  if (s.causal && s.self_mask)
+    hipLaunchKernelGGL((local_bf16_kernel<true, true, NPRE>), dim3(grid), dim3(256), 0, stream, a);
+  else if (s.causal)
+    hipLaunchKernelGGL((local_bf16_kernel<true, false, NPRE>), dim3(grid), dim3(256), 0, stream, a);
+  else if (s.self_mask)
+    hipLaunchKernelGGL((local_bf16_kernel<false, true, NPRE>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((local_bf16_kernel<false, false, NPRE>), dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_local(const Shape& s, int before, int after, const void* qk, const void* v,
                         float* y, float* lse, hipStream_t stream) {
   LocalArgs a;
@@ -316,15 +348,9 @@ hipError_t launch_local(const Shape& s, int before, int after, const void* qk, c
     hipLaunchKernelGGL(local_f32_kernel, dim3(grid), dim3(64), 0, stream, a, s.causal, s.self_mask);
     return hipGetLastError();
   }
-  if (s.causal && s.self_mask)
-    hipLaunchKernelGGL((local_bf16_kernel<true, true>), dim3(grid), dim3(256), 0, stream, a);
-  else if (s.causal)
-    hipLaunchKernelGGL((local_bf16_kernel<true, false>), dim3(grid), dim3(256), 0, stream, a);
-  else if (s.self_mask)
-    hipLaunchKernelGGL((local_bf16_kernel<false, true>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((local_bf16_kernel<false, false>), dim3(grid), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (a.before + 1 + (s.causal ? 0 : a.after) <= 3)
+    return launch_local_bf16<3>(s, a, grid, stream);
+  return launch_local_bf16<1>(s, a, grid, stream);
 }
 
 }  // namespace lsh
