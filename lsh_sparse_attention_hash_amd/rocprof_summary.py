@@ -28,10 +28,12 @@ KERNEL_SOURCES = {
     "attend": [f"{CSRC}/attend.hip", f"{CSRC}/lsh_device.h"],
     "combine": [f"{CSRC}/combine.hip", f"{CSRC}/lsh_device.h"],
     "local": [f"{CSRC}/local.hip", f"{CSRC}/lsh_device.h"],
+    "gemm": [f"{CSRC}/gemm.hip", f"{CSRC}/lsh_device.h"],
 }
 # kernel name prefix (as rocprofv3 prints it) -> step
 STEP_OF = [("lsh::hash", "hash"), ("lsh::sort", "sort"), ("lsh::attend", "attend"),
-           ("lsh::union_keys", "attend"), ("lsh::combine", "combine"), ("lsh::local", "local")]
+           ("lsh::union_keys", "attend"), ("lsh::combine", "combine"), ("lsh::local", "local"),
+           ("lsh::gemm", "gemm")]
 COPY_BYTES = 512 << 20
 
 
@@ -95,7 +97,7 @@ def traffic(args):
             "| kernel | read MB | written MB |", "|---|---|---|"] + lines
     out += ["", "Per step (bytes per launch, all kernels of the step; digest of the step's sources):",
             "", "| step | workload | digest | bytes | read MB | written MB |", "|---|---|---|---|---|---|"]
-    for st in ("hash", "sort", "attend", "combine", "local"):
+    for st in ("hash", "sort", "attend", "combine", "local", "gemm"):
         if st in steps:
             fb, wb = steps[st]
             out.append(f"| {st} | {args.workload} | {source_digest(st)} | {fb + wb:.0f} | "
