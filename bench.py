@@ -215,8 +215,31 @@ def bench_layer(args, binding, torch, synth):
         "roofline": roof, "kernels": kernels,
         "gemm_TFLOPs": round(sum(work[n]["flops"] for n in gemms) /
                              (sum(per[n] for n in gemms) * 1e-3) / 1e12, 2),
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_layer(w, inp, synth),
     }
+
+
+def cpu_baseline_layer(w, inp, synth):
+    """The fp64 oracle of the whole layer forward (dense maps in plain loops,
+    the LSH oracle for the attention) over the full workload."""
+    threads = len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    import numpy as np
+    from oracle import layer as olayer
+    from oracle import oracle
+    oracle.build(force=False)
+    log("[bench] timing the CPU oracle of the layer")
+    wf = {k: synth.to_f64(inp[k], "bf16") for k in ("w_qk", "w_v", "w_o", "rot", "w_1", "w_2")}
+    wf.update({k: inp[k].astype(np.float64) for k in ("b_1", "b_2")})
+    cfg = dict(n_buckets=w.n_buckets, n_rounds=w.n_rounds, causal=w.causal,
+               self_mask=w.self_mask, ffn_chunk=w.ffn_chunk)
+    t0 = time.perf_counter()
+    olayer.reversible_forward(inp["x1"].astype(np.float64), inp["x2"].astype(np.float64), wf, cfg)
+    dt = time.perf_counter() - t0
+    return {"value": w.batch * w.seq_len / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole layer forward (batch {w.batch}, L={w.seq_len}, d_model "
+                      f"{w.d_model}, d_ff {w.d_ff}), fp64"}
 
 
 def copy_calibration(torch):
