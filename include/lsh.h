@@ -32,7 +32,8 @@
  *     even with 2 <= n_buckets <= 16384; 1 <= n_rounds <= 1024;
  *     batch * heads * n_rounds * seq_len < 2^31.  A zero batch, heads or
  *     seq_len is an empty problem: the call returns LSH_OK and does nothing.
- *   - Inputs must be finite.
+ *   - Inputs must be finite, with |x|_2 < 2^60 and |R_j|_2 < 2^60 (the
+ *     fp32 headroom of the matrix-core scores and the squared key norms).
  *   - Calls are thread-safe and may run concurrently on different streams.
  */
 #ifndef LSH_H_

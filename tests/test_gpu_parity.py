@@ -138,6 +138,26 @@ def test_repeat_runs_are_bitwise_identical(B):
             assert np.array_equal(x, host(t))
 
 
+@pytest.mark.parametrize("log2_scale", [30, -60])
+def test_scaled_inputs_parity(B, log2_scale):
+    """qk scaled by a power of two (exact in bf16): very large scores, and
+    scores so small that fp32 sums approach the denormal range (those rows
+    must be settled in fp64).  Buckets are scale-invariant."""
+    w = synth.Workload(f"scaled{log2_scale}", 1, 2, 2048, 64, 64, 2, 64, True, True, "bf16",
+                       24 + abs(log2_scale))
+    inp = synth.make_inputs(w)
+    scaled = synth.to_f64(inp["qk"], "bf16") * 2.0 ** log2_scale
+    inp = dict(inp, qk=synth.bf16_bits(scaled.astype(np.float32)))
+    assert np.array_equal(synth.to_f64(inp["qk"], "bf16"), scaled)   # the scaling was exact
+    f = run_gpu(B, w, inp)
+    ref = oracle.forward(scaled, synth.to_f64(inp["v"], "bf16"), synth.to_f64(inp["rot"], "bf16"),
+                         w.n_buckets, w.n_rounds, w.chunk_len, w.causal, w.self_mask)
+    assert np.array_equal(host(f.buckets), ref["buckets"])
+    assert_close_lse(host(f.lse), ref["lse"], 2e-2 * max(1.0, 2.0 ** log2_scale), "lse")
+    assert_close(host(f.y), ref["y"], 2e-2, "y")
+    say(f"[scaled 2^{log2_scale}] fallback rows {int(host(f.fallback_rows)[0])}")
+
+
 def test_hash_matches_exactly_on_skewed_and_tied_inputs(B):
     """Integer-valued bf16 inputs produce exact ties; zero rows tie everywhere."""
     w = synth.Workload("ties", 1, 2, 1024, 64, 64, 2, 64, True, True, "bf16", 20)
