@@ -170,6 +170,11 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
       const int4 w = *reinterpret_cast<const int4*>(&kkey[qrow * kMaxUnionRounds + q4]);
       kq[q4] = w.x; kq[q4 + 1] = w.y; kq[q4 + 2] = w.z; kq[q4 + 3] = w.w;
     }
+    // rounds past the last never match: keys are >= -2, so a difference from
+    // 2^30 is never 0 or 1
+#pragma unroll
+    for (int q = 0; q < kMaxUnionRounds; ++q)
+      if (q >= a.rounds) kq[q] = 1 << 30;
   }
 
   // scores, log2-scaled: s[t][i] is key 16t + 4g + i of the window for query ql
@@ -223,8 +228,7 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
           const int4 w = *reinterpret_cast<const int4*>(kk + q4);
           const int wk[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            cnt += (q4 + e < a.rounds && (uint32_t)(kq[q4 + e] - wk[e]) <= 1u) ? 1 : 0;
+          for (int e = 0; e < 4; ++e) cnt += (uint32_t)(kq[q4 + e] - wk[e]) <= 1u ? 1 : 0;
         }
         if (oka[i]) s[t][i] -= __builtin_amdgcn_logf((float)cnt);
       }
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(256) void union_keys_kernel(const int32_t* __restri
   const int span = L / kChunk + 1;
   int32_t* out = keys + g * stride;
   for (int r = 0; r < stride; ++r) {
-    int32_t k = -2;   // padding, never compared
+    int32_t k = -2;   // padding (the query side pads with 2^30: never a match)
     if (r < rounds) {
       const int64_t f = (bh * rounds + r) * L + pos;
       const int b = min(max(buckets[f], 0), nb - 1);
