@@ -7,12 +7,19 @@ input with every tensor already resident in HBM.  Default workload: the
 headline shape (batch 1, 8 heads, L = 65,536, d = 64, B = 1,024 buckets,
 8 hash rounds, chunk 64, causal, self-masked, bf16 inputs).
 
-Prints one JSON line: tokens/s (batch * L per step, all heads and rounds),
-the roofline position of the dominant kernel (per-launch time from HIP
-events on the stream the kernels run on) and the fp64 CPU oracle timed on a
-bounded sample of the same workload on this host's cores.
+Prints one JSON line: tokens/s (batch * L per step, all heads and rounds;
+`value` over the whole timed region, plus the median step and its p10-p90
+range from HIP events around every step), token-head-rounds/s, the roofline
+position of the dominant kernel (per-launch time from HIP events on the
+stream the kernels run on), the roofline time of a whole step against the
+median step, the same figures for the other LSH configs (tiny, small,
+medium, verylong), and the fp64 CPU oracle timed on a bounded sample of the
+same workload on this host's cores (with the CPU model, and the small
+configs on all cores and on one).
 
     python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+                    [--no-other-configs] [--union]
+    python bench.py --workload local_long | layer_long
 """
 import argparse
 import json
@@ -89,15 +96,17 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, inputs, union=False):
+def cpu_baseline(w, inputs, union=False, small_configs=True):
     """The fp64 oracle on a bounded sample of the workload: every head for the
     shapes up to L = 64K (a few seconds on a many-core host), one head of the
-    half-million-token shape."""
+    half-million-token shape.  With `small_configs`, also the full forward of
+    the tiny, small and medium configs on all cores and on one core."""
     threads = len(os.sched_getaffinity(0))
     os.environ["OMP_NUM_THREADS"] = str(threads)
     from lsh_sparse_attention_hash_amd import synth
     from oracle import oracle
     oracle.build(force=False)
+    oracle.set_threads(threads)
     hs = w.heads if w.seq_len <= 65536 else 1
     qk = synth.to_f64(inputs["qk"][:, :hs], w.dtype)
     v = synth.to_f64(inputs["v"][:, :hs], w.dtype)
@@ -107,13 +116,16 @@ def cpu_baseline(w, inputs, union=False):
                                                         w.chunk_len, w.causal, w.self_mask)
     dt = time.perf_counter() - t0
     full_est = dt * w.heads / hs
-    return {"value": w.batch * w.seq_len / full_est, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
+    out = {"value": w.batch * w.seq_len / full_est, "unit": "tokens/s", "cores": threads,
+           "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{hs} of {w.heads} heads (batch {w.batch}, L={w.seq_len}, all "
                       f"{w.n_rounds} rounds), full fp64 forward (hash, sort, "
                       f"{'set-union attend' if union else 'attend'}, combine)" +
                       ("" if hs == w.heads else
                                      f"; tokens/s scaled by {w.heads // hs}x to all heads")}
+    if not union and small_configs:
+        out["small_configs"] = cpu_small_configs(synth)
+    return out
 
 
 def bench_layer(args, binding, torch, synth):
@@ -134,10 +146,14 @@ def bench_layer(args, binding, torch, synth):
         layer.forward(x1, x2, y1, y2)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     t0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        ev[k][0].record(stream)
         layer.forward(x1, x2, y1, y2)
+        ev[k][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -206,7 +222,8 @@ def bench_layer(args, binding, torch, synth):
         "metric": "reversible LSH layer fwd tokens/s (qk/v maps, LSH attention, output map, "
                   "chunked FFN) at L=64K; % of roofline",
         "value": round(M / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "step_ms": pct([a.elapsed_time(e) for a, e in ev]), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) stream, N(0,1/fan_in) bf16 weights, random rotations)",
         "config": {"workload": w.name, "batch": b, "seq_len": L, "d_model": D, "heads": H,
@@ -228,6 +245,7 @@ def cpu_baseline_layer(w, inp, synth):
     from oracle import layer as olayer
     from oracle import oracle
     oracle.build(force=False)
+    oracle.set_threads(threads)
     log("[bench] timing the CPU oracle of the layer")
     wf = {k: synth.to_f64(inp[k], "bf16") for k in ("w_qk", "w_v", "w_o", "rot", "w_1", "w_2")}
     wf.update({k: inp[k].astype(np.float64) for k in ("b_1", "b_2")})
@@ -237,7 +255,7 @@ def cpu_baseline_layer(w, inp, synth):
     olayer.reversible_forward(inp["x1"].astype(np.float64), inp["x2"].astype(np.float64), wf, cfg)
     dt = time.perf_counter() - t0
     return {"value": w.batch * w.seq_len / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"the whole layer forward (batch {w.batch}, L={w.seq_len}, d_model "
                       f"{w.d_model}, d_ff {w.d_ff}), fp64"}
 
@@ -291,7 +309,8 @@ def bench_local(args, w, inputs, binding, torch):
         "metric": "local chunked attention fwd tokens/s (all heads) at L=64K; % of HBM roofline",
         "value": round(w.batch * w.seq_len / (ms * 1e-3), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": round(ms, 5), "step_ms": pct([a.elapsed_time(b) for a, b in ev]),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
@@ -318,24 +337,161 @@ def cpu_baseline_local(w, inputs):
     from lsh_sparse_attention_hash_amd import synth
     from oracle import oracle
     oracle.build(force=False)
+    oracle.set_threads(threads)
     qk = synth.to_f64(inputs["qk"], w.dtype)
     v = synth.to_f64(inputs["v"], w.dtype)
     t0 = time.perf_counter()
     oracle.local_attend(qk, v, w.chunk_len, w.look_before, w.look_after, w.causal, w.self_mask)
     dt = time.perf_counter() - t0
     return {"value": w.batch * w.seq_len / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"all {w.heads} heads (batch {w.batch}, L={w.seq_len}), full fp64 local "
                       f"attention"}
+
+
+def pct(xs):
+    """Median and the p10-p90 range of a list of times (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def time_forward(args, w, inputs, binding, torch, union=False):
+    """Warm-up steps, then `args.steps` timed passes of the four calls on one
+    stream with HIP events around each pass and each call (recorded on the
+    stream the calls are launched on).  Inputs and scratch are allocated
+    before the timed region."""
+    qk = binding.to_device(inputs["qk"], w.dtype)
+    v = binding.to_device(inputs["v"], w.dtype)
+    rot = binding.to_device(inputs["rot"], w.dtype)
+    f = binding.Forward(binding.config_for(w))
+    stream = torch.cuda.current_stream()
+    attend = f.attend_union if union else f.attend
+    for _ in range(args.warmup):
+        f.run(qk, v, rot, union=union)
+    torch.cuda.synchronize()
+    names = ("hash", "sort", "attend", "combine")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        f.hash(qk, rot)
+        e[1].record(stream)
+        f.sort()
+        e[2].record(stream)
+        attend(qk, v)
+        e[3].record(stream)
+        f.combine(v)
+        e[4].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    kt = {n: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]
+          for i, n in enumerate(names)}
+    steps = [ev[k][0].elapsed_time(ev[k][4]) for k in range(args.steps)]
+    per = {n: sum(kt[n]) / args.steps for n in names}
+    log(f"[bench] {w.name}: {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s); per call "
+        "ms: " + ", ".join(f"{n} {per[n]:.4f}" for n in names))
+    out = {"ms": ms, "per": per, "step_pct": pct(steps),
+           "kernel_pct": {n: pct(kt[n]) for n in names},
+           "fallback_rows": int(f.fallback_rows.item()) // (args.warmup + args.steps)}
+    del f, qk, v, rot
+    torch.cuda.synchronize()
+    return out
+
+
+def roofline_us(w, union=False):
+    """Time of one forward at the roofline: each call at the larger of its
+    algorithmic bytes at HBM peak and its algorithmic flops at the dense bf16
+    MFMA peak (flops counted for the hash only: the attention's intensity sits
+    far below the ridge point)."""
+    work = algorithmic(w, union)
+    t = {n: work[n]["bytes"] / (HBM_PEAK_GBS * 1e9) for n in work}
+    t["hash"] = max(t["hash"], work["hash"]["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+    return {n: round(x * 1e6, 2) for n, x in t.items()}
+
+
+def forward_summary(w, tm, union=False):
+    """Median-based figures of one config: tokens/s and token-head-rounds/s
+    over the median step, and the roofline time over the median step."""
+    med = tm["step_pct"]["median"] * 1e-3
+    roof = roofline_us(w, union)
+    t_roof = sum(roof.values())
+    return {"tokens_per_s_median": round(w.batch * w.seq_len / med, 1),
+            "token_head_rounds_per_s": round(w.token_rounds / med, 1),
+            "roofline_us": {**roof, "total": round(t_roof, 2)},
+            "frac_of_roofline_time": round(t_roof * 1e-6 / med, 4)}
+
+
+def other_configs(args, w0, binding, torch, synth):
+    """The same protocol on every other LSH-attention config (throughput only;
+    their parity is covered by the tests)."""
+    res = {}
+    for name, w in synth.WORKLOADS.items():
+        if name == w0.name or w.is_local:
+            continue
+        inputs = synth.make_inputs(w)
+        tm = time_forward(args, w, inputs, binding, torch)
+        del inputs
+        res[name] = {"batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                     "n_buckets": w.n_buckets, "n_rounds": w.n_rounds, "dtype": w.dtype,
+                     "ms_per_step": round(tm["ms"], 5), "step_ms": tm["step_pct"],
+                     **forward_summary(w, tm),
+                     "kernels_ms": {n: round(x, 5) for n, x in tm["per"].items()},
+                     "hash_fallback_rows_per_step": tm["fallback_rows"]}
+    return res
+
+
+def cpu_model():
+    """The host CPU's model name, as lscpu prints it (from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_small_configs(synth):
+    """The oracle's full forward on the small configs, on every core the
+    process may use and on one core."""
+    from oracle import oracle
+    threads = len(os.sched_getaffinity(0))
+    res = {}
+    for name in ("tiny", "small", "medium"):
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        qk, v, rot = (synth.to_f64(inp[k], w.dtype) for k in ("qk", "v", "rot"))
+        row = {}
+        for th in (threads, 1):
+            oracle.set_threads(th)
+            t0 = time.perf_counter()
+            oracle.forward(qk, v, rot, w.n_buckets, w.n_rounds, w.chunk_len, w.causal,
+                           w.self_mask)
+            row["seconds_1_thread" if th == 1 else "seconds"] = round(time.perf_counter() - t0, 4)
+        row["tokens_per_s"] = round(w.batch * w.seq_len / row["seconds"], 1)
+        res[name] = row
+    oracle.set_threads(threads)
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time the headline config only (skip tiny/small/medium/verylong)")
     ap.add_argument("--union", action="store_true",
                     help="set reading of the union over rounds (lsh_chunk_attend_union)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -367,45 +523,9 @@ def main():
     if w.is_local:
         print(json.dumps(bench_local(args, w, inputs, binding, torch)), flush=True)
         return
-    qk = binding.to_device(inputs["qk"], w.dtype)
-    v = binding.to_device(inputs["v"], w.dtype)
-    rot = binding.to_device(inputs["rot"], w.dtype)
-    f = binding.Forward(binding.config_for(w))
-    stream = torch.cuda.current_stream()
-
-    attend = f.attend_union if args.union else f.attend
-    for _ in range(args.warmup):
-        f.run(qk, v, rot, union=args.union)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-
+    tm = time_forward(args, w, inputs, binding, torch, args.union)
+    ms, per = tm["ms"], tm["per"]
     names = ("hash", "sort", "attend", "combine")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for k in range(args.steps):
-        e = ev[k]
-        e[0].record(stream)
-        f.hash(qk, rot)
-        e[1].record(stream)
-        f.sort()
-        e[2].record(stream)
-        attend(qk, v)
-        e[3].record(stream)
-        f.combine(v)
-        e[4].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
-    per = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
-           for i, n in enumerate(names)}
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s); per call ms: "
-        + ", ".join(f"{n} {per[n]:.4f}" for n in names))
-
     if args.copy_calibration:
         copy_calibration(torch)
 
@@ -413,8 +533,8 @@ def main():
     kernels = {}
     for n in names:
         t = per[n] * 1e-3
-        kb = {"ms": round(per[n], 5), "algorithmic_bytes": work[n]["bytes"],
-              "GBps": round(work[n]["bytes"] / t / 1e9, 1)}
+        kb = {"ms": round(per[n], 5), "median_ms": round(tm["kernel_pct"][n]["median"], 5),
+              "algorithmic_bytes": work[n]["bytes"], "GBps": round(work[n]["bytes"] / t / 1e9, 1)}
         if "flops" in work[n]:
             kb["algorithmic_flops"] = work[n]["flops"]
             kb["TFLOPs"] = round(work[n]["flops"] / t / 1e12, 2)
@@ -454,11 +574,15 @@ def main():
                    "chunk_len": w.chunk_len, "causal": w.causal, "self_mask": w.self_mask,
                    "qk": ("gaussian mixture, %d clusters" % w.n_clusters) if w.n_clusters
                    else "N(0,1)"},
+        "step_ms": tm["step_pct"],
+        **forward_summary(w, tm, args.union),
         "roofline": roof,
         "kernels": kernels,
-        "hash_fallback_rows_per_step": int(f.fallback_rows.item()) // (args.warmup + args.steps),
+        "hash_fallback_rows_per_step": tm["fallback_rows"],
         "cpu_baseline": None,
     }
+    if not args.union and not args.no_other_configs:
+        result["other_configs"] = other_configs(args, w, binding, torch, synth)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(w, inputs, args.union)

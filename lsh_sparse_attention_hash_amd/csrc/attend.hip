@@ -15,7 +15,7 @@
 // P^T fragments of two score tiles are directly the B operand of the PV
 // product (the contraction over keys is permuted consistently in A and B).
 // V is stored transposed in LDS while it is staged.
-// fp32: one thread per query, fp32 arithmetic with an online softmax.
+// fp32: one workgroup per chunk, four threads per query, fp32 arithmetic.
 #include <math.h>
 
 #include "lsh_device.h"
@@ -334,14 +334,35 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
 }
 
 // ------------------------------------------------------------------- fp32
-// One wave per chunk; lane q is query q of the chunk.  The window is staged
-// one chunk (64 keys) at a time; the softmax runs online in fp32.
-__global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
-  __shared__ float xw[kChunk][kHeadDim];
-  __shared__ float vw[kChunk][kHeadDim];
+// One workgroup of 256 threads per chunk; the 64 queries are the chunk's
+// rows.  The window is taken one 64-key half at a time (the chunk itself,
+// then its predecessor): the half's x and v rows are staged in LDS with
+// coalesced 16-byte loads, thread t scores query t/4 against keys t%4,
+// t%4 + 4, ... of the half, the four threads of a query agree on the running
+// maximum, and the half's weights go through LDS so that thread t can sum the
+// value features 16*(t%4) .. 16*(t%4)+15 of its query.  fp32 arithmetic, a
+// softmax rescaled once between the halves.
+constexpr int kF32Row = 68;   // floats per staged row (64 + 4 pad: 4-bank offset per row)
+
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1));
+  return fmaxf(x, __shfl_xor(x, 2));
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  return x + __shfl_xor(x, 2);
+}
+
+__global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
+  __shared__ float xw[kChunk * kF32Row];
+  __shared__ float vw[kChunk * kF32Row];
+  __shared__ float pw[kChunk * (kChunk + 1)];   // weights [query][key], row padded by 1
   __shared__ float kinv[kChunk];
   __shared__ int32_t kbk[kChunk], kpos[kChunk];
-  const int lane = lane_id();
+  const int t = threadIdx.x;
+  const int qi = t >> 2;      // query of the chunk (scores, outputs)
+  const int part = t & 3;     // key residue (scores) / feature block (outputs)
   const int64_t seg = blockIdx.x / a.nchunks;
   const int c = blockIdx.x % a.nchunks;
   const int64_t bh = seg / a.rounds;
@@ -350,65 +371,107 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttendArgs a) {
   const int32_t* bk = a.buckets + seg * a.L;
   const int32_t* pm = a.perm + seg * a.L;
 
-  const int qp = clamp_index(pm[(int64_t)c * kChunk + lane], a.L);
+  const int qp = clamp_index(pm[(int64_t)c * kChunk + qi], a.L);
   const int qb = bk[qp];
-  float xq[kHeadDim];
+  float4 xq[kHeadDim / 4];
 #pragma unroll
-  for (int k = 0; k < kHeadDim; ++k) xq[k] = xb[(int64_t)qp * kHeadDim + k];
-  float m = -INFINITY, l = 0.f, o[kHeadDim];
-#pragma unroll
-  for (int k = 0; k < kHeadDim; ++k) o[k] = 0.f;
+  for (int k = 0; k < kHeadDim / 4; ++k)
+    xq[k] = *reinterpret_cast<const float4*>(xb + (int64_t)qp * kHeadDim + 4 * k);
+  const int32_t* uq = a.ukeys ? a.ukeys + (bh * a.L + qp) * a.ukey_stride : nullptr;
 
-  for (int cc = (c == 0 ? 0 : c - 1); cc <= c; ++cc) {
-    __syncthreads();
-    const int pos = clamp_index(pm[(int64_t)cc * kChunk + lane], a.L);
+  float m = -INFINITY, l = 0.f;
+  float o[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) o[k] = 0.f;
+
+  for (int h = 0; h < (c == 0 ? 1 : 2); ++h) {
+    const int cc = c - h;
+    // stage: thread t loads columns 16*part .. 16*part+15 of row qi of chunk cc
+    const int pos = clamp_index(pm[(int64_t)cc * kChunk + qi], a.L);
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < kHeadDim; ++k) {
-      const float xv = xb[(int64_t)pos * kHeadDim + k];
-      xw[lane][k] = xv;
-      vw[lane][k] = vb[(int64_t)pos * kHeadDim + k];
-      ss += xv * xv;
+    for (int k = 0; k < 4; ++k) {
+      const float4 xv = *reinterpret_cast<const float4*>(xb + (int64_t)pos * kHeadDim + 16 * part + 4 * k);
+      const float4 vv = *reinterpret_cast<const float4*>(vb + (int64_t)pos * kHeadDim + 16 * part + 4 * k);
+      *reinterpret_cast<float4*>(&xw[qi * kF32Row + 16 * part + 4 * k]) = xv;
+      *reinterpret_cast<float4*>(&vw[qi * kF32Row + 16 * part + 4 * k]) = vv;
+      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
     }
-    kinv[lane] = 1.0f / (fmaxf(sqrtf(ss), kNormEps) * 8.0f);
-    kbk[lane] = bk[pos];
-    kpos[lane] = pos;
+    ss = quad_sum(ss);
+    if (part == 0) {
+      kinv[qi] = 1.0f / (fmaxf(sqrtf(ss), kNormEps) * 8.0f);
+      kbk[qi] = bk[pos];
+      kpos[qi] = pos;
+    }
     __syncthreads();
-    for (int kk = 0; kk < kChunk; ++kk) {
-      if (kbk[kk] != qb || (a.causal && kpos[kk] > qp) || (a.self_mask && kpos[kk] == qp)) continue;
-      float dot = 0.f;
+
+    float sc[16];
+    float mh = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < kHeadDim; ++k) dot = fmaf(xq[k], xw[kk][k], dot);
-      float sc = dot * kinv[kk];
-      if (a.ukeys) {
+    for (int i = 0; i < 16; ++i) {
+      const int kk = part + 4 * i;
+      const float* xr = &xw[kk * kF32Row];
+      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+      for (int k = 0; k < kHeadDim / 4; ++k) {
+        const float4 kv = *reinterpret_cast<const float4*>(xr + 4 * k);
+        d0 = fmaf(xq[k].x, kv.x, d0);
+        d1 = fmaf(xq[k].y, kv.y, d1);
+        d2 = fmaf(xq[k].z, kv.z, d2);
+        d3 = fmaf(xq[k].w, kv.w, d3);
+      }
+      float s = ((d0 + d1) + (d2 + d3)) * kinv[kk];
+      const int kp = kpos[kk];
+      const bool keep = kbk[kk] == qb && !(a.causal && kp > qp) && !(a.self_mask && kp == qp);
+      if (keep && uq) {
         // set union over rounds: the key weighs once over all rounds
-        const int32_t* uq = a.ukeys + (bh * a.L + qp) * a.ukey_stride;
-        const int32_t* uj = a.ukeys + (bh * a.L + kpos[kk]) * a.ukey_stride;
+        const int32_t* uj = a.ukeys + (bh * a.L + kp) * a.ukey_stride;
         int cnt = 0;
         for (int r = 0; r < a.rounds; ++r) cnt += (uint32_t)(uq[r] - uj[r]) <= 1u ? 1 : 0;
-        sc -= logf((float)cnt);
+        s -= logf((float)cnt);
       }
-      if (sc > m) {
-        const float f = expf(m - sc);
-        l *= f;
-#pragma unroll
-        for (int k = 0; k < kHeadDim; ++k) o[k] *= f;
-        m = sc;
-      }
-      const float p = expf(sc - m);
-      l += p;
-#pragma unroll
-      for (int k = 0; k < kHeadDim; ++k) o[k] = fmaf(p, vw[kk][k], o[k]);
+      sc[i] = keep ? s : -INFINITY;
+      mh = fmaxf(mh, sc[i]);
     }
+    const float mn = fmaxf(m, quad_max(mh));
+    // rescale what the earlier half summed; no key so far leaves it at zero
+    const float f = (mn == -INFINITY) ? 0.f : expf(m - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = (mn == -INFINITY) ? 0.f : expf(sc[i] - mn);
+      pw[qi * (kChunk + 1) + part + 4 * i] = p;
+      ls += p;
+    }
+    l = l * f + quad_sum(ls);
+    m = mn;
+    __syncthreads();
+
+    const float* pr = &pw[qi * (kChunk + 1)];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o[k] *= f;
+    for (int kk = 0; kk < kChunk; ++kk) {
+      const float p = pr[kk];
+      const float* vr = &vw[kk * kF32Row + 16 * part];
+#pragma unroll
+      for (int k = 0; k < 16; k += 4) {
+        const float4 vv = *reinterpret_cast<const float4*>(vr + k);
+        o[k] = fmaf(p, vv.x, o[k]);
+        o[k + 1] = fmaf(p, vv.y, o[k + 1]);
+        o[k + 2] = fmaf(p, vv.z, o[k + 2]);
+        o[k + 3] = fmaf(p, vv.w, o[k + 3]);
+      }
+    }
+    __syncthreads();
   }
-  const int64_t slot = (int64_t)c * kChunk + lane;
-  float* orow = a.o + (seg * a.L + slot) * kHeadDim;
+  const int64_t slot = (int64_t)c * kChunk + qi;
+  float* orow = a.o + (seg * a.L + slot) * kHeadDim + 16 * part;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-  for (int k = 0; k < kHeadDim; k += 4)
+  for (int k = 0; k < 16; k += 4)
     *reinterpret_cast<float4*>(orow + k) =
         make_float4(o[k] * inv, o[k + 1] * inv, o[k + 2] * inv, o[k + 3] * inv);
-  a.lse[seg * a.L + slot] = (m == -INFINITY) ? -INFINITY : m + logf(l);
+  if (part == 0) a.lse[seg * a.L + slot] = (m == -INFINITY) ? -INFINITY : m + logf(l);
 }
 
 int union_key_stride(const Shape& s) { return (s.rounds + 3) & ~3; }
@@ -466,7 +529,7 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
   if (!s.bf16) {
     a.cpw = 1;
     a.runs_per_seg = a.nchunks;
-    hipLaunchKernelGGL(attend_f32_kernel, dim3((unsigned)(S * a.nchunks)), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(attend_f32_kernel, dim3((unsigned)(S * a.nchunks)), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   // runs of consecutive chunks per workgroup: long runs re-gather fewer

@@ -54,6 +54,7 @@
  * Every function returns 0 on success and -1 on an invalid argument.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -608,4 +609,12 @@ int oracle_linear(int64_t rows, int n_out, int n_in, const double* a,
     }
   }
   return 0;
+}
+
+/* Thread count of the OpenMP loops above from the next call on (n < 1 leaves
+ * it unchanged); returns the count now in force.  Used to time the oracle on
+ * one core beside all of them; results do not depend on it. */
+int oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
 }

@@ -23,6 +23,7 @@ file.  Function map:
     local_attend() y, lse of local chunked attention (no hashing) [Reformer
                    overview page, "Approach / What changed", "Takeaways"]
     *_rows(...)    the same on a sample of rows (for full-size parity)
+    set_threads()  OpenMP thread count of the calls that follow (timing only)
     candidates()   attended positions of one query (window-rule tests)
 """
 from __future__ import annotations
@@ -72,13 +73,14 @@ def _bind(lib):
     lib.oracle_linear.argtypes = [_I64, _I, _I, _P, _P, _P, _P]
     lib.oracle_local_attend.argtypes = [_I] * 9 + [_P] * 4
     lib.oracle_local_attend_rows.argtypes = [_I] * 9 + [_P, _P, _I64, _P, _P, _P]
+    lib.oracle_set_threads.argtypes = [_I]
     for name in ("oracle_lsh_hash", "oracle_lsh_hash_rows", "oracle_lsh_sort",
                  "oracle_lsh_attend", "oracle_lsh_attend_rows",
                  "oracle_lsh_candidates", "oracle_lsh_combine",
                  "oracle_lsh_combine_rows", "oracle_lsh_forward",
                  "oracle_local_attend", "oracle_local_attend_rows",
                  "oracle_lsh_attend_union", "oracle_lsh_attend_union_rows",
-                 "oracle_linear"):
+                 "oracle_linear", "oracle_set_threads"):
         getattr(lib, name).restype = _I
     return lib
 
@@ -341,3 +343,9 @@ def linear(a, w, bias=None) -> np.ndarray:
     _check(_load().oracle_linear(rows, N, K, _ptr(a), _ptr(w), None if b is None else _ptr(b),
                                  _ptr(out)), "linear")
     return out
+
+
+def set_threads(n: int = 0) -> int:
+    """Use n OpenMP threads from the next call on (n < 1: unchanged); returns
+    the count in force.  Results do not depend on it."""
+    return int(_load().oracle_set_threads(int(n)))
