@@ -42,6 +42,8 @@ __device__ __forceinline__ int clamp_bucket(int k, int nb) {
   return k < 0 ? 0 : (k >= nb ? nb - 1 : k);
 }
 
+constexpr int kCountBatch = 8;
+
 __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ buckets,
                                                         int32_t* __restrict__ cnt, int L, int nb,
                                                         int tile, int ntiles) {
@@ -53,8 +55,16 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
   const int lo = t * tile;
   const int hi = min(L, lo + tile);
   const int32_t* bk = buckets + seg * L;
-  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x)
-    atomicAdd(&hist[clamp_bucket(bk[i], nb)], 1);
+  // eight keys per thread requested before any is counted: the loads are
+  // unconditional (index clamped to the tile) so that they are all in flight
+  for (int i0 = lo; i0 < hi; i0 += 256 * kCountBatch) {
+    int32_t k[kCountBatch];
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) k[u] = bk[min(i0 + 256 * u + (int)threadIdx.x, hi - 1)];
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u)
+      if (i0 + 256 * u + (int)threadIdx.x < hi) atomicAdd(&hist[clamp_bucket(k[u], nb)], 1);
+  }
   __syncthreads();
   int32_t* out = cnt + (seg * ntiles + t) * (int64_t)nb;
   for (int i = threadIdx.x; i < nb; i += blockDim.x) out[i] = hist[i];
@@ -144,15 +154,26 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
   int32_t* ip = inv_perm + seg * L;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  for (int i = lane; i < nb; i += kWave) run[i] = bs[i] + pre[i];
+  // bucket offsets of this tile, sixteen per lane requested at once
+  for (int i0 = 0; i0 < nb; i0 += kWave * 16) {
+    int32_t bv[16], pv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = min(i0 + kWave * u + lane, nb - 1);
+      bv[u] = bs[i];
+      pv[u] = pre[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i0 + kWave * u + lane < nb) run[i0 + kWave * u + lane] = bv[u] + pv[u];
+  }
+  __builtin_amdgcn_wave_barrier();
 
   for (int c0 = lo; c0 < hi; c0 += kWave * kScatterBatches) {
+    // unconditional loads (index clamped to the tile), so all are in flight
     int key[kScatterBatches];
 #pragma unroll
-    for (int b = 0; b < kScatterBatches; ++b) {
-      const int i = c0 + b * kWave + lane;
-      key[b] = i < hi ? clamp_bucket(bk[i], nb) : 0;
-    }
+    for (int b = 0; b < kScatterBatches; ++b) key[b] = bk[min(c0 + b * kWave + lane, hi - 1)];
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int b = 0; b < kScatterBatches; ++b) {
@@ -160,7 +181,7 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
       if (i0 >= hi) break;
       const int i = i0 + lane;
       const bool valid = i < hi;
-      const int k = key[b];
+      const int k = valid ? clamp_bucket(key[b], nb) : 0;
       uint64_t peers = __ballot(valid);
       for (int bit = 0; bit < nbits; ++bit) {
         const bool set = (k >> bit) & 1;
