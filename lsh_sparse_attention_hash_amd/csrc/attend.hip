@@ -485,6 +485,7 @@ size_t union_workspace_bytes(const Shape& s) {
 // that key j is a candidate of query i in round r exactly when the two share
 // the bucket and j's chunk is i's chunk or the one before, i.e. when
 // key_r(i) - key_r(j) is 0 or 1 (C + 1 > C keeps different buckets apart).
+template <int RMAX>
 __global__ __launch_bounds__(256) void union_keys_kernel(const int32_t* __restrict__ buckets,
                                                         const int32_t* __restrict__ inv_perm,
                                                         int32_t* __restrict__ keys, int rounds,
@@ -494,16 +495,24 @@ __global__ __launch_bounds__(256) void union_keys_kernel(const int32_t* __restri
   const int64_t bh = g / L;
   const int pos = (int)(g % L);
   const int span = L / kChunk + 1;
-  int32_t* out = keys + g * stride;
-  for (int r = 0; r < stride; ++r) {
-    int32_t k = -2;   // padding (the query side pads with 2^30: never a match)
-    if (r < rounds) {
-      const int64_t f = (bh * rounds + r) * L + pos;
-      const int b = min(max(buckets[f], 0), nb - 1);
-      k = b * span + clamp_index(inv_perm[f], L) / kChunk;
-    }
-    out[r] = k;
+  // every round's bucket and slot requested at once (rounds past the last
+  // repeat its addresses); padding keys are -2, and the query side pads with
+  // 2^30, so a padded round never matches
+  int32_t bk[RMAX], ip[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const int64_t f = (bh * rounds + (r < rounds ? r : rounds - 1)) * L + pos;
+    bk[r] = buckets[f];
+    ip[r] = inv_perm[f];
   }
+  int32_t k[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    k[r] = r < rounds ? min(max(bk[r], 0), nb - 1) * span + clamp_index(ip[r], L) / kChunk : -2;
+  int32_t* out = keys + g * stride;
+#pragma unroll
+  for (int r = 0; r < RMAX; r += 4)
+    if (r < stride) *reinterpret_cast<int4*>(out + r) = make_int4(k[r], k[r + 1], k[r + 2], k[r + 3]);
 }
 
 template <bool UNION>
@@ -562,9 +571,16 @@ hipError_t launch_attend_union(const Shape& s, const void* qk, const void* v,
                                void* workspace, hipStream_t stream) {
   int32_t* keys = static_cast<int32_t*>(workspace);
   const int64_t total = s.token_heads();
-  hipLaunchKernelGGL(union_keys_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, buckets, inv_perm, keys, s.rounds, union_key_stride(s), s.len,
-                     s.buckets, total);
+  const dim3 kgrid((unsigned)((total + 255) / 256)), kblock(256);
+  if (s.rounds <= 4)
+    hipLaunchKernelGGL(union_keys_kernel<4>, kgrid, kblock, 0, stream, buckets, inv_perm, keys,
+                       s.rounds, union_key_stride(s), s.len, s.buckets, total);
+  else if (s.rounds <= 8)
+    hipLaunchKernelGGL(union_keys_kernel<8>, kgrid, kblock, 0, stream, buckets, inv_perm, keys,
+                       s.rounds, union_key_stride(s), s.len, s.buckets, total);
+  else
+    hipLaunchKernelGGL(union_keys_kernel<kMaxUnionRounds>, kgrid, kblock, 0, stream, buckets,
+                       inv_perm, keys, s.rounds, union_key_stride(s), s.len, s.buckets, total);
   return launch_attend_impl<true>(s, qk, v, buckets, perm, keys, o_rounds, lse, stream);
 }
 

@@ -43,18 +43,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int i = (int)(tok % L);
   const int64_t seg0 = bh * rounds;
 
+  // The loads are unconditional so that they are all in flight at once:
+  // slots past the last round repeat the last round's addresses (ignored).
   int64_t row[RMAX];
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r)
-    if (r < rounds) row[r] = (seg0 + r) * L + clamp_index(inv_perm[(seg0 + r) * L + i], L);
+  for (int r = 0; r < RMAX; ++r) {
+    const int64_t seg = seg0 + (r < rounds ? r : rounds - 1);
+    row[r] = seg * L + clamp_index(inv_perm[seg * L + i], L);
+  }
   float l[RMAX];
   float4 o[RMAX];
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
-    if (r < rounds) {
-      l[r] = lse[row[r]];
-      o[r] = *reinterpret_cast<const float4*>(o_rounds + row[r] * kHeadDim + c4);
-    }
+    l[r] = lse[row[r]];
+    o[r] = *reinterpret_cast<const float4*>(o_rounds + row[r] * kHeadDim + c4);
   }
   float mx = -INFINITY;
 #pragma unroll
