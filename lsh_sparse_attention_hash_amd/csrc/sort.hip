@@ -9,8 +9,9 @@
 //   scan_t   one thread per (segment, bucket): exclusive prefix over tiles
 //   scan_b   one workgroup per segment: exclusive prefix over bucket totals
 //   scatter  one wave per (segment, tile): walks the tile in order, 64 keys
-//            at a time; equal keys inside a batch are ranked with ballots
-//            (match over the key bits), so the scatter is stable.
+//            at a time; equal keys inside a batch are ranked by lane (found
+//            through per-bucket LDS masks, or ballots over the key bits for
+//            B > 2048), so the scatter is stable.
 // Workspace: cnt[S][tiles][B] (counts, then tile prefixes) and base[S][B].
 #include "lsh_device.h"
 #include "lsh_launch.h"
@@ -18,10 +19,13 @@
 namespace lsh {
 
 int sort_tile(const Shape& s) {
-  // tiles of at least max(2048, B) tokens keep the count table no larger
-  // than the keys themselves
-  int t = 2048;
+  // at least max(1024, B) keys per tile keeps the count table no larger than
+  // the keys; large calls double it up to 4096 while they would have more
+  // than 1024 tiles (fewer, longer scatter waves)
+  int t = 1024;
   while (t < s.buckets) t <<= 1;
+  const int64_t keys = s.segments() * (int64_t)s.len;
+  while (t < 4096 && keys / t > 1024) t <<= 1;
   return t;
 }
 
@@ -129,16 +133,25 @@ __global__ __launch_bounds__(1024) void sort_scan_bins_kernel(int32_t* __restric
 
 // One wave per (segment, tile).  The tile's keys are first loaded into
 // registers (kScatterBatches loads in flight per lane), then ranked 64 at a
-// time in position order: lanes holding equal keys are found by intersecting
-// the ballots of every key bit, and each key's slot is its bucket's running
-// offset (LDS) plus its rank among the equal keys of lower lanes.
-constexpr int kScatterBatches = 32;   // tile = 32 batches of 64 keys (2048 keys)
+// time in position order; each key's slot is its bucket's running offset (LDS)
+// plus its rank among the equal keys of lower lanes.  The lanes holding equal
+// keys are found
+//   MASK:  through LDS -- every lane ORs its lane bit into its bucket's 64-bit
+//          mask, reads the mask back (a wave's LDS operations take effect in
+//          order, so the read sees the whole batch), and the group's last lane
+//          advances the bucket's offset and clears the mask (B <= 2048);
+//   else:  by intersecting the ballots of every key bit.
+constexpr int kScatterBatches = 32;   // keys taken 32 batches of 64 at a time
+constexpr int kMaskMatchMaxBuckets = 2048;
 
+template <bool MASK>
 __global__ __launch_bounds__(64) void sort_scatter_kernel(
     const int32_t* __restrict__ buckets, const int32_t* __restrict__ cnt,
     const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int L, int nb, int nbits, int tile, int ntiles) {
-  extern __shared__ int32_t run[];
+  extern __shared__ uint64_t smem[];
+  uint64_t* mask = smem;                                              // [nb] (MASK)
+  int32_t* run = MASK ? reinterpret_cast<int32_t*>(smem + nb) : reinterpret_cast<int32_t*>(smem);
   const int lane = lane_id();
   // each XCD scatters whole segments, so a segment's perm lines fill up in one
   // L2 before they are written back
@@ -152,7 +165,6 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
   const int32_t* bk = buckets + seg * L;
   int32_t* pm = perm + seg * L;
   int32_t* ip = inv_perm + seg * L;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   // bucket offsets of this tile, sixteen per lane requested at once
   for (int i0 = 0; i0 < nb; i0 += kWave * 16) {
@@ -164,8 +176,13 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
       pv[u] = pre[i];
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (i0 + kWave * u + lane < nb) run[i0 + kWave * u + lane] = bv[u] + pv[u];
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + kWave * u + lane;
+      if (i < nb) {
+        run[i] = bv[u] + pv[u];
+        if (MASK) mask[i] = 0;
+      }
+    }
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -182,17 +199,34 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
       const int i = i0 + lane;
       const bool valid = i < hi;
       const int k = valid ? clamp_bucket(key[b], nb) : 0;
-      uint64_t peers = __ballot(valid);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const bool set = (k >> bit) & 1;
-        const uint64_t ones = __ballot(set);
-        peers &= set ? ones : ~ones;
+      uint64_t peers;
+      int32_t start = 0;
+      if (MASK) {
+        if (valid) __hip_atomic_fetch_or(&mask[k], 1ull << lane, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+        __builtin_amdgcn_wave_barrier();
+        peers = 0;
+        if (valid) {
+          peers = __hip_atomic_load(&mask[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          start = run[k];
+        }
+      } else {
+        peers = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+          const bool set = (k >> bit) & 1;
+          const uint64_t ones = __ballot(set);
+          peers &= set ? ones : ~ones;
+        }
+        start = valid ? run[k] : 0;
       }
-      const int rank = __popcll(peers & below);
+      const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
       const int n = __popcll(peers);
-      const int32_t start = valid ? run[k] : 0;
       __builtin_amdgcn_wave_barrier();
-      if (valid && rank == n - 1) run[k] = start + n;
+      if (valid && rank == n - 1) {
+        run[k] = start + n;
+        if (MASK) __hip_atomic_store(&mask[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
       __builtin_amdgcn_wave_barrier();
       if (valid) {
         const int32_t slot = start + rank;
@@ -222,8 +256,13 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
   hipLaunchKernelGGL(sort_scan_tiles_kernel, dim3((unsigned)((nbins + 255) / 256)), dim3(256), 0,
                      stream, cnt, base, nb, ntiles, nbins);
   hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base, nb);
-  hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)(S * ntiles)), dim3(64), lds, stream,
-                     buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
+  if (nb <= kMaskMatchMaxBuckets)
+    hipLaunchKernelGGL(sort_scatter_kernel<true>, dim3((unsigned)(S * ntiles)), dim3(64),
+                       (size_t)nb * (sizeof(uint64_t) + sizeof(int32_t)), stream, buckets, cnt,
+                       base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
+  else
+    hipLaunchKernelGGL(sort_scatter_kernel<false>, dim3((unsigned)(S * ntiles)), dim3(64), lds,
+                       stream, buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
   return hipGetLastError();
 }
 

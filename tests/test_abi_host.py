@@ -105,11 +105,15 @@ def test_workspace_bytes_cover_the_count_tables():
     for L, nb, R in ((1024, 16, 1), (4096, 64, 2), (65536, 1024, 8), (524288, 8192, 2),
                      (2048, 16384, 1)):
         c = cfg(seq_len=L, n_buckets=nb, n_rounds=R, heads=4)
-        tile = 2048
+        S = 4 * R
+        # tiles of max(1024, B) keys, doubled up to 4096 while there would
+        # be more than 1024 of them
+        tile = 1024
         while tile < nb:
             tile *= 2
+        while tile < 4096 and S * L // tile > 1024:
+            tile *= 2
         tiles = -(-L // tile)
-        S = 4 * R
         assert B.lsh_sort_workspace_bytes(c) >= 4 * S * nb * (tiles + 1)
 
 
