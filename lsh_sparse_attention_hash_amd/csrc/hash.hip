@@ -105,13 +105,49 @@ __device__ __forceinline__ void load_dir(uint4 (&r)[8], const uint16_t* rhr, int
 struct SettleLds {
   double wbest[2][kHashWaves];   // per-wave winners, double-buffered by row parity
   int wbesti[2][kHashWaves];
+  float wlow[2][kHashWaves];     // per-wave lower bounds on the best |score|
 };
+
+// fp32 score x.R_j (exact bf16 products, fp32 sums) and an upper bound e_j
+// on its distance from the definition: the fp32 bound 64 * 2^-22 * 1.01 *
+// sum_k |x_k R_kj| of the main loop (the sum itself taken in fp32, with 2^-10
+// of slack), plus flush-to-zero slack.
+__device__ __forceinline__ void score_fp32(const uint4 (&r)[8], const uint32_t (&xw)[kHeadDim / 2],
+                                           float& s, float& ej) {
+  float acc = 0.f, aacc = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xw[4 * c + e]),
+                                            __builtin_bit_cast(bf16x2, w[e]), acc, false);
+      aacc = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2, xw[4 * c + e] & 0x7fff7fffu),
+          __builtin_bit_cast(bf16x2, w[e] & 0x7fff7fffu), aacc, false);
+    }
+  }
+  s = acc;
+  ej = aacc * (64.0f * 0x1p-22f * 1.01f * (1.0f + 0x1p-10f)) + 0x1p-117f;
+}
 
 // Settles list[0..n): entry (r << 8) | t is token tok0 + t of round r, whose
 // x is row t of xsm (bf16, kRowStride apart).  Called by all threads of the
 // workgroup; every listed row is written when it returns.
-__device__ void settle_rows(const uint32_t* list, int n, const uint16_t* xsm, const uint16_t* rot_h,
-                            int32_t* out_bh, int tok0, int L, int half, SettleLds& sl) {
+//
+// Two passes per row.  The first scores every direction in fp32 with its
+// bound e_j, and the workgroup takes the largest lower bound |s_j| - e_j of
+// the best |score|.  Only directions whose upper bound |s_j| + e_j reaches
+// it can hold the maximum of [xR; -xR] or tie with it; the second pass
+// recomputes those in fp64 in the defining order and keeps the first
+// maximum.  Each thread remembers its best upper bound (and direction) and
+// its second best; when the second best also reaches the lower bound (rare)
+// the thread scans its directions again.
+// Inlined: as a called function its register saves would raise the kernel's
+// register count for the main loop as well.
+__device__ __forceinline__ void settle_rows(const uint32_t* list, int n, const uint16_t* xsm,
+                                            const uint16_t* rot_h, int32_t* out_bh, int tok0,
+                                            int L, int half, SettleLds& sl) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int iters = (half + kHashTokWG - 1) / kHashTokWG;
@@ -120,7 +156,7 @@ __device__ void settle_rows(const uint32_t* list, int n, const uint16_t* xsm, co
     const uint32_t ent = list[e];
     const int t = (int)(ent & 255u);
     const uint16_t* rhr = rot_h + (size_t)(ent >> 8) * rot_round;
-    uint32_t xw[kHeadDim / 2];   // x as packed bf16 pairs, widened per use
+    uint32_t xw[kHeadDim / 2];   // x as packed bf16 pairs
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint4 u = *reinterpret_cast<const uint4*>(xsm + t * kRowStride + 8 * c);
@@ -129,20 +165,71 @@ __device__ void settle_rows(const uint32_t* list, int n, const uint16_t* xsm, co
       xw[4 * c + 2] = u.z;
       xw[4 * c + 3] = u.w;
     }
+
+    // pass 1: fp32 scores; the next direction's row is in flight meanwhile
+    float low = -INFINITY, up1 = -INFINITY, up2 = -INFINITY;
+    int j1 = -1;
+    uint4 rv[8];
+    if ((int)threadIdx.x < half) load_dir(rv, rhr, threadIdx.x);
+    for (int it = 0; it < iters; ++it) {
+      const int j = threadIdx.x + it * kHashTokWG;
+      uint4 rn[8];
+      const bool next = j + kHashTokWG < half;
+      if (next) load_dir(rn, rhr, j + kHashTokWG);
+      if (j < half) {
+        float sc, ej;
+        score_fp32(rv, xw, sc, ej);
+        const float up = fabsf(sc) + ej;
+        low = fmaxf(low, fabsf(sc) - ej);
+        if (up > up1) {
+          up2 = up1;
+          up1 = up;
+          j1 = j;
+        } else {
+          up2 = fmaxf(up2, up);
+        }
+      }
+      if (next) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) rv[c] = rn[c];
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) low = fmaxf(low, __shfl_xor(low, off));
+    if (lane == 0) sl.wlow[e & 1][wave] = low;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kHashWaves; ++w) low = fmaxf(low, sl.wlow[e & 1][w]);
+
+    // pass 2: the directions that can reach the maximum, in fp64
     double best = -INFINITY;
     int besti = INT_MAX;
-    for (int it = 0; it < iters; ++it) {
-      // opaque to the compiler, so the widened x is not hoisted out of the
-      // loop (64 doubles would not fit beside the main loop's registers)
+    if (j1 >= 0 && up1 >= low) {
+      // opaque to the compiler, so the widened x is not hoisted (64 doubles
+      // would not fit beside the main loop's registers)
 #pragma unroll
       for (int q = 0; q < kHeadDim / 2; ++q) asm volatile("" : "+v"(xw[q]));
-      const int j = threadIdx.x + it * kHashTokWG;
-      if (j < half) {
-        uint4 rv[8];
-        load_dir(rv, rhr, j);
-        const double s = dot_fp64(rv, xw);
-        settle_take(s, j, best, besti);
-        settle_take(-s, j + half, best, besti);
+      uint4 r1[8];
+      load_dir(r1, rhr, j1);
+      const double sd = dot_fp64(r1, xw);
+      settle_take(sd, j1, best, besti);
+      settle_take(-sd, j1 + half, best, besti);
+    }
+    if (up2 >= low) {
+      for (int it = 0; it < iters; ++it) {
+        const int j = threadIdx.x + it * kHashTokWG;
+        if (j >= half || j == j1) continue;
+        uint4 r2[8];
+        load_dir(r2, rhr, j);
+        float sc, ej;
+        score_fp32(r2, xw, sc, ej);
+        if (fabsf(sc) + ej >= low) {
+#pragma unroll
+          for (int q = 0; q < kHeadDim / 2; ++q) asm volatile("" : "+v"(xw[q]));
+          const double sd = dot_fp64(r2, xw);
+          settle_take(sd, j, best, besti);
+          settle_take(-sd, j + half, best, besti);
+        }
       }
     }
     // larger value wins, lower index on equal values: a total order, so any
