@@ -433,8 +433,13 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
       const bool pos = part + __shfl_xor(part, 32) > 0.f;
       const float lower1 = __uint_as_float(__float_as_uint(w1) & kKeyMask);
       const float upper2 = __uint_as_float((__float_as_uint(w2) & kKeyMask) + 32u);
-      // |fp32 MFMA score - exact| <= 64 * 2^-23 * sum_k |x_k R_kj| <= 64 * 2^-23 |x| |R_j|;
-      // doubled to cover the fp64 rounding of the definition, plus flush-to-zero slack.
+      // |fp32 MFMA score - exact| <= 64 * 2^-23 * sum_k |x_k R_kj| <= 64 * 2^-23 |x| |R_j|
+      // when each of the 64 additions rounds once, by at most one ulp.  The
+      // bound is doubled: the matrix core's internal datapath is not
+      // documented, and one that aligns a block of products to its largest
+      // exponent and truncates can exceed 64 ulps by a few percent.  The 1%
+      // covers the fp64 rounding of the definition; the last terms are
+      // flush-to-zero slack.
       const float E = xnorm[nb] * rcol * (64.0f * 0x1p-22f * 1.01f) +
                       (xnorm[nb] + rcol) * 0x1p-120f + 0x1p-118f;
       const bool cert = (lower1 - upper2 > 2.0f * E + lower1 * 0x1p-20f) && (jstar < (uint32_t)half);
