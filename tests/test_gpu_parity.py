@@ -108,6 +108,14 @@ EDGE = {
                                         "f32", 17),
     "clusters": synth.Workload("clusters", 1, 2, 4096, 64, 64, 2, 64, True, True, "bf16", 18,
                                n_clusters=4),
+    # largest bucket count whose sort ranks equal keys through LDS masks, and
+    # the smallest that uses ballots
+    "mask_match_limit": synth.Workload("b2048", 1, 2, 4096, 64, 2048, 2, 64, True, True, "bf16",
+                                       23),
+    "ballot_match": synth.Workload("b4096", 1, 1, 4096, 64, 4096, 1, 64, False, True, "bf16", 24),
+    # round counts that leave padded slots in the combine's unrolled loads
+    "rounds5": synth.Workload("r5", 1, 2, 64 * 11, 64, 16, 5, 64, True, True, "bf16", 25),
+    "rounds12": synth.Workload("r12", 1, 1, 64 * 6, 64, 8, 12, 64, False, False, "bf16", 26),
 }
 
 

@@ -60,6 +60,8 @@ CASES = {
     "clusters": synth.Workload("u_cl", 1, 4, 4096, 64, 64, 4, 64, True, True, "bf16", 56,
                                n_clusters=8),
     "ragged": synth.Workload("u_rag", 3, 1, 64 * 21, 64, 10, 3, 64, False, False, "bf16", 57),
+    # 5 to 8 rounds: the round-key table's 8-wide variant with padded slots
+    "six_rounds": synth.Workload("u_r6", 1, 2, 2048, 64, 16, 6, 64, True, True, "bf16", 59),
 }
 
 
