@@ -148,24 +148,113 @@ __device__ __forceinline__ void gemm_store_w(uint16_t* ws, const uint4 (&t)[2]) 
   }
 }
 
+// The epilogue of one wave's 64 x 64 block, staged through the wave's own
+// 9,216 bytes of the (by then idle) operand LDS so that every global access
+// is a 16-byte piece of a full output row.  The products are taken as
+// C^T = W A^T, so register r of lane l of block (i, j) holds feature
+// 8*(r/4) + 4*(l/32) + r%4 of token l%32: registers 4q .. 4q+3 are four
+// consecutive features of one token.  bf16 outputs (qk/v, the hidden layer)
+// go through LDS in one pass of 64 rows x 128 B; fp32 outputs with the
+// residual in two passes of 32 rows x 256 B.  The 64 features of a block
+// are one head of qk or v (the block starts at a multiple of 64).
+constexpr int kStageBf16 = 72;    // bf16 per staged row (128 B + 16 B pad)
+constexpr int kStageF32 = 68;     // floats per staged row (256 B + 16 B pad)
+static_assert(64 * kStageBf16 * 2 <= 9216 && 32 * kStageF32 * 4 <= 9216, "stage exceeds 9,216 B");
+static_assert(2 * 9216 <= 2 * kBM * kTS * 2 && 2 * 9216 <= 2 * kBN * kTS * 2, "two stages per array");
+
 template <int EPI>
-__device__ __forceinline__ void gemm_emit(const GemmArgs& g, int m, int n, float acc) {
-  if (m >= g.M || n >= g.N) return;
-  if (EPI == kEpiQkv) {
-    // feature n of qk (n < n0) or v: head n / 64, column n % 64, [b][H][L][64]
-    const int nn = n < g.n0 ? n : n - g.n0;
-    uint16_t* out = static_cast<uint16_t*>(n < g.n0 ? g.out0 : g.out1);
-    const int bi = m / g.L, l = m - bi * g.L;
-    const int64_t at = (((int64_t)bi * g.heads + nn / kHeadDim) * g.L + l) * kHeadDim + nn % kHeadDim;
-    out[at] = __builtin_bit_cast(uint16_t, (__bf16)acc);
-  } else if (EPI == kEpiResidual) {
-    const int64_t at = (int64_t)m * g.N + n;
-    const float v = acc + (g.bias ? g.bias[n] : 0.f);
-    static_cast<float*>(g.out0)[at] = g.resid[at] + g.sign * v;
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const f32x16 (&acc)[2][2], int mb,
+                                              int nb, void* stage_mem) {
+  const int lane = lane_id();
+  if (EPI != kEpiResidual) {
+    uint16_t* st = static_cast<uint16_t*>(stage_mem);
+    float4 bias[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bias[j][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (EPI == kEpiReluBf16 && g.bias)
+          bias[j][q] = *reinterpret_cast<const float4*>(
+              g.bias + min(nb + j * 32 + 8 * q + 4 * (lane >> 5), g.N - 4));
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          if (EPI == kEpiReluBf16) {
+            v[0] = fmaxf(v[0] + bias[j][q].x, 0.f);
+            v[1] = fmaxf(v[1] + bias[j][q].y, 0.f);
+            v[2] = fmaxf(v[2] + bias[j][q].z, 0.f);
+            v[3] = fmaxf(v[3] + bias[j][q].w, 0.f);
+          }
+          const int row = i * 32 + (lane & 31), col = j * 32 + 8 * q + 4 * (lane >> 5);
+          *reinterpret_cast<uint2*>(&st[row * kStageBf16 + col]) =
+              make_uint2(gemm_pack2(v[0], v[1]), gemm_pack2(v[2], v[3]));
+        }
+    __builtin_amdgcn_wave_barrier();
+    // 8 lanes per row, 16 bytes each: 8 rows per pass
+    const int c8 = (lane & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int row = p * 8 + (lane >> 3);
+      const int m = mb + row;
+      const uint4 u = *reinterpret_cast<const uint4*>(&st[row * kStageBf16 + c8]);
+      if (m >= g.M || nb >= g.N) continue;
+      if (EPI == kEpiQkv) {
+        // features nb .. nb+63 of qk (nb < n0) or v: one head, [b][H][L][64]
+        const int f = nb < g.n0 ? nb : nb - g.n0;
+        uint16_t* out = static_cast<uint16_t*>(nb < g.n0 ? g.out0 : g.out1);
+        const int bi = m / g.L, l = m - bi * g.L;
+        store16(out + (((int64_t)bi * g.heads + f / kHeadDim) * g.L + l) * kHeadDim + c8, u);
+      } else {
+        store16(static_cast<uint16_t*>(g.out0) + (int64_t)m * g.N + nb + c8, u);
+      }
+    }
   } else {
-    const int64_t at = (int64_t)m * g.N + n;
-    static_cast<uint16_t*>(g.out0)[at] =
-        __builtin_bit_cast(uint16_t, (__bf16)fmaxf(acc + (g.bias ? g.bias[n] : 0.f), 0.f));
+    if (nb >= g.N) return;   // the block lies past the last feature (N % 128 == 64)
+    float* st = static_cast<float*>(stage_mem);
+    // 16 lanes per row, 16 bytes each: 4 rows per pass; a lane's columns
+    // are the same in every pass
+    const int c4 = (lane & 15) * 4;
+    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (g.bias) b = *reinterpret_cast<const float4*>(g.bias + nb + c4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = lane & 31, col = j * 32 + 8 * q + 4 * (lane >> 5);
+          *reinterpret_cast<float4*>(&st[row * kStageF32 + col]) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+        }
+      __builtin_amdgcn_wave_barrier();
+      float4 rv[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int64_t mc = min(mb + i * 32 + p * 4 + (lane >> 4), g.M - 1);
+        rv[p] = *reinterpret_cast<const float4*>(g.resid + mc * g.N + nb + c4);
+      }
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int row = p * 4 + (lane >> 4);
+        const int m = mb + i * 32 + row;
+        const float4 a = *reinterpret_cast<const float4*>(&st[row * kStageF32 + c4]);
+        if (m >= g.M) continue;
+        const float v0 = a.x + b.x, v1 = a.y + b.y, v2 = a.z + b.z, v3 = a.w + b.w;
+        *reinterpret_cast<float4*>(static_cast<float*>(g.out0) + (int64_t)m * g.N + nb + c4) =
+            make_float4(rv[p].x + g.sign * v0, rv[p].y + g.sign * v1, rv[p].z + g.sign * v2,
+                        rv[p].w + g.sign * v3);
+      }
+    }
   }
 }
 
@@ -224,7 +313,7 @@ __global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(GemmArgs g) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
     }
     if (more) {
       gemm_store_a<AL>(as[(kt + 1) & 1], ta);
@@ -233,17 +322,11 @@ __global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // register r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int n = n_base + wn * 64 + j * 32 + (lane & 31);
-        gemm_emit<EPI>(g, m, n, acc[i][j][r]);
-      }
+  // every wave is past its last operand reads (the loop ends on a barrier):
+  // waves 0-1 stage their outputs in as, waves 2-3 in ws
+  char* stage = wave < 2 ? reinterpret_cast<char*>(&as[0][0]) + wave * 9216
+                         : reinterpret_cast<char*>(&ws[0][0]) + (wave - 2) * 9216;
+  gemm_epilogue<EPI>(g, acc, m0 + wm * 64, n_base + wn * 64, stage);
 }
 
 template <int AL, int EPI>
