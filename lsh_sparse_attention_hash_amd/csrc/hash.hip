@@ -131,6 +131,16 @@ __device__ __forceinline__ void score_fp32(const uint4 (&r)[8], const uint32_t (
   ej = aacc * (64.0f * 0x1p-22f * 1.01f * (1.0f + 0x1p-10f)) + 0x1p-117f;
 }
 
+// Row e's bucket: the first maximum among the four waves' winners.
+__device__ __forceinline__ void settle_pick(const SettleLds& sl, int e, uint32_t ent,
+                                            int32_t* out_bh, int tok0, int L) {
+  double best = sl.wbest[e & 1][0];
+  int besti = sl.wbesti[e & 1][0];
+#pragma unroll
+  for (int w = 1; w < kHashWaves; ++w) settle_take(sl.wbest[e & 1][w], sl.wbesti[e & 1][w], best, besti);
+  out_bh[(size_t)(ent >> 8) * L + tok0 + (int)(ent & 255u)] = besti;
+}
+
 // Settles list[0..n): entry (r << 8) | t is token tok0 + t of round r, whose
 // x is row t of xsm (bf16, kRowStride apart).  Called by all threads of the
 // workgroup; every listed row is written when it returns.
@@ -198,6 +208,7 @@ __device__ __forceinline__ void settle_rows(const uint32_t* list, int n, const u
     for (int off = 1; off < kWave; off <<= 1) low = fmaxf(low, __shfl_xor(low, off));
     if (lane == 0) sl.wlow[e & 1][wave] = low;
     __syncthreads();
+    if (threadIdx.x == 0 && e > 0) settle_pick(sl, e - 1, list[e - 1], out_bh, tok0, L);
 #pragma unroll
     for (int w = 0; w < kHashWaves; ++w) low = fmaxf(low, sl.wlow[e & 1][w]);
 
@@ -244,13 +255,11 @@ __device__ __forceinline__ void settle_rows(const uint32_t* list, int n, const u
       sl.wbest[e & 1][wave] = best;
       sl.wbesti[e & 1][wave] = besti;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int w = 1; w < kHashWaves; ++w) settle_take(sl.wbest[e & 1][w], sl.wbesti[e & 1][w], best, besti);
-      out_bh[(size_t)(ent >> 8) * L + tok0 + t] = besti;
-    }
+    // the four waves' winners of this row are combined after the next row's
+    // first barrier (or the barrier below after the last row)
   }
+  __syncthreads();
+  if (threadIdx.x == 0 && n > 0) settle_pick(sl, n - 1, list[n - 1], out_bh, tok0, L);
 }
 
 // ---------------------------------------------------------------------------
