@@ -96,6 +96,24 @@ def measured_traffic(kernel, workload):
     return None
 
 
+def measured_kernel_traffic(step, workload, kernels):
+    """HBM bytes of a call made of several kernel launches: sum of count x
+    (read + written bytes per launch) over {kernel name: count}, from the
+    per-kernel table of the committed counter summary, if the step's sources
+    are unchanged since it was taken (else None)."""
+    if measured_traffic(step, workload) is None:
+        return None
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    found = {}
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 3 and cells[0] in kernels:
+            found[cells[0]] = (float(cells[1]) + float(cells[2])) * 1e6
+    if set(found) != set(kernels):
+        return None
+    return sum(kernels[k] * found[k] for k in kernels)
+
+
 def cpu_baseline(w, inputs, union=False, small_configs=True):
     """The fp64 oracle on a bounded sample of the workload: every head for the
     shapes up to L = 64K (a few seconds on a many-core host), one head of the
@@ -189,13 +207,18 @@ def bench_layer(args, binding, torch, synth):
         e.record(stream)
         torch.cuda.synchronize()
         per[name] = a.elapsed_time(e) / args.steps
+    if args.copy_calibration:
+        copy_calibration(torch)
     M = b * L
     aw = synth.Workload(w.name, b, H, L, 64, w.n_buckets, w.n_rounds, 64, w.causal, w.self_mask,
                         "bf16", w.seed)
     work = algorithmic(aw)
     work["project_qkv"] = {"flops": 2 * M * 2 * D * D, "bytes": M * D * 4 + 2 * D * D * 2 + 2 * M * D * 2}
     work["project_out"] = {"flops": 2 * M * D * D, "bytes": M * D * 4 * 3 + D * D * 2}
-    work["ffn"] = {"flops": 2 * 2 * M * D * F, "bytes": M * D * 4 * 3 + 2 * D * F * 2}
+    # x and the residual read, the output written (fp32), both weights read,
+    # and the bf16 hidden activation of every chunk written and read back
+    work["ffn"] = {"flops": 2 * 2 * M * D * F,
+                   "bytes": M * D * 4 * 3 + 2 * D * F * 2 + 2 * M * F * 2}
     kernels = {}
     for n, t_ms in per.items():
         t = t_ms * 1e-3
@@ -217,7 +240,17 @@ def bench_layer(args, binding, torch, synth):
         ach = work[dom]["bytes"] / t / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
+    if dom == "ffn":
+        chunks = -(-M // (w.ffn_chunk or M))
+        roof["traffic"] = measured_kernel_traffic(
+            "gemm", w.name, {"lsh::gemm_bf16_kernel<0, 2>": chunks,
+                             "lsh::gemm_bf16_kernel<1, 1>": chunks})
+    elif dom in gemms:
+        k = {"project_qkv": "lsh::gemm_bf16_kernel<0, 0>",
+             "project_out": "lsh::gemm_bf16_kernel<2, 1>"}[dom]
+        roof["traffic"] = measured_kernel_traffic("gemm", w.name, {k: 1})
+    else:
+        roof["traffic"] = measured_traffic(dom, w.name)
     return {
         "metric": "reversible LSH layer fwd tokens/s (qk/v maps, LSH attention, output map, "
                   "chunked FFN) at L=64K; % of roofline",
@@ -552,7 +585,7 @@ def main():
         roof = {"kernel": {"attend": "attend_bf16_kernel", "combine": "combine_kernel"}[dom],
                 "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None if args.union else measured_traffic(dom, w.name)
+    roof["traffic"] = measured_traffic(dom, w.name + ("_union" if args.union else ""))
 
     result = {
         "metric": METRIC if not args.union else
