@@ -4,7 +4,9 @@
 // enter in increasing order and the scatter is stable, the result is the
 // order of the unique key (bucket, original position).
 //
-// Four launches per call:
+// Four launches per call (two for segments of at most 16,384 tokens whose
+// tile histograms fit in LDS: prefix, one workgroup per segment, does the
+// first three):
 //   count    one workgroup per (segment, tile): LDS histogram of the tile
 //   scan_t   one thread per (segment, bucket): exclusive prefix over tiles
 //   scan_b   one workgroup per segment: exclusive prefix over bucket totals
@@ -131,6 +133,73 @@ __global__ __launch_bounds__(1024) void sort_scan_bins_kernel(int32_t* __restric
   }
 }
 
+// One workgroup per segment, for calls whose per-tile histograms fit in LDS:
+// count, tile prefixes and bucket bases in one launch.  Every tile's
+// histogram is built in LDS from the segment's keys (sixteen loads per thread
+// in flight), each thread then walks its bins over the tiles, writing the
+// exclusive prefixes the scatter reads, and a block scan over the bin totals
+// gives the bucket bases.  Same outputs as count + scan_t + scan_b.
+constexpr int kPrefixThreads = 1024;
+constexpr int kPrefixLdsInts = 32768;   // 128 KB of histograms
+constexpr int kPrefixMaxLen = 16384;    // longest segment counted by one workgroup
+
+__global__ __launch_bounds__(kPrefixThreads) void sort_prefix_kernel(
+    const int32_t* __restrict__ buckets, int32_t* __restrict__ cnt, int32_t* __restrict__ base,
+    int L, int nb, int tile, int ntiles) {
+  __shared__ int32_t hist[kPrefixLdsInts];
+  __shared__ int32_t part[kPrefixThreads];
+  const int tid = threadIdx.x;
+  const int64_t seg = blockIdx.x;
+  const int cells = ntiles * nb;
+  for (int i = tid; i < cells; i += kPrefixThreads) hist[i] = 0;
+  __syncthreads();
+  const int32_t* bk = buckets + seg * L;
+  for (int i0 = 0; i0 < L; i0 += kPrefixThreads * 16) {
+    int32_t k[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) k[u] = bk[min(i0 + kPrefixThreads * u + tid, L - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + kPrefixThreads * u + tid;
+      if (i < L) atomicAdd(&hist[(i / tile) * nb + clamp_bucket(k[u], nb)], 1);
+    }
+  }
+  __syncthreads();
+  // bins tid*per .. tid*per+per-1: exclusive prefixes over the tiles
+  const int per = (nb + kPrefixThreads - 1) / kPrefixThreads;
+  int32_t* out = cnt + seg * (int64_t)ntiles * nb;
+  int32_t mine = 0;
+  for (int q = 0; q < per; ++q) {
+    const int b = tid * per + q;
+    if (b >= nb) break;
+    int32_t run = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const int32_t c = hist[t * nb + b];
+      out[(int64_t)t * nb + b] = run;
+      run += c;
+    }
+    hist[b] = run;   // tile 0's counts are no longer needed: bin totals
+    mine += run;
+  }
+  part[tid] = mine;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread sums
+  for (int off = 1; off < kPrefixThreads; off <<= 1) {
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t acc = part[tid] - mine;
+  int32_t* bs = base + seg * nb;
+  for (int q = 0; q < per; ++q) {
+    const int b = tid * per + q;
+    if (b >= nb) break;
+    bs[b] = acc;
+    acc += hist[b];
+  }
+}
+
 // One wave per (segment, tile).  The tile's keys are first loaded into
 // registers (kScatterBatches loads in flight per lane), then ranked 64 at a
 // time in position order; each key's slot is its bucket's running offset (LDS)
@@ -250,12 +319,19 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
   int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cnt_bytes);
   const size_t lds = (size_t)nb * sizeof(int32_t);
 
-  hipLaunchKernelGGL(sort_count_kernel, dim3((unsigned)(S * ntiles)), dim3(256), lds, stream,
-                     buckets, cnt, s.len, nb, tile, ntiles);
-  const int64_t nbins = S * nb;
-  hipLaunchKernelGGL(sort_scan_tiles_kernel, dim3((unsigned)((nbins + 255) / 256)), dim3(256), 0,
-                     stream, cnt, base, nb, ntiles, nbins);
-  hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base, nb);
+  // one workgroup per segment pays off while a segment is short: a long one
+  // is counted faster by a workgroup per tile
+  if ((int64_t)ntiles * nb <= kPrefixLdsInts && s.len <= kPrefixMaxLen) {
+    hipLaunchKernelGGL(sort_prefix_kernel, dim3((unsigned)S), dim3(kPrefixThreads), 0, stream,
+                       buckets, cnt, base, s.len, nb, tile, ntiles);
+  } else {
+    hipLaunchKernelGGL(sort_count_kernel, dim3((unsigned)(S * ntiles)), dim3(256), lds, stream,
+                       buckets, cnt, s.len, nb, tile, ntiles);
+    const int64_t nbins = S * nb;
+    hipLaunchKernelGGL(sort_scan_tiles_kernel, dim3((unsigned)((nbins + 255) / 256)), dim3(256),
+                       0, stream, cnt, base, nb, ntiles, nbins);
+    hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base, nb);
+  }
   if (nb <= kMaskMatchMaxBuckets)
     hipLaunchKernelGGL(sort_scatter_kernel<true>, dim3((unsigned)(S * ntiles)), dim3(64),
                        (size_t)nb * (sizeof(uint64_t) + sizeof(int32_t)), stream, buckets, cnt,
