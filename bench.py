@@ -114,6 +114,26 @@ def measured_kernel_traffic(step, workload, kernels):
     return sum(kernels[k] * found[k] for k in kernels)
 
 
+def measured_busy(step, workload, kernel=None):
+    """Fraction of the matrix cores' cycles busy during a launch, from the
+    committed rocprofv3 counter summary, if it was taken on the step's current
+    sources (else None): the step's kernel with the most matrix-core work, or
+    the named kernel."""
+    from lsh_sparse_attention_hash_amd.rocprof_summary import source_digest
+    path = os.path.join(ROOT, "profiles", f"mfma_busy_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rows = [[c.strip() for c in line.strip().strip("|").split("|")] for line in open(path)
+            if line.startswith("|")]
+    steprow = [r for r in rows if len(r) == 5 and r[0] == step and r[1] == workload]
+    if not steprow or steprow[0][2] != source_digest(step):
+        return None
+    if kernel is None:
+        return float(steprow[0][4])
+    krow = [r for r in rows if len(r) == 8 and r[0] == kernel]
+    return float(krow[0][7]) if krow else None
+
+
 def cpu_baseline(w, inputs, union=False, small_configs=True):
     """The fp64 oracle on a bounded sample of the workload: every head for the
     shapes up to L = 64K (a few seconds on a many-core host), one head of the
@@ -228,6 +248,15 @@ def bench_layer(args, binding, torch, synth):
             kb["algorithmic_flops"] = work[n]["flops"]
             kb["TFLOPs"] = round(work[n]["flops"] / t / 1e12, 2)
         kernels[n] = kb
+    # matrix-core busy fraction per launch, from the committed counter summary
+    busy_of = {"hash": ("hash", None), "attend": ("attend", None),
+               "project_qkv": ("gemm", "lsh::gemm_bf16_kernel<0, 0>"),
+               "project_out": ("gemm", "lsh::gemm_bf16_kernel<2, 1>")}
+    for n, (st, k) in busy_of.items():
+        kernels[n]["mfma_busy"] = measured_busy(st, w.name, k)
+    kernels["ffn"]["mfma_busy"] = {k: measured_busy("gemm", w.name, k)
+                                   for k in ("lsh::gemm_bf16_kernel<0, 2>",
+                                             "lsh::gemm_bf16_kernel<1, 1>")}
     log("[bench] per call ms: " + ", ".join(f"{n} {t:.4f}" for n, t in per.items()))
     gemms = ("project_qkv", "project_out", "ffn")
     dom = max(per, key=lambda n: per[n])
@@ -353,7 +382,8 @@ def bench_local(args, w, inputs, binding, torch):
         "roofline": roof,
         "kernels": {"local_attend": {"ms": round(per, 5), "algorithmic_bytes": work["bytes"],
                                      "GBps": round(ach, 1), "algorithmic_flops": work["flops"],
-                                     "TFLOPs": round(work["flops"] / t / 1e12, 2)}},
+                                     "TFLOPs": round(work["flops"] / t / 1e12, 2),
+                                     "mfma_busy": measured_busy("local", w.name)}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -571,6 +601,7 @@ def main():
         if "flops" in work[n]:
             kb["algorithmic_flops"] = work[n]["flops"]
             kb["TFLOPs"] = round(work[n]["flops"] / t / 1e12, 2)
+            kb["mfma_busy"] = measured_busy(n, w.name + ("_union" if args.union else ""))
         kernels[n] = kb
     # the dominant step by time among the single-launch kernels
     dom = max(("hash", "attend", "combine"), key=lambda n: per[n])

@@ -5,12 +5,19 @@
     python3 -m lsh_sparse_attention_hash_amd.rocprof_summary traffic \
         --fetch <fetch>_counter_collection.csv --write <write>_counter_collection.csv \
         --workload long --command "..."
+    python3 -m lsh_sparse_attention_hash_amd.rocprof_summary busy \
+        --counters <busy>_counter_collection.csv --workload long --command "..."
 
 `traffic` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) by
 what the same counters read for the plain device copies of known size that
 `bench.py --copy-calibration` runs after its timed steps (512 MiB read and
 512 MiB written per copy).  Each row carries a digest of the kernel's source
 files; bench.py reports the traffic only while that digest is current.
+
+`busy` turns one pass of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA,
+SQ_INSTS_VALU and GRBM_GUI_ACTIVE into the matrix cores' busy fraction per
+kernel: busy SIMD-cycles / (SIMDs x cycles of the dispatch), the cycles being
+GRBM_GUI_ACTIVE divided by the number of XCDs it is summed over.
 """
 from __future__ import annotations
 
@@ -35,6 +42,8 @@ STEP_OF = [("lsh::hash", "hash"), ("lsh::sort", "sort"), ("lsh::attend", "attend
            ("lsh::union_keys", "attend"), ("lsh::combine", "combine"), ("lsh::local", "local"),
            ("lsh::gemm", "gemm")]
 COPY_BYTES = 512 << 20
+SIMDS = 256 * 4   # 256 CUs of 4 SIMDs
+XCDS = 8          # GRBM_GUI_ACTIVE is summed over the XCDs
 
 
 def source_digest(step: str) -> str:
@@ -120,6 +129,53 @@ def trace(args):
     print("\n".join(out))
 
 
+def busy(args):
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    for r in csv.DictReader(open(args.counters)):
+        k = _short(r["Kernel_Name"])
+        if _step(k) is None:
+            continue
+        per[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    out = [f"# Matrix-core busy fraction per launch — {args.workload} workload", "",
+           "Commands (one MI355X, repository root):", ""]
+    out += ["    " + c for c in args.command]
+    out += ["", f"busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS} SIMDs x GRBM_GUI_ACTIVE / {XCDS}); "
+            "clock = GRBM_GUI_ACTIVE / {XCDS} / dispatch time (the profiled dispatch, counters "
+            "on; shown for dispatches of 50 us or more). Instruction counts are wave instructions per launch; SQ_INSTS_VALU includes "
+            "the MFMA instructions.".replace("{XCDS}", str(XCDS)), "",
+            "| kernel | launches | dispatch us | clock GHz | MFMA instructions | VALU instructions "
+            "| MFMA busy SIMD-cycles | MFMA busy |", "|---|---|---|---|---|---|---|---|"]
+    steps = {}
+    mean = lambda xs: sum(xs) / len(xs)
+    for k in sorted(per, key=lambda n: (_step(n) or "~", n)):
+        c = per[k]
+        if not all(n in c for n in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                                    "GRBM_GUI_ACTIVE")):
+            continue
+        cyc = mean(c["GRBM_GUI_ACTIVE"]) / XCDS
+        mb = mean(c["SQ_VALU_MFMA_BUSY_CYCLES"])
+        frac = mb / (SIMDS * cyc) if cyc > 0 else 0.0
+        t = mean(dur[k])
+        # a short dispatch's GRBM count is dominated by the counters' own set-up
+        clock = f"{cyc / t / 1e9:.2f}" if t >= 50e-6 else "-"
+        out.append(f"| {k} | {len(c['GRBM_GUI_ACTIVE'])} | {t * 1e6:.1f} | {clock} | "
+                   f"{mean(c['SQ_INSTS_MFMA']):.0f} | {mean(c['SQ_INSTS_VALU']):.0f} | {mb:.0f} | "
+                   f"{frac:.3f} |")
+        st = _step(k)
+        if mb > 0 and (st not in steps or mb > steps[st][1]):
+            steps[st] = (k, mb, frac)
+    out += ["", "Per step (the step's kernel with the most matrix-core work; digest of the step's "
+            "sources):", "", "| step | workload | digest | kernel | MFMA busy |", "|---|---|---|---|---|"]
+    for st in ("hash", "sort", "attend", "combine", "local", "gemm"):
+        if st in steps:
+            k, _, frac = steps[st]
+            out.append(f"| {st} | {args.workload} | {source_digest(st)} | {k} | {frac:.3f} |")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -132,8 +188,12 @@ def main():
     k.add_argument("--stats", required=True)
     k.add_argument("--workload", required=True)
     k.add_argument("--command", action="append", default=[])
+    b = sub.add_parser("busy")
+    b.add_argument("--counters", required=True)
+    b.add_argument("--workload", required=True)
+    b.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
-    {"traffic": traffic, "trace": trace}[args.what](args)
+    {"traffic": traffic, "trace": trace, "busy": busy}[args.what](args)
 
 
 if __name__ == "__main__":

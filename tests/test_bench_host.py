@@ -64,3 +64,14 @@ def test_percentiles():
     assert p["median"] == pytest.approx(50.5)
     assert p["p10"] == pytest.approx(10.9)
     assert p["p90"] == pytest.approx(90.1)
+
+
+def test_matrix_core_busy_is_reported_only_for_the_profiled_sources(monkeypatch):
+    from lsh_sparse_attention_hash_amd import rocprof_summary
+    busy = bench.measured_busy("hash", "long")
+    assert busy is not None and 0.0 < busy < 1.0
+    k = bench.measured_busy("gemm", "layer_long", "lsh::gemm_bf16_kernel<1, 1>")
+    assert k is not None and 0.0 < k < 1.0
+    assert bench.measured_busy("hash", "no_such_workload") is None
+    monkeypatch.setattr(rocprof_summary, "source_digest", lambda step: "000000000000")
+    assert bench.measured_busy("hash", "long") is None
