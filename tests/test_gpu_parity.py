@@ -116,6 +116,11 @@ EDGE = {
     # round counts that leave padded slots in the combine's unrolled loads
     "rounds5": synth.Workload("r5", 1, 2, 64 * 11, 64, 16, 5, 64, True, True, "bf16", 25),
     "rounds12": synth.Workload("r12", 1, 1, 64 * 6, 64, 8, 12, 64, False, False, "bf16", 26),
+    # more rounds than the combine unrolls (the running softmax over rounds);
+    # bf16 causal attention without the self-mask
+    "rounds20": synth.Workload("r20", 1, 2, 64 * 4, 64, 8, 20, 64, True, False, "bf16", 27),
+    "f32_rounds18": synth.Workload("f32r18", 1, 1, 64 * 3, 64, 4, 18, 64, False, True, "f32",
+                                   28),
 }
 
 
