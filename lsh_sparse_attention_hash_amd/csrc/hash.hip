@@ -269,20 +269,32 @@ __device__ __forceinline__ void settle_rows(const uint32_t* list, int n, const u
 // that truncation; the tile of the running maximum is tracked per lane.
 constexpr uint32_t kKeyMask = ~31u;
 
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* rhr, int half, int st,
-                                           uint4 (&buf)[4], bool load) {
-  // 128 rows x 8 chunks of 16 B = 1024 chunks, 4 per thread
+// Raw buffer descriptor word 3 for gfx9 (32-bit data format; no swizzle): a
+// load at a byte offset past the descriptor's size returns zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Stage st of a round: rows [128 st, 128 st + 128) of the rotation, 1024
+// pieces of 16 B, 4 per thread.  The descriptor covers only the stage's rows
+// below `half`, so the pieces of rows past it read as zero.
+__device__ __forceinline__ void stage_load(uint4 (&buf)[4], const uint16_t* rhr, int half,
+                                           int st) {
+  const int rows = min(kStageRows, half - st * kStageRows);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(rhr + (size_t)st * kStageRows * kHeadDim), (short)0,
+      rows * kHeadDim * (int)sizeof(uint16_t), kBufferWord3);
+  // piece c = threadIdx.x + 256 q: row c / 8, 16-byte column c % 8
+  const uint32_t off = (threadIdx.x >> 3) * (kHeadDim * 2) + (threadIdx.x & 7) * 16;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    buf[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rsrc, off + q * 32 * kHeadDim * 2, 0, 0));
+}
+
+__device__ __forceinline__ void stage_store(uint16_t* dst, const uint4 (&buf)[4]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int c = threadIdx.x + 256 * q;
-    const int row = c >> 3, col = (c & 7) * 8;
-    const int j = st * kStageRows + row;
-    if (load) {
-      buf[q] = make_uint4(0, 0, 0, 0);
-      if (j < half) buf[q] = load16(rhr + (size_t)j * kHeadDim + col);
-    } else {
-      store16(&dst[row * kRowStride + col], buf[q]);
-    }
+    store16(&dst[(c >> 3) * kRowStride + (c & 7) * 8], buf[q]);
   }
 }
 
@@ -343,14 +355,14 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
     float gmax = 0.f;
 
     uint4 buf[4];
-    stage_rows(nullptr, rhr, half, 0, buf, true);
+    stage_load(buf, rhr, half, 0);
     __syncthreads();   // previous round's readers of rs[0] are done
-    stage_rows(rs[0], rhr, half, 0, buf, false);
+    stage_store(rs[0], buf);
     __syncthreads();
     for (int st = 0; st < nstages; ++st) {
       const uint16_t* cur = rs[st & 1];
       const bool more = st + 1 < nstages;
-      if (more) stage_rows(nullptr, rhr, half, st + 1, buf, true);   // in flight during compute
+      if (more) stage_load(buf, rhr, half, st + 1);   // in flight during compute
 
 #pragma unroll
       for (int t = 0; t < kStageRows / 32; ++t) {
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
         }
       }
       if (more) {
-        stage_rows(rs[(st + 1) & 1], rhr, half, st + 1, buf, false);
+        stage_store(rs[(st + 1) & 1], buf);
         __syncthreads();
       }
     }
