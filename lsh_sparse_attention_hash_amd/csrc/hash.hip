@@ -375,14 +375,23 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
           a[ks] = as_bf16x8(load16(&cur[(t * 32 + (lane & 31)) * kRowStride + 8 * (lane >> 5) + 16 * ks]));
 
         if ((tile & (kHashWaves - 1)) == wave) {
-          // Gram block R_tile^T R_tile: its largest entry is the largest squared
-          // direction norm of the tile (off-diagonal entries never exceed it).
-          f32x16 g = {};
+          // The two diagonal 16 x 16 blocks of the Gram matrix R_tile^T R_tile:
+          // every direction of the tile lies on one of their diagonals, and an
+          // off-diagonal entry never exceeds the larger of its two diagonal
+          // ones, so their largest entry is the tile's largest squared
+          // direction norm.  Operand of lane l: direction 16 blk + l % 16,
+          // k = 32 kh + 8 (l / 16) .. + 7 (the same fragment on both sides).
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], a[ks], g, 0, 0, 0);
+          for (int blk = 0; blk < 2; ++blk) {
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) gmax = fmaxf(gmax, g[i]);
+            for (int kh = 0; kh < 2; ++kh) {
+              const bf16x8 r = as_bf16x8(load16(
+                  &cur[(t * 32 + blk * 16 + (lane & 15)) * kRowStride + 8 * (lane >> 4) + 32 * kh]));
+              g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r, r, g, 0, 0, 0);
+            }
+            gmax = fmaxf(gmax, fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3])));
+          }
         }
 
 #pragma unroll
