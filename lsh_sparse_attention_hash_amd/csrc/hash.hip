@@ -323,17 +323,29 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
   }
 
   // B operand (x^T, k x token): lane holds x[token = lane%32][k = 8*(lane/32) + 16*ks + 0..7].
+  // All eight pieces are requested before any is used.  The descriptor covers
+  // the wave's tokens below L, so the rows of tokens past L read as zero.
   bf16x8 xf[2][4];
   float xnorm[2];
+  {
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(xbase + (size_t)min(tok_wave, L) * kHeadDim), (short)0,
+        max(0, min(kHashTokWave, L - tok_wave)) * kHeadDim * (int)sizeof(uint16_t), kBufferWord3);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        xf[nb][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                        xr, (uint32_t)((nb * 32 + (lane & 31)) * kHeadDim * 2 + (lane >> 5) * 16 + ks * 32),
+                        0, 0));
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int tok = tok_wave + nb * 32 + (lane & 31);
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (tok < L) u = load16(xbase + (size_t)tok * kHeadDim + 8 * (lane >> 5) + 16 * ks);
-      xf[nb][ks] = as_bf16x8(u);
+      const uint4 u = __builtin_bit_cast(uint4, xf[nb][ks]);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
