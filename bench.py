@@ -45,7 +45,9 @@ def algorithmic(w, union=False):
     N = w.token_rounds
     T = w.batch * w.heads * w.seq_len
     d = w.head_dim
-    el = 2 if w.dtype == "bf16" else 4
+    bf16 = w.dtype == "bf16"
+    el = 2 if bf16 else 4
+    oel = 2 if bf16 else 4   # per-round output rows: fp16 / fp32
     rot = w.heads * w.n_rounds * (w.n_buckets // 2) * d * el
     out = {
         # x read once, rotations read, bucket ids written; contraction flops
@@ -53,10 +55,12 @@ def algorithmic(w, union=False):
         # keys read twice, perm and inv_perm written
         "sort": {"bytes": 16 * N},
         # per token-round: x and v rows gathered (predecessor reused), perm and
-        # bucket id, fp32 output row and lse
-        "attend": {"bytes": N * (2 * d * el + 8 + 4 * d + 4), "flops": N * 4 * 2 * 64 * d},
+        # bucket id, output row (fp16 for bf16 inputs, fp32 for fp32 inputs)
+        # and lse; bf16 inputs: v read once more for the output scale
+        "attend": {"bytes": N * (2 * d * el + 8 + oel * d + 4) + (T * d * el if bf16 else 0),
+                   "flops": N * 4 * 2 * 64 * d},
         # per token-round: o row, lse and inv_perm read; per token-head: y row written
-        "combine": {"bytes": N * (4 * d + 8) + T * 4 * d},
+        "combine": {"bytes": N * (oel * d + 8) + T * 4 * d},
     }
     if union:
         # round-key table: built from buckets and inv_perm (8 B per token-round

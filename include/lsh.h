@@ -132,7 +132,8 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets,
  *   qk, v     [b][H][L][d]        dtype
  *   buckets   [b][H][R][L]        int32, original order (from lsh_hash)
  *   perm      [b][H][R][L]        int32 (from lsh_sort)
- *   o_rounds  [b][H][R][L][d]     fp32 output, SORTED order
+ *   o_rounds  device buffer of lsh_o_rounds_bytes(cfg) bytes (see below):
+ *             the per-round outputs o, SORTED order
  *   lse       [b][H][R][L]        fp32 output, SORTED order
  *
  * For the query i = perm[seg][s] of sorted chunk c = s / m, the window is the
@@ -143,11 +144,27 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets,
  *   o_rounds[seg][s] = sum_j exp(s_ij - lse) v_j  (0 if there is no key)
  * bf16 inputs use bf16 matrix-core products with fp32 accumulation; fp32
  * inputs use fp32 arithmetic.
+ *
+ * Layout of o_rounds (written here, read by lsh_unsort_combine):
+ *   fp32 inputs: o as fp32 [b][H][R][L][d].
+ *   bf16 inputs: a header of 256 fp32 partial maxima of |v| per (b, h)
+ *     ([b][H][256], padded to a multiple of 256 bytes), then o as fp16
+ *     [b][H][R][L][d] holding o * 2^-k (round to nearest even).  With V the
+ *     largest of the (b, h)'s 256 header values and e the smallest integer
+ *     with V < 2^e (e = -126 when V < 2^-126), k = max(e - 15, -100).  Each o
+ *     is a weighted mean of v rows, so every stored |o| * 2^-k stays within
+ *     rounding of 2^15; o is recovered exactly as the fp16 value times 2^k,
+ *     with 11 significant bits (more than bf16's 8).
  */
 lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk,
                             const void* v, const int32_t* buckets,
-                            const int32_t* perm, float* o_rounds, float* lse,
+                            const int32_t* perm, void* o_rounds, float* lse,
                             void* stream);
+
+/* Bytes of the o_rounds buffer of lsh_chunk_attend, lsh_chunk_attend_union
+ * and lsh_unsort_combine for cfg (0 for an empty or unsupported problem).
+ * The caller allocates it; its layout is given above. */
+size_t lsh_o_rounds_bytes(const lsh_config* cfg);
 
 /* Bytes of device workspace lsh_chunk_attend_union needs for cfg (0 for an
  * empty or unsupported problem). */
@@ -175,7 +192,7 @@ size_t lsh_union_workspace_bytes(const lsh_config* cfg);
 lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk,
                                   const void* v, const int32_t* buckets,
                                   const int32_t* perm, const int32_t* inv_perm,
-                                  float* o_rounds, float* lse, void* workspace,
+                                  void* o_rounds, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
 /*
@@ -185,7 +202,8 @@ lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk,
  * neighbourhoods), taken as a multiset: the rounds' softmaxes are merged with
  * weights from their logsumexps.
  *
- *   o_rounds, lse   from lsh_chunk_attend (sorted order)
+ *   o_rounds, lse   from lsh_chunk_attend (sorted order; o_rounds in the
+ *                   layout described there)
  *   inv_perm        [b][H][R][L] int32 (from lsh_sort)
  *   v               [b][H][L][d] dtype
  *   y               [b][H][L][d] fp32 output, original order
@@ -194,7 +212,7 @@ lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk,
  * M = max_r lse_r(i), where o_r(i), lse_r(i) are read at slot inv_perm[r][i].
  * If every lse_r(i) is -inf (self-masked token with no other key), y_i = v_i.
  */
-lsh_status lsh_unsort_combine(const lsh_config* cfg, const float* o_rounds,
+lsh_status lsh_unsort_combine(const lsh_config* cfg, const void* o_rounds,
                               const float* lse, const int32_t* inv_perm,
                               const void* v, float* y, void* stream);
 

@@ -25,7 +25,7 @@ LSH_ERR_HIP = 4
 LSH_F32 = 0
 LSH_BF16 = 1
 
-EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attend",
+EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_o_rounds_bytes", "lsh_chunk_attend",
            "lsh_unsort_combine", "lsh_union_workspace_bytes", "lsh_chunk_attend_union",
            "lsh_local_attend", "lsh_project_qkv", "lsh_project_out", "lsh_ffn_workspace_bytes",
            "lsh_ffn", "lsh_layer_workspace_bytes", "lsh_reversible_forward",
@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsh_sort_workspace_bytes.argtypes = [cfgp]
     lib.lsh_sort_workspace_bytes.restype = SZ
     lib.lsh_sort.argtypes = [cfgp, P, P, P, P, SZ, P]
+    lib.lsh_o_rounds_bytes.argtypes = [cfgp]
+    lib.lsh_o_rounds_bytes.restype = SZ
     lib.lsh_chunk_attend.argtypes = [cfgp, P, P, P, P, P, P, P]
     lib.lsh_unsort_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.lsh_local_attend.argtypes = [cfgp, I32, I32, P, P, P, P, P]
@@ -173,6 +175,19 @@ def lsh_sort(cfg: LshConfig, buckets, perm, inv_perm, workspace, stream=None):
                                      _stream(stream)))
 
 
+def lsh_o_rounds_bytes(cfg: LshConfig) -> int:
+    return int(_lib.lsh_o_rounds_bytes(ctypes.byref(cfg)))
+
+
+def _expect_o_rounds(cfg: LshConfig, t):
+    """o_rounds is an opaque device byte buffer of lsh_o_rounds_bytes(cfg) bytes
+    (fp32 rows for fp32 inputs; a header and fp16 rows for bf16 inputs)."""
+    need = lsh_o_rounds_bytes(cfg)
+    if not (isinstance(t, torch.Tensor) and t.dtype == torch.uint8 and t.is_contiguous()
+            and t.numel() >= need):
+        raise ValueError(f"o_rounds: expected a contiguous uint8 tensor of >= {need} bytes")
+
+
 def lsh_chunk_attend(cfg: LshConfig, qk, v, buckets, perm, o_rounds, lse, stream=None):
     b, H, L, d, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_rounds
     dt = _dtype_of(cfg)
@@ -180,7 +195,7 @@ def lsh_chunk_attend(cfg: LshConfig, qk, v, buckets, perm, o_rounds, lse, stream
     _expect(v, (b, H, L, d), dt, "v")
     _expect(buckets, (b, H, R, L), torch.int32, "buckets")
     _expect(perm, (b, H, R, L), torch.int32, "perm")
-    _expect(o_rounds, (b, H, R, L, d), torch.float32, "o_rounds")
+    _expect_o_rounds(cfg, o_rounds)
     _expect(lse, (b, H, R, L), torch.float32, "lse")
     _check("lsh_chunk_attend",
            _lib.lsh_chunk_attend(ctypes.byref(cfg), _ptr(qk), _ptr(v), _ptr(buckets), _ptr(perm),
@@ -199,7 +214,7 @@ def lsh_chunk_attend_union(cfg: LshConfig, qk, v, buckets, perm, inv_perm, o_rou
     _expect(v, (b, H, L, d), dt, "v")
     for t, n in ((buckets, "buckets"), (perm, "perm"), (inv_perm, "inv_perm")):
         _expect(t, (b, H, R, L), torch.int32, n)
-    _expect(o_rounds, (b, H, R, L, d), torch.float32, "o_rounds")
+    _expect_o_rounds(cfg, o_rounds)
     _expect(lse, (b, H, R, L), torch.float32, "lse")
     _check("lsh_chunk_attend_union",
            _lib.lsh_chunk_attend_union(ctypes.byref(cfg), _ptr(qk), _ptr(v), _ptr(buckets),
@@ -211,7 +226,7 @@ def lsh_chunk_attend_union(cfg: LshConfig, qk, v, buckets, perm, inv_perm, o_rou
 
 def lsh_unsort_combine(cfg: LshConfig, o_rounds, lse, inv_perm, v, y, stream=None):
     b, H, L, d, R = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_rounds
-    _expect(o_rounds, (b, H, R, L, d), torch.float32, "o_rounds")
+    _expect_o_rounds(cfg, o_rounds)
     _expect(lse, (b, H, R, L), torch.float32, "lse")
     _expect(inv_perm, (b, H, R, L), torch.int32, "inv_perm")
     _expect(v, (b, H, L, d), _dtype_of(cfg), "v")
@@ -263,7 +278,9 @@ class Forward:
         self.buckets = torch.empty((b, H, R, L), **i32)
         self.perm = torch.empty((b, H, R, L), **i32)
         self.inv_perm = torch.empty((b, H, R, L), **i32)
-        self.o_rounds = torch.empty((b, H, R, L, d), **f32)
+        # per-round outputs: an opaque buffer in the library's layout
+        self.o_rounds = torch.empty(max(16, lsh_o_rounds_bytes(cfg)), dtype=torch.uint8,
+                                    device=device)
         self.lse = torch.empty((b, H, R, L), **f32)
         self.y = torch.empty((b, H, L, d), **f32)
         nbytes = max(16, lsh_sort_workspace_bytes(cfg))

@@ -175,7 +175,7 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm
 }
 
 lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk, const void* v,
-                            const int32_t* buckets, const int32_t* perm, float* o_rounds,
+                            const int32_t* buckets, const int32_t* perm, void* o_rounds,
                             float* lse, void* stream) {
   lsh::Shape s;
   bool empty = false;
@@ -192,6 +192,13 @@ lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk, const void* v
                   "lsh_chunk_attend");
 }
 
+size_t lsh_o_rounds_bytes(const lsh_config* cfg) {
+  lsh::Shape s;
+  bool empty = false;
+  if (check_config(cfg, &s, &empty) != LSH_OK || empty) return 0;
+  return lsh::o_rounds_bytes(s);
+}
+
 size_t lsh_union_workspace_bytes(const lsh_config* cfg) {
   lsh::Shape s;
   bool empty = false;
@@ -201,7 +208,7 @@ size_t lsh_union_workspace_bytes(const lsh_config* cfg) {
 
 lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk, const void* v,
                                   const int32_t* buckets, const int32_t* perm,
-                                  const int32_t* inv_perm, float* o_rounds, float* lse,
+                                  const int32_t* inv_perm, void* o_rounds, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   lsh::Shape s;
   bool empty = false;
@@ -225,7 +232,7 @@ lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk, const v
                   "lsh_chunk_attend_union");
 }
 
-lsh_status lsh_unsort_combine(const lsh_config* cfg, const float* o_rounds, const float* lse,
+lsh_status lsh_unsort_combine(const lsh_config* cfg, const void* o_rounds, const float* lse,
                               const int32_t* inv_perm, const void* v, float* y, void* stream) {
   lsh::Shape s;
   bool empty = false;

@@ -14,8 +14,12 @@
 // accumulation).  The S^T layout puts one query per lane column, so the
 // P^T fragments of two score tiles are directly the B operand of the PV
 // product (the contraction over keys is permuted consistently in A and B).
-// V is stored transposed in LDS while it is staged.
-// fp32: one workgroup per chunk, four threads per query, fp32 arithmetic.
+// V is stored transposed in LDS while it is staged.  The output rows are
+// written as fp16 of o * 2^-k, one power-of-two scale per (batch, head) taken
+// from the largest |v| (vmax_kernel runs first and leaves partial maxima in
+// the header of the output buffer; the fp32 accumulation is unchanged).
+// fp32: one workgroup per chunk, four threads per query, fp32 arithmetic and
+// fp32 output rows.
 #include <math.h>
 
 #include "lsh_device.h"
@@ -34,7 +38,8 @@ struct AttendArgs {
   const void* v;
   const int32_t* buckets;
   const int32_t* perm;
-  float* o;
+  void* o;               // fp32 rows (fp32 inputs) or fp16 rows (bf16 inputs)
+  const float* vpart;    // bf16 inputs: partial maxima of |v| per (batch, head)
   float* lse;
   int rounds, L, nchunks, cpw, runs_per_seg, causal, self_mask;
   // set union over rounds: per-token round keys bucket * (C + 1) + chunk of
@@ -148,7 +153,8 @@ __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, 
 
 template <bool CAUSAL, bool SELF, bool UNION = false>
 __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArgs& a, int64_t seg,
-                                                  int c, const int32_t* kkey = nullptr) {
+                                                  int c, float oscale,
+                                                  const int32_t* kkey = nullptr) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;          // 16-lane group
@@ -283,15 +289,18 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
     oacc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, oacc[4], 0, 0, 0);
   }
 
+  // the row written as fp16 of o * 2^-k (the power of two oscale folds into
+  // the reciprocal exactly)
   const float sum = oacc[4][0];
-  const float inv = sum > 0.f ? __builtin_amdgcn_rcpf(sum) : 0.f;
+  const float inv = (sum > 0.f ? __builtin_amdgcn_rcpf(sum) : 0.f) * oscale;
   const int64_t slot = (int64_t)c * kChunk + 16 * wave + ql;
-  float* orow = a.o + ((int64_t)seg * a.L + slot) * kHeadDim;
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)seg * a.L + slot) * kHeadDim;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    const float4 val = make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
-                                   oacc[dt][3] * inv);
-    *reinterpret_cast<float4*>(orow + 16 * dt + 4 * g) = val;
+    const half2v lo = {(_Float16)(oacc[dt][0] * inv), (_Float16)(oacc[dt][1] * inv)};
+    const half2v hi = {(_Float16)(oacc[dt][2] * inv), (_Float16)(oacc[dt][3] * inv)};
+    *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
+        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   }
   if (g == 0)
     a.lse[(int64_t)seg * a.L + slot] =
@@ -313,6 +322,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   const int32_t* bk = a.buckets + seg * a.L;
   const int32_t* pm = a.perm + seg * a.L;
   const int32_t* uk = UNION ? a.ukeys + bh * (int64_t)a.L * a.ukey_stride : nullptr;
+  // scale of the (batch, head)'s fp16 output rows: 2^-k
+  const float oscale = pow2f(-o_scale_exponent(head_vmax(a.vpart + bh * kVParts)));
   ChunkRegs g;
   if (c0 > 0) {
     gather_chunk<UNION>(g, load_perm_pair(pm, c0 - 1, a.L), xb, vb, bk, uk, a.ukey_stride);
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
       if (c + 2 < c1) next = load_perm_pair(pm, c + 2, a.L);
     }
     __syncthreads();
-    attend_chunk_bf16<CAUSAL, SELF, UNION>(sm, a, seg, c, kkey);
+    attend_chunk_bf16<CAUSAL, SELF, UNION>(sm, a, seg, c, oscale, kkey);
     __syncthreads();
   }
 }
@@ -465,7 +476,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
     __syncthreads();
   }
   const int64_t slot = (int64_t)c * kChunk + qi;
-  float* orow = a.o + (seg * a.L + slot) * kHeadDim + 16 * part;
+  float* orow = static_cast<float*>(a.o) + (seg * a.L + slot) * kHeadDim + 16 * part;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
   for (int k = 0; k < 16; k += 4)
@@ -515,10 +526,74 @@ __global__ __launch_bounds__(256) void union_keys_kernel(const int32_t* __restri
     if (r < stride) *reinterpret_cast<int4*>(out + r) = make_int4(k[r], k[r + 1], k[r + 2], k[r + 3]);
 }
 
+// ------------------------------------------------------- fp16 output scale
+// Partial maxima of |v| for the scale of the fp16 per-round outputs: part p of
+// (batch, head) bh covers rows [p * per, (p + 1) * per), per = ceil(L /
+// kVParts).  Finite bf16 magnitudes order like their 15-bit patterns, so the
+// maximum is taken on those.  A workgroup takes 256 / TPP consecutive parts,
+// TPP threads each (small parts share a workgroup instead of leaving most of
+// its threads idle); each thread keeps eight 16-byte pieces in flight.
+template <int TPP>
+__global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ v,
+                                                   float* __restrict__ part, int L,
+                                                   int64_t nparts) {
+  constexpr int kWaves = 256 / kWave;
+  __shared__ uint32_t wmax[kWaves];
+  const int64_t gp = (int64_t)blockIdx.x * (256 / TPP) + threadIdx.x / TPP;   // global part
+  const int t = threadIdx.x % TPP;
+  uint32_t m = 0;
+  if (gp < nparts) {
+    const int64_t bh = gp / kVParts;
+    const int p = (int)(gp % kVParts);
+    const int per = (L + kVParts - 1) / kVParts;
+    const int r0 = min(L, p * per), r1 = min(L, r0 + per);
+    const uint4* src = reinterpret_cast<const uint4*>(v + (bh * L + r0) * kHeadDim);
+    const int n = (r1 - r0) * (kHeadDim / 8);   // 16-byte pieces of the part
+    for (int i0 = 0; i0 < n; i0 += TPP * 8) {
+      uint4 u[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) u[q] = src[min(i0 + TPP * q + t, n - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t w[4] = {u[q].x & 0x7fff7fffu, u[q].y & 0x7fff7fffu, u[q].z & 0x7fff7fffu,
+                               u[q].w & 0x7fff7fffu};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0xffffu, w[e] >> 16));
+      }
+    }
+  }
+  // maximum over the part's TPP threads (lanes of one wave, or whole waves)
+#pragma unroll
+  for (int off = 1; off < (TPP < kWave ? TPP : kWave); off <<= 1)
+    m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if (TPP <= kWave) {
+    if (t == 0 && gp < nparts) part[gp] = bf16_to_f32((uint16_t)m);
+  } else {
+    if (lane_id() == 0) wmax[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (t == 0 && gp < nparts) {
+      const int w0 = (threadIdx.x / TPP) * (TPP / kWave);
+      for (int w = 1; w < TPP / kWave; ++w) m = max(m, wmax[w0 + w]);
+      part[gp] = bf16_to_f32((uint16_t)max(m, wmax[w0]));
+    }
+  }
+}
+
+size_t o_header_bytes(const Shape& s) {
+  if (!s.bf16) return 0;
+  const size_t b = (size_t)s.batch * s.heads * kVParts * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
+size_t o_rounds_bytes(const Shape& s) {
+  return o_header_bytes(s) +
+         (size_t)s.segments() * s.len * kHeadDim * (s.bf16 ? sizeof(uint16_t) : sizeof(float));
+}
+
 template <bool UNION>
 static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void* v,
                                      const int32_t* buckets, const int32_t* perm,
-                                     const int32_t* ukeys, float* o_rounds, float* lse,
+                                     const int32_t* ukeys, void* o_rounds, float* lse,
                                      hipStream_t stream) {
   AttendArgs a;
   a.ukeys = ukeys;
@@ -527,7 +602,8 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
   a.v = v;
   a.buckets = buckets;
   a.perm = perm;
-  a.o = o_rounds;
+  a.o = static_cast<char*>(o_rounds) + o_header_bytes(s);
+  a.vpart = static_cast<const float*>(o_rounds);
   a.lse = lse;
   a.rounds = s.rounds;
   a.L = s.len;
@@ -540,6 +616,26 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
     a.runs_per_seg = a.nchunks;
     hipLaunchKernelGGL(attend_f32_kernel, dim3((unsigned)(S * a.nchunks)), dim3(256), 0, stream, a);
     return hipGetLastError();
+  }
+  // the scale of the fp16 rows first: partial maxima of |v| into the header
+  {
+    const int64_t nparts = (int64_t)s.batch * s.heads * kVParts;
+    const int pieces = (s.len + kVParts - 1) / kVParts * (kHeadDim / 8);   // per part
+    const uint16_t* vb = static_cast<const uint16_t*>(v);
+    float* part = static_cast<float*>(o_rounds);
+    // threads per part: about eight pieces each, 32 to 256
+    if (pieces <= 32 * 8)
+      hipLaunchKernelGGL(vmax_kernel<32>, dim3((unsigned)((nparts + 7) / 8)), dim3(256), 0,
+                         stream, vb, part, s.len, nparts);
+    else if (pieces <= 64 * 8)
+      hipLaunchKernelGGL(vmax_kernel<64>, dim3((unsigned)((nparts + 3) / 4)), dim3(256), 0,
+                         stream, vb, part, s.len, nparts);
+    else if (pieces <= 128 * 8)
+      hipLaunchKernelGGL(vmax_kernel<128>, dim3((unsigned)((nparts + 1) / 2)), dim3(256), 0,
+                         stream, vb, part, s.len, nparts);
+    else
+      hipLaunchKernelGGL(vmax_kernel<256>, dim3((unsigned)nparts), dim3(256), 0, stream, vb,
+                         part, s.len, nparts);
   }
   // runs of consecutive chunks per workgroup: long runs re-gather fewer
   // predecessor chunks; keep at least ~2048 workgroups in flight
@@ -561,13 +657,13 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
 }
 
 hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const int32_t* buckets,
-                         const int32_t* perm, float* o_rounds, float* lse, hipStream_t stream) {
+                         const int32_t* perm, void* o_rounds, float* lse, hipStream_t stream) {
   return launch_attend_impl<false>(s, qk, v, buckets, perm, nullptr, o_rounds, lse, stream);
 }
 
 hipError_t launch_attend_union(const Shape& s, const void* qk, const void* v,
                                const int32_t* buckets, const int32_t* perm,
-                               const int32_t* inv_perm, float* o_rounds, float* lse,
+                               const int32_t* inv_perm, void* o_rounds, float* lse,
                                void* workspace, hipStream_t stream) {
   int32_t* keys = static_cast<int32_t*>(workspace);
   const int64_t total = s.token_heads();

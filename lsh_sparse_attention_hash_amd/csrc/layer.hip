@@ -27,8 +27,8 @@ struct Carve {
 struct LayerScratch {
   uint16_t *qk, *v, *hidden;
   int32_t *buckets, *perm, *inv_perm;
-  void* sort_ws;
-  float *o_rounds, *lse, *y_att;
+  void *sort_ws, *o_rounds;
+  float *lse, *y_att;
   size_t bytes;
 };
 
@@ -42,7 +42,7 @@ LayerScratch carve(const LayerShape& ls, const Shape& as, void* base) {
   w.perm = c.take<int32_t>(N * 4);
   w.inv_perm = c.take<int32_t>(N * 4);
   w.sort_ws = c.take<char>(sort_workspace_bytes(as));
-  w.o_rounds = c.take<float>(N * kHeadDim * 4);
+  w.o_rounds = c.take<char>(o_rounds_bytes(as));
   w.lse = c.take<float>(N * 4);
   w.y_att = c.take<float>(T * kHeadDim * 4);
   w.hidden = c.take<uint16_t>(ffn_workspace_bytes(ls));

@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kHeadDim = 64;   // d
 constexpr int kChunk = 64;     // m
@@ -70,6 +71,35 @@ __device__ __forceinline__ int64_t xcd_interleaved_block(int64_t w, int64_t unit
   if (units % kXcds != 0) return w;
   const int64_t x = w % kXcds, k = w / kXcds;
   return (x + kXcds * (k / per)) * per + k % per;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 per-round outputs (bf16 inputs).  Every output row o is a weighted mean
+// of v rows, so |o| <= max |v| of its (batch, head) up to the rounding of the
+// mean.  The rows are stored as fp16 of o * 2^-k, where k = max(e - 15, -100)
+// for the smallest e with max |v| < 2^e: each stored magnitude stays within
+// rounding of 2^15, far below fp16's largest value 65504, and the scale is a
+// power of two, so it adds no rounding of its own.
+constexpr int kVParts = 256;   // partial maxima of |v| per (batch, head)
+
+__device__ __forceinline__ int o_scale_exponent(float vmax) {
+  const int biased = (int)(__float_as_uint(vmax) >> 23);   // vmax >= 0, finite
+  const int e = biased == 0 ? -126 : biased - 126;
+  return max(e - 15, -100);
+}
+
+// 2^k for -126 <= k <= 127.
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(127 + k) << 23); }
+
+// The largest of one (batch, head)'s kVParts partial maxima (16-byte aligned),
+// in every lane of the calling wave.
+__device__ __forceinline__ float head_vmax(const float* part) {
+  static_assert(kVParts == 4 * kWave, "one float4 per lane");
+  const float4 p = *reinterpret_cast<const float4*>(part + 4 * (threadIdx.x & (kWave - 1)));
+  float m = fmaxf(fmaxf(p.x, p.y), fmaxf(p.z, p.w));
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  return m;
 }
 
 }  // namespace lsh

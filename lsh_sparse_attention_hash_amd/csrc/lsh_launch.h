@@ -24,18 +24,26 @@ size_t sort_workspace_bytes(const Shape& s);
 hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, int32_t* inv_perm,
                        void* workspace, hipStream_t stream);
 
+// Per-round outputs.  fp32 inputs: fp32 rows [S][L][64].  bf16 inputs: a
+// header of kVParts partial maxima of |v| per (batch, head) (fp32, padded to
+// 256 bytes), then fp16 rows [S][L][64] holding o * 2^-k, with k the
+// (batch, head)'s scale exponent (o_scale_exponent of the header's maximum;
+// kVParts and the rule are in lsh_device.h).
+size_t o_header_bytes(const Shape& s);
+size_t o_rounds_bytes(const Shape& s);
+
 hipError_t launch_attend(const Shape& s, const void* qk, const void* v, const int32_t* buckets,
-                         const int32_t* perm, float* o_rounds, float* lse, hipStream_t stream);
+                         const int32_t* perm, void* o_rounds, float* lse, hipStream_t stream);
 
 // Set union over rounds: workspace = per-token round keys (see attend.hip).
 int union_key_stride(const Shape& s);
 size_t union_workspace_bytes(const Shape& s);
 hipError_t launch_attend_union(const Shape& s, const void* qk, const void* v,
                                const int32_t* buckets, const int32_t* perm,
-                               const int32_t* inv_perm, float* o_rounds, float* lse,
+                               const int32_t* inv_perm, void* o_rounds, float* lse,
                                void* workspace, hipStream_t stream);
 
-hipError_t launch_combine(const Shape& s, const float* o_rounds, const float* lse,
+hipError_t launch_combine(const Shape& s, const void* o_rounds, const float* lse,
                           const int32_t* inv_perm, const void* v, float* y, hipStream_t stream);
 
 hipError_t launch_local(const Shape& s, int before, int after, const void* qk, const void* v,

@@ -29,9 +29,16 @@ def test_algorithmic_work_of_the_headline_shape():
     a = bench.algorithmic(w)
     assert a["hash"]["flops"] == N * 64 * 1024                     # N.d.B
     assert a["sort"]["bytes"] == 16 * N                            # keys twice, perm, inv_perm
-    assert a["attend"]["bytes"] == 524 * N                         # x, v rows; perm, bucket; o; lse
+    # x, v rows; perm, bucket; fp16 o row; lse -- and v once more for the output scale
+    assert a["attend"]["bytes"] == 396 * N + 128 * T
     assert a["attend"]["flops"] == 32_768 * N                      # 4 x 64 x 2 x 64 per token-round
-    assert a["combine"]["bytes"] == 264 * N + 256 * T              # o row, lse, inv_perm; y row
+    assert a["combine"]["bytes"] == 136 * N + 256 * T              # fp16 o row, lse, inv_perm; y row
+    # fp32 inputs keep fp32 output rows and need no scale pass
+    f = bench.algorithmic(synth.WORKLOADS["tiny"])
+    tw = synth.WORKLOADS["tiny"]
+    Nt, Tt = tw.token_rounds, tw.batch * tw.heads * tw.seq_len
+    assert f["attend"]["bytes"] == (2 * 64 * 4 + 8 + 4 * 64 + 4) * Nt
+    assert f["combine"]["bytes"] == 264 * Nt + 256 * Tt
     # x read once, every rotation read, bucket ids written
     assert a["hash"]["bytes"] == T * 128 + 8 * 8 * 512 * 64 * 2 + 4 * N
 
@@ -39,8 +46,8 @@ def test_algorithmic_work_of_the_headline_shape():
 def test_roofline_time_of_the_headline_shape():
     r = bench.roofline_us(synth.WORKLOADS["long"])
     assert r["hash"] == pytest.approx(274.877906944e9 / 2.5e15 * 1e6, abs=0.01)   # MFMA-bound
-    assert r["attend"] == pytest.approx(524 * 4_194_304 / 8e12 * 1e6, abs=0.01)
-    assert sum(v for k, v in r.items()) == pytest.approx(548.3, abs=0.2)
+    assert r["attend"] == pytest.approx((396 * 4_194_304 + 128 * 524_288) / 8e12 * 1e6, abs=0.01)
+    assert sum(r.values()) == pytest.approx(109.95 + 8.39 + 216.0 + 88.1, abs=0.2)
 
 
 def test_set_union_adds_the_round_key_table():
@@ -66,12 +73,23 @@ def test_percentiles():
     assert p["p90"] == pytest.approx(90.1)
 
 
-def test_matrix_core_busy_is_reported_only_for_the_profiled_sources(monkeypatch):
+def test_matrix_core_busy_is_reported_only_for_the_profiled_sources(monkeypatch, tmp_path):
     from lsh_sparse_attention_hash_amd import rocprof_summary
-    busy = bench.measured_busy("hash", "long")
-    assert busy is not None and 0.0 < busy < 1.0
-    k = bench.measured_busy("gemm", "layer_long", "lsh::gemm_bf16_kernel<1, 1>")
-    assert k is not None and 0.0 < k < 1.0
+    d = rocprof_summary.source_digest("hash")
+    g = rocprof_summary.source_digest("gemm")
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "mfma_busy_w.md").write_text(
+        "| kernel | launches | dispatch us | clock GHz | MFMA instructions | VALU instructions "
+        "| MFMA busy SIMD-cycles | MFMA busy |\n|---|---|---|---|---|---|---|---|\n"
+        "| lsh::hash_bf16_kernel | 13 | 400.0 | 2.07 | 1 | 2 | 3 | 0.352 |\n"
+        "| lsh::gemm_bf16_kernel<1, 1> | 13 | 100.0 | 2.27 | 1 | 2 | 3 | 0.273 |\n\n"
+        "| step | workload | digest | kernel | MFMA busy |\n|---|---|---|---|---|\n"
+        f"| hash | w | {d} | lsh::hash_bf16_kernel | 0.352 |\n"
+        f"| gemm | w | {g} | lsh::gemm_bf16_kernel<1, 1> | 0.273 |\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_busy("hash", "w") == 0.352
+    assert bench.measured_busy("gemm", "w", "lsh::gemm_bf16_kernel<1, 1>") == 0.273
+    assert bench.measured_busy("gemm", "w", "lsh::gemm_bf16_kernel<0, 0>") is None
     assert bench.measured_busy("hash", "no_such_workload") is None
     monkeypatch.setattr(rocprof_summary, "source_digest", lambda step: "000000000000")
-    assert bench.measured_busy("hash", "long") is None
+    assert bench.measured_busy("hash", "w") is None

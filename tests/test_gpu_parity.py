@@ -18,6 +18,7 @@ import pytest
 import torch
 
 from lsh_sparse_attention_hash_amd import synth
+from o_rounds_layout import header, read_o_rounds
 from oracle import oracle
 
 pytestmark = pytest.mark.gpu
@@ -80,10 +81,11 @@ def full_parity(B, w):
     assert np.array_equal(host(f.perm), ref["perm"]), "perm differs"
     assert np.array_equal(host(f.inv_perm), ref["inv_perm"]), "inv_perm differs"
     assert_close_lse(host(f.lse), ref["lse"], tol, "lse")
-    assert_close(host(f.o_rounds), ref["o_rounds"], tol, "o_rounds")
+    o_gpu = read_o_rounds(host(f.o_rounds), w)
+    assert_close(o_gpu, ref["o_rounds"], tol, "o_rounds")
     err = assert_close(host(f.y), ref["y"], tol, "y")
     # the combine step alone, on the GPU's own per-round outputs
-    y2 = oracle.combine(host(f.o_rounds), host(f.lse), host(f.inv_perm), v)
+    y2 = oracle.combine(o_gpu, host(f.lse), host(f.inv_perm), v)
     assert_close(host(f.y), y2, 1e-5, "combine on identical inputs")
     say(f"[parity] {w.name}: y max abs err {err:.3g}, fallback rows {int(host(f.fallback_rows)[0])}")
     return f
@@ -149,6 +151,39 @@ def test_repeat_runs_are_bitwise_identical(B):
         b = run_gpu(B, w, inp)
         for x, t in zip(outs, (b.buckets, b.perm, b.inv_perm, b.o_rounds, b.lse, b.y)):
             assert np.array_equal(x, host(t))
+
+
+def test_per_round_output_scale(B):
+    """bf16 inputs store the per-round outputs as fp16 with one power-of-two
+    scale per (batch, head): the header's partial maxima give max |v| of each
+    (batch, head) exactly, every stored magnitude stays within rounding of
+    2^15, and heads whose v are scaled by 2^40 or 2^-60 (or are all zero) keep
+    the bf16 tolerance relative to that scale."""
+    w = synth.Workload("oscale", 2, 4, 1024, 64, 16, 2, 64, True, True, "bf16", 41)
+    inp = synth.make_inputs(w)
+    v = synth.to_f64(inp["v"], "bf16")
+    shift = np.zeros((w.batch, w.heads))
+    shift[0, 1], shift[1, 2] = 40, -60
+    v = v * 2.0 ** shift[:, :, None, None]
+    v[1, 3] = 0.0
+    inp = dict(inp, v=synth.bf16_bits(v.astype(np.float32)))
+    assert np.array_equal(synth.to_f64(inp["v"], "bf16"), v)   # the scaling was exact
+    f = run_gpu(B, w, inp)
+    raw = host(f.o_rounds)
+    hdr = header(raw, w)
+    assert np.array_equal(hdr.max(axis=2).astype(np.float64), np.abs(v).max(axis=(2, 3)))
+    from o_rounds_layout import header_bytes
+    n = w.batch * w.heads * w.n_rounds * w.seq_len * w.head_dim
+    stored = raw[header_bytes(w): header_bytes(w) + 2 * n].view(np.float16)
+    assert np.abs(stored.astype(np.float64)).max() <= 2.0 ** 15 * (1 + 2.0 ** -10)
+    ref = oracle.forward(synth.to_f64(inp["qk"], "bf16"), v, synth.to_f64(inp["rot"], "bf16"),
+                         w.n_buckets, w.n_rounds, w.chunk_len, w.causal, w.self_mask)
+    assert np.array_equal(host(f.buckets), ref["buckets"])
+    unit = 2.0 ** shift[:, :, None, None]
+    o = read_o_rounds(raw, w).astype(np.float64)
+    assert np.abs((o - ref["o_rounds"]) / unit[:, :, None]).max() <= TOL["bf16"]
+    assert np.abs((host(f.y) - ref["y"]) / unit).max() <= TOL["bf16"]
+    assert not host(f.y)[1, 3].any()
 
 
 @pytest.mark.parametrize("log2_scale", [30, -60])
@@ -229,10 +264,11 @@ def sampled_parity(B, w, n_hash, n_rows, seed):
                                         w.self_mask, rows)
     lse = host(f.lse).ravel()[rows]
     assert_close_lse(lse, lse_ref, tol, "lse")
-    o = host(f.o_rounds).reshape(-1, w.head_dim)[rows]
+    o_all = read_o_rounds(host(f.o_rounds), w)
+    o = o_all.reshape(-1, w.head_dim)[rows]
     err_o = assert_close(o, o_ref, tol, "o_rounds")
     toks = g.integers(0, w.batch * w.heads * w.seq_len, n_rows)
-    y_ref = oracle.combine_rows(host(f.o_rounds), host(f.lse), inv, v, toks)
+    y_ref = oracle.combine_rows(o_all, host(f.lse), inv, v, toks)
     y = host(f.y).reshape(-1, w.head_dim)[toks]
     assert_close(y, y_ref, 1e-5, "combine rows")
     say(f"[parity-full] {w.name}: o err {err_o:.3g}, fallback rows {int(host(f.fallback_rows)[0])}")

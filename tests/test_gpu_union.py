@@ -11,6 +11,7 @@ import pytest
 import torch
 
 from lsh_sparse_attention_hash_amd import synth
+from o_rounds_layout import read_o_rounds
 from oracle import oracle
 
 pytestmark = pytest.mark.gpu
@@ -81,7 +82,7 @@ def test_union_parity(B, name):
     assert np.array_equal(host(f.inv_perm), ref["inv_perm"])
     tol = TOL[w.dtype]
     close(host(f.lse), ref["lse"], tol, "lse")
-    close(host(f.o_rounds), ref["o_rounds"], tol, "o_rounds")
+    close(read_o_rounds(host(f.o_rounds), w), ref["o_rounds"], tol, "o_rounds")
     err = close(host(f.y), ref["y"], tol, "y")
     multi = oracle.forward(qk, v, rot, w.n_buckets, w.n_rounds, w.chunk_len, w.causal,
                            w.self_mask)
@@ -118,8 +119,9 @@ def test_union_long_full_size_sampled(B):
     o_ref, lse_ref = oracle.attend_union_rows(qk, v, bk, pm, ip, w.n_buckets, w.chunk_len,
                                               w.causal, w.self_mask, rows)
     close(host(f.lse).ravel()[rows], lse_ref, 2e-2, "lse")
-    close(host(f.o_rounds).reshape(-1, 64)[rows], o_ref, 2e-2, "o_rounds")
+    o_all = read_o_rounds(host(f.o_rounds), w)
+    close(o_all.reshape(-1, 64)[rows], o_ref, 2e-2, "o_rounds")
     toks = g.integers(0, w.batch * w.heads * w.seq_len, 2000)
-    y_ref = oracle.combine_rows(host(f.o_rounds), host(f.lse), ip, v, toks)
+    y_ref = oracle.combine_rows(o_all, host(f.lse), ip, v, toks)
     assert np.abs(host(f.y).reshape(-1, 64)[toks] - y_ref).max() <= 1e-5
     say("[union-full] long: 2000 sampled rows of o_rounds / lse / y within tolerance")
