@@ -39,7 +39,8 @@ KERNEL_SOURCES = {
 }
 # kernel name prefix (as rocprofv3 prints it) -> step
 STEP_OF = [("lsh::hash", "hash"), ("lsh::sort", "sort"), ("lsh::attend", "attend"),
-           ("lsh::union_keys", "attend"), ("lsh::combine", "combine"), ("lsh::local", "local"),
+           ("lsh::union_keys", "attend"), ("lsh::vmax", "attend"), ("lsh::combine", "combine"),
+           ("lsh::local", "local"),
            ("lsh::gemm", "gemm")]
 COPY_BYTES = 512 << 20
 SIMDS = 256 * 4   # 256 CUs of 4 SIMDs
