@@ -157,13 +157,15 @@ def test_per_round_output_scale(B):
     """bf16 inputs store the per-round outputs as fp16 with one power-of-two
     scale per (batch, head): the header's partial maxima give max |v| of each
     (batch, head) exactly, every stored magnitude stays within rounding of
-    2^15, and heads whose v are scaled by 2^40 or 2^-60 (or are all zero) keep
-    the bf16 tolerance relative to that scale."""
+    2^15, and heads whose v are scaled by 2^40, 2^-60, 2^120 or 2^-100 (or are
+    all zero) keep the bf16 tolerance relative to that scale."""
     w = synth.Workload("oscale", 2, 4, 1024, 64, 16, 2, 64, True, True, "bf16", 41)
     inp = synth.make_inputs(w)
     v = synth.to_f64(inp["v"], "bf16")
     shift = np.zeros((w.batch, w.heads))
-    shift[0, 1], shift[1, 2] = 40, -60
+    # moderate scales, and the ends of the bf16 range: k up to 108 and the
+    # exponent clamp at -100
+    shift[0, 1], shift[1, 2], shift[0, 3], shift[1, 0] = 40, -60, 120, -100
     v = v * 2.0 ** shift[:, :, None, None]
     v[1, 3] = 0.0
     inp = dict(inp, v=synth.bf16_bits(v.astype(np.float32)))
