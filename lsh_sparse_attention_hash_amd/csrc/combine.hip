@@ -28,7 +28,8 @@ __device__ __forceinline__ float4 load_v4<float>(const float* row, int c4) {
   return *reinterpret_cast<const float4*>(row + c4);
 }
 
-// Per-round rows: fp32 for fp32 inputs, fp16 for bf16 inputs.
+// Per-round rows, keyed by the input type T: fp32 rows for fp32 inputs, fp16
+// rows for bf16 inputs (T = uint16_t).
 template <typename T>
 struct ORows;
 template <>
@@ -48,8 +49,8 @@ struct ORows<uint16_t> {
   }
 };
 
-// 2^k of the (batch, head) of token `tok` (1 for fp32 rows); every lane of the
-// wave must call it.
+// 2^k of (batch, head) bh (1 for fp32 rows); every lane of the wave must call
+// it.
 template <typename T>
 __device__ __forceinline__ float o_unscale(const float* vpart, int64_t bh) {
   if (sizeof(T) == sizeof(float)) return 1.0f;
@@ -61,10 +62,8 @@ __device__ __forceinline__ float o_unscale(const float* vpart, int64_t bh) {
 template <typename T, int RMAX>
 __global__ __launch_bounds__(256) void combine_kernel(
     const typename ORows<T>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
-                                                      const float* __restrict__ lse,
-                                                      const int32_t* __restrict__ inv_perm,
-                                                      const T* __restrict__ v, float* __restrict__ y,
-                                                      int rounds, int L, int64_t total) {
+    const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
+    float* __restrict__ y, int rounds, int L, int64_t total) {
   // Last tokens first: the per-round rows written last by the attention step
   // are the likeliest to still sit in the memory-side cache.
   const int64_t tok0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * 16;   // < total
@@ -123,11 +122,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
 template <typename T>
 __global__ __launch_bounds__(256) void combine_many_kernel(
     const typename ORows<T>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
-                                                           const float* __restrict__ lse,
-                                                           const int32_t* __restrict__ inv_perm,
-                                                           const T* __restrict__ v,
-                                                           float* __restrict__ y, int rounds,
-                                                           int L, int64_t total) {
+    const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
+    float* __restrict__ y, int rounds, int L, int64_t total) {
   const int64_t tok0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * 16;
   const float unscale = o_unscale<T>(vpart, tok0 / L);
   const int64_t tok = tok0 + (threadIdx.x >> 4);
