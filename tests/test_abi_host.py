@@ -117,6 +117,22 @@ def test_workspace_bytes_cover_the_count_tables():
         assert B.lsh_sort_workspace_bytes(c) >= 4 * S * nb * (tiles + 1)
 
 
+def test_per_round_buffer_size():
+    """fp32 inputs: fp32 rows; bf16 inputs: 256 fp32 partial maxima per
+    (batch, head), padded to a multiple of 256 bytes, then fp16 rows."""
+    for b, H, L, R, dt in ((1, 8, 65536, 8, B.LSH_BF16), (2, 3, 192, 5, B.LSH_BF16),
+                           (1, 1, 1024, 1, B.LSH_F32), (3, 2, 448, 3, B.LSH_F32)):
+        c = cfg(batch=b, heads=H, seq_len=L, n_rounds=R, dtype=dt)
+        rows = b * H * R * L * 64
+        if dt == B.LSH_BF16:
+            header = -(-(b * H * 256 * 4) // 256) * 256
+            assert B.lsh_o_rounds_bytes(c) == header + 2 * rows
+        else:
+            assert B.lsh_o_rounds_bytes(c) == 4 * rows
+    assert B.lsh_o_rounds_bytes(cfg(seq_len=0)) == 0
+    assert B.lsh_o_rounds_bytes(cfg(head_dim=32)) == 0
+
+
 def test_empty_problems_are_no_ops():
     lib = B.library()
     for kw in (dict(batch=0), dict(heads=0), dict(seq_len=0)):
