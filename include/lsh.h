@@ -153,8 +153,8 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets,
  *     largest of the (b, h)'s 256 header values and e the smallest integer
  *     with V < 2^e (e = -126 when V < 2^-126), k = max(e - 15, -100).  Each o
  *     is a weighted mean of v rows, so every stored |o| * 2^-k stays within
- *     rounding of 2^15; o is recovered exactly as the fp16 value times 2^k,
- *     with 11 significant bits (more than bf16's 8).
+ *     rounding of 2^15.  o is read back as the fp16 value times 2^k: o
+ *     rounded to 11 significant bits (bf16 has 8), with no overflow.
  */
 lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk,
                             const void* v, const int32_t* buckets,
