@@ -82,7 +82,9 @@ __device__ __forceinline__ void gemm_a_rows(GemmARows<AL>& ar, const GemmArgs& g
   }
 }
 
-template <int AL>
+// FULL: every row of the tile exists, so no load needs a guard (and the
+// compiler needs no zero fill or branch per load).
+template <int AL, bool FULL>
 __device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g,
                                             const GemmARows<AL>& ar, int k0) {
   if (AL == kABf16Rows) {
@@ -90,7 +92,8 @@ __device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g,
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int c8 = ((threadIdx.x + 256 * q) & 3) * 8;
-      t.r[q] = ar.off[q] >= 0 ? load16(a + ar.off[q] + k0 + c8) : make_uint4(0, 0, 0, 0);
+      t.r[q] = (FULL || ar.off[q] >= 0) ? load16(a + ar.off[q] + k0 + c8)
+                                         : make_uint4(0, 0, 0, 0);
     }
   } else {
     const float* a = static_cast<const float*>(g.a);
@@ -101,7 +104,8 @@ __device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c4 = ((threadIdx.x + 256 * q) & 7) * 4;
-      t.r[q] = ar.off[q] >= 0 ? load16(a + ar.off[q] + kofs + c4) : make_uint4(0, 0, 0, 0);
+      t.r[q] = (FULL || ar.off[q] >= 0) ? load16(a + ar.off[q] + kofs + c4)
+                                         : make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -126,13 +130,14 @@ __device__ __forceinline__ void gemm_store_a(uint16_t* as, const GemmATile<AL>& 
   }
 }
 
+template <bool FULL>
 __device__ __forceinline__ void gemm_load_w(uint4 (&t)[2], const GemmArgs& g, int n_base, int k0) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int idx = threadIdx.x + 256 * q;
     const int n = n_base + (idx >> 2), c8 = (idx & 3) * 8;
     uint4 u = make_uint4(0, 0, 0, 0);
-    if (n < g.N) {
+    if (FULL || n < g.N) {
       const uint16_t* row = n < g.n0 ? g.w0 + (int64_t)n * g.K : g.w1 + (int64_t)(n - g.n0) * g.K;
       u = load16(row + k0 + c8);
     }
@@ -258,35 +263,21 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const f32x16 (&
   }
 }
 
-// at most 128 VGPRs: four workgroups per CU hide each other's load latency
-template <int AL, int EPI>
-__global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[2][kBM * kTS];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kBN * kTS];
+// The K loop: the next K-tile is requested while the current one is multiplied
+// out of LDS (double-buffered), one barrier per K-tile.
+template <int AL, bool FULL>
+__device__ __forceinline__ void gemm_main_loop(const GemmArgs& g, const GemmARows<AL>& ar,
+                                               int n_base, uint16_t (&as)[2][kBM * kTS],
+                                               uint16_t (&ws)[2][kBN * kTS],
+                                               f32x16 (&acc)[2][2]) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int ntn = (g.N + kBN - 1) / kBN;
-  // each XCD takes a contiguous range of row tiles, so its A rows stay in its L2
-  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int m0 = (int)(blk / ntn) * kBM;
-  const int n_base = (int)(blk % ntn) * kBN;
   const int nkt = g.K / kBK;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  GemmARows<AL> ar;
-  gemm_a_rows<AL>(ar, g, m0);
   GemmATile<AL> ta;
   uint4 tw[2];
-  gemm_load_a<AL>(ta, g, ar, 0);
-  gemm_load_w(tw, g, n_base, 0);
+  gemm_load_a<AL, FULL>(ta, g, ar, 0);
+  gemm_load_w<FULL>(tw, g, n_base, 0);
   gemm_store_a<AL>(as[0], ta);
   gemm_store_w(ws[0], tw);
   __syncthreads();
@@ -294,8 +285,8 @@ __global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(GemmArgs g) {
   for (int kt = 0; kt < nkt; ++kt) {
     const bool more = kt + 1 < nkt;
     if (more) {   // next K-tile in flight during the products
-      gemm_load_a<AL>(ta, g, ar, (kt + 1) * kBK);
-      gemm_load_w(tw, g, n_base, (kt + 1) * kBK);
+      gemm_load_a<AL, FULL>(ta, g, ar, (kt + 1) * kBK);
+      gemm_load_w<FULL>(tw, g, n_base, (kt + 1) * kBK);
     }
     const uint16_t* a_s = as[kt & 1];
     const uint16_t* w_s = ws[kt & 1];
@@ -321,6 +312,36 @@ __global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
+}
+
+// at most 128 VGPRs: four workgroups per CU hide each other's load latency
+template <int AL, int EPI>
+__global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[2][kBM * kTS];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kBN * kTS];
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int ntn = (g.N + kBN - 1) / kBN;
+  // each XCD takes a contiguous range of row tiles, so its A rows stay in its L2
+  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int m0 = (int)(blk / ntn) * kBM;
+  const int n_base = (int)(blk % ntn) * kBN;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  GemmARows<AL> ar;
+  gemm_a_rows<AL>(ar, g, m0);
+  // the usual case: the whole tile lies inside M and N
+  if (m0 + kBM <= g.M && n_base + kBN <= g.N)
+    gemm_main_loop<AL, true>(g, ar, n_base, as, ws, acc);
+  else
+    gemm_main_loop<AL, false>(g, ar, n_base, as, ws, acc);
 
   // every wave is past its last operand reads (the loop ends on a barrier):
   // waves 0-1 stage their outputs in as, waves 2-3 in ws
