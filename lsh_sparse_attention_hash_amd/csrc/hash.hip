@@ -310,13 +310,18 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.y;
-  const size_t bh = (size_t)blockIdx.z * heads + h;
-  const int tok_wave = blockIdx.x * kHashTokWG + wave * kHashTokWave;
+  // each XCD takes a contiguous range of (batch, head, token block): its L2
+  // then holds the rotations of one or two heads instead of all of them
+  const int nblk = (L + kHashTokWG - 1) / kHashTokWG;
+  const int64_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int bx = (int)(lb % nblk);
+  const size_t bh = (size_t)(lb / nblk);
+  const int h = (int)(bh % heads);
+  const int tok_wave = bx * kHashTokWG + wave * kHashTokWave;
   const uint16_t* xbase = qk + bh * (size_t)L * kHeadDim;
   const uint16_t* rot_h = rot + (size_t)h * rounds * half * kHeadDim;
   int32_t* out_bh = buckets + bh * rounds * (size_t)L;
-  const int tok0 = blockIdx.x * kHashTokWG;
+  const int tok0 = bx * kHashTokWG;
   if (threadIdx.x == 0) {
     settle_n = 0;
     settle_over = 0;
@@ -581,8 +586,7 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
                        buckets, s.heads, s.len, half, s.rounds, rows);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((s.len + kHashTokWG - 1) / kHashTokWG), (unsigned)s.heads,
-                  (unsigned)s.batch);
+  const dim3 grid((unsigned)((int64_t)(s.len + kHashTokWG - 1) / kHashTokWG * s.heads * s.batch));
   hipLaunchKernelGGL(hash_bf16_kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
                      fallback_rows, s.heads, s.len, half, s.rounds);
