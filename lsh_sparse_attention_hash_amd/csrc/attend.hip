@@ -14,12 +14,17 @@
 // accumulation).  The S^T layout puts one query per lane column, so the
 // P^T fragments of two score tiles are directly the B operand of the PV
 // product (the contraction over keys is permuted consistently in A and B).
-// V is stored transposed in LDS while it is staged.  The output rows are
+// V is stored transposed in LDS while it is staged.  Each wave skips the
+// 16-key tiles of the window in which none of its queries keeps a key (keys
+// of other buckets, or past every query under causal masking): in a
+// bucket-sorted window most tiles are such, and skipped tiles add only zeros.
+// The output rows are
 // written as fp16 of o * 2^-k, one power-of-two scale per (batch, head) taken
 // from the largest |v| (vmax_kernel runs first and leaves partial maxima in
 // the header of the output buffer; the fp32 accumulation is unchanged).
 // fp32: one workgroup per chunk, four threads per query, fp32 arithmetic and
 // fp32 output rows.
+#include <limits.h>
 #include <math.h>
 
 #include "lsh_device.h"
@@ -183,11 +188,46 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
       if (q >= a.rounds) kq[q] = 1 << 30;
   }
 
+  // Tiles of the window (16 keys each) that hold no key any query of this
+  // wave can keep are skipped: a key whose bucket lies outside the range of
+  // the wave's query buckets, or (causal) whose position is past that of every
+  // query, is masked for all sixteen.  The bounds are those of queries 0 and 15
+  // when they bound all sixteen (bucket-sorted chunks), else they are left open,
+  // so the skip never changes a result.
+  uint32_t live;   // bit t: window keys 16t .. 16t+15 may hold a kept key
+  {
+    const int qb0 = __builtin_amdgcn_readfirstlane(qb);
+    const int qb15 = __builtin_amdgcn_readlane(qb, 15);
+    const bool bsorted = __ballot(qb < qb0 || qb > qb15) == 0;
+    const int blo = bsorted ? qb0 : INT_MIN, bhi = bsorted ? qb15 : INT_MAX;
+    int phi = INT_MAX;
+    if (CAUSAL) {
+      const int qp15 = __builtin_amdgcn_readlane(qp, 15);
+      if (__ballot(qp > qp15) == 0) phi = qp15;
+    }
+    const int rp = 64 * hp + lane, rc = 64 * hq + lane;
+    const int bkp = sm.kbk[rp], bkc = sm.kbk[rc];
+    bool okp = bkp >= blo && bkp <= bhi;
+    bool okc = bkc >= blo && bkc <= bhi;
+    if (CAUSAL) {
+      okp = okp && sm.kpos[rp] <= phi;
+      okc = okc && sm.kpos[rc] <= phi;
+    }
+    const uint64_t mp = first ? 0ull : (uint64_t)__ballot(okp);
+    const uint64_t mc = __ballot(okc);
+    live = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if ((mp >> (16 * t)) & 0xffffull) live |= 1u << t;
+      if ((mc >> (16 * t)) & 0xffffull) live |= 1u << (t + 4);
+    }
+  }
+
   // scores, log2-scaled: s[t][i] is key 16t + 4g + i of the window for query ql
   float s[8][4];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    if (first && t < 4) {
+    if (!((live >> t) & 1u)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[t][i] = -INFINITY;
       continue;
@@ -244,8 +284,9 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 8; ++t)
+    if ((live >> t) & 1u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][i]);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][i]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float msafe = (mx == -INFINITY) ? 0.f : mx;
@@ -254,6 +295,10 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
   uint32_t pw[8][2];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
+    if (!((live >> t) & 1u)) {
+      pw[t][0] = pw[t][1] = 0u;
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
       const bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(s[t][i] - msafe),
@@ -264,7 +309,6 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
 
   // O^T = V^T P^T; a fifth tile of ones yields the row sums of the rounded P,
   // so every output row is a weighted mean with weights adding up to one.
-  const int kfirst = first ? 2 : 0;
   f32x4 oacc[5];
 #pragma unroll
   for (int dt = 0; dt < 5; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -272,7 +316,7 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
                                                             0x3f803f80u));
 #pragma unroll
   for (int k2 = 0; k2 < 4; ++k2) {
-    if (k2 < kfirst) continue;
+    if (!((live >> (2 * k2)) & 3u)) continue;
     // MFMA contraction index 8g + j <-> window key 32*k2 + 16*(j/4) + 4g + j%4
     const bf16x8 pb = __builtin_bit_cast(
         bf16x8, make_uint4(pw[2 * k2][0], pw[2 * k2][1], pw[2 * k2 + 1][0], pw[2 * k2 + 1][1]));
