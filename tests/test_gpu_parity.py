@@ -131,6 +131,47 @@ def test_edge_case_parity(B, name):
     full_parity(B, EDGE[name])
 
 
+
+def _perm_variants(perm, buckets, seed):
+    """Permutations of each segment that are not the (bucket, position) sort:
+    every bucket run reversed, buckets in descending order, and a shuffle."""
+    rng = np.random.default_rng(seed)
+    L = perm.shape[-1]
+    pos = np.arange(L)
+    rev, desc, shuf = (np.empty_like(perm) for _ in range(3))
+    for idx in np.ndindex(perm.shape[:-1]):
+        bk = buckets[idx]
+        rev[idx] = np.lexsort((-pos, bk)).astype(np.int32)
+        desc[idx] = np.lexsort((pos, -bk)).astype(np.int32)
+        shuf[idx] = rng.permutation(L).astype(np.int32)
+    return {"runs_reversed": rev, "buckets_descending": desc, "shuffled": shuf}
+
+
+@pytest.mark.parametrize("name", ["small", "ragged_noncausal", "ragged_self", "clusters",
+                                  "rounds20"])
+def test_attention_of_any_permutation(B, name):
+    """The attention step takes the window of every chunk from the permutation
+    it is given; its tile skipping must not assume that permutation to be the
+    bucket sort (the oracle applies the masks key by key)."""
+    w = EDGE.get(name) or synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    f = run_gpu(B, w, inp)
+    qk_d = B.to_device(inp["qk"], w.dtype)
+    v_d = B.to_device(inp["v"], w.dtype)
+    qk = synth.to_f64(inp["qk"], w.dtype)
+    v = synth.to_f64(inp["v"], w.dtype)
+    buckets = host(f.buckets)
+    tol = TOL[w.dtype]
+    for kind, perm in _perm_variants(host(f.perm), buckets, w.seed).items():
+        say(f"[parity] attention of a {kind} permutation, {w}")
+        f.perm.copy_(torch.from_numpy(perm))
+        f.attend(qk_d, v_d)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attend(qk, v, buckets, perm, w.n_buckets, w.chunk_len, w.causal,
+                                       w.self_mask)
+        assert_close_lse(host(f.lse), lse_ref, tol, f"lse ({kind})")
+        assert_close(read_o_rounds(host(f.o_rounds), w), o_ref, tol, f"o_rounds ({kind})")
+
 def test_empty_problem_is_a_no_op(B):
     w = synth.Workload("empty", 1, 2, 0, 64, 8, 2, 64, True, True, "bf16", 19)
     cfg = B.config_for(w)
