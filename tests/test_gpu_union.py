@@ -125,3 +125,37 @@ def test_union_long_full_size_sampled(B):
     y_ref = oracle.combine_rows(o_all, host(f.lse), ip, v, toks)
     assert np.abs(host(f.y).reshape(-1, 64)[toks] - y_ref).max() <= 1e-5
     say("[union-full] long: 2000 sampled rows of o_rounds / lse / y within tolerance")
+
+
+@pytest.mark.parametrize("name", ["small", "many_repeats", "clusters"])
+def test_union_attention_of_any_permutation(B, name):
+    """The set-union attention of permutations that are not the bucket sort
+    (every bucket run reversed; a shuffle), with inv_perm their inverse,
+    matches the oracle: its tile skipping assumes nothing of the order."""
+    w = CASES[name]
+    inp = synth.make_inputs(w)
+    f = run_union(B, w, inp)
+    qk_d, v_d = B.to_device(inp["qk"], w.dtype), B.to_device(inp["v"], w.dtype)
+    qk, v = synth.to_f64(inp["qk"], w.dtype), synth.to_f64(inp["v"], w.dtype)
+    buckets = host(f.buckets)
+    L = buckets.shape[-1]
+    pos = np.arange(L)
+    rng = np.random.default_rng(w.seed)
+    tol = TOL[w.dtype]
+    for kind in ("runs_reversed", "shuffled"):
+        perm = np.empty_like(buckets)
+        for idx in np.ndindex(buckets.shape[:-1]):
+            perm[idx] = (np.lexsort((-pos, buckets[idx])) if kind == "runs_reversed"
+                         else rng.permutation(L))
+        inv = np.empty_like(perm)
+        np.put_along_axis(inv, perm.astype(np.int64),
+                          np.broadcast_to(pos.astype(np.int32), perm.shape), axis=-1)
+        say(f"[union] attention of a {kind} permutation, {w}")
+        f.perm.copy_(torch.from_numpy(perm))
+        f.inv_perm.copy_(torch.from_numpy(inv))
+        f.attend_union(qk_d, v_d)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attend_union(qk, v, buckets, perm, inv, w.n_buckets, w.chunk_len,
+                                             w.causal, w.self_mask)
+        close(host(f.lse), lse_ref, tol, f"lse ({kind})")
+        close(read_o_rounds(host(f.o_rounds), w), o_ref, tol, f"o_rounds ({kind})")
