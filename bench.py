@@ -41,13 +41,15 @@ def log(msg):
 
 
 def algorithmic(w, union=False):
-    """Algorithmic work per launch of each kernel (bytes or flops)."""
+    """Algorithmic work per launch of each kernel (bytes or flops), for the
+    per-round output format the workload uses (fp32 rows, or fp16 rows with a
+    per-head scale taken from one extra pass over v)."""
     N = w.token_rounds
     T = w.batch * w.heads * w.seq_len
     d = w.head_dim
     bf16 = w.dtype == "bf16"
     el = 2 if bf16 else 4
-    oel = 2 if bf16 else 4   # per-round output rows: fp16 / fp32
+    oel = 2 if w.o16 else 4   # per-round output rows: fp16 / fp32
     rot = w.heads * w.n_rounds * (w.n_buckets // 2) * d * el
     out = {
         # x read once, rotations read, bucket ids written; contraction flops
@@ -55,9 +57,9 @@ def algorithmic(w, union=False):
         # keys read twice, perm and inv_perm written
         "sort": {"bytes": 16 * N},
         # per token-round: x and v rows gathered (predecessor reused), perm and
-        # bucket id, output row (fp16 for bf16 inputs, fp32 for fp32 inputs)
-        # and lse; bf16 inputs: v read once more for the output scale
-        "attend": {"bytes": N * (2 * d * el + 8 + oel * d + 4) + (T * d * el if bf16 else 0),
+        # bucket id, output row and lse; fp16 rows: v read once more for the
+        # output scale
+        "attend": {"bytes": N * (2 * d * el + 8 + oel * d + 4) + (T * d * el if w.o16 else 0),
                    "flops": N * 4 * 2 * 64 * d},
         # per token-round: o row, lse and inv_perm read; per token-head: y row written
         "combine": {"bytes": N * (oel * d + 8) + T * 4 * d},
@@ -68,6 +70,41 @@ def algorithmic(w, union=False):
         stride = (w.n_rounds + 3) // 4 * 4
         out["attend"]["bytes"] += 8 * N + 4 * stride * T + 4 * stride * N
     return out
+
+
+def survey_bytes(w):
+    """The fixed per-step byte counts every build is compared on (bf16 or fp32
+    inputs, fp32 per-round rows, predecessor chunk reused): hash T*2d + 4N
+    (bf16), sort 16 N, attention 524 N (780 N for fp32 inputs), combine
+    264 N + 256 T."""
+    N = w.token_rounds
+    T = w.batch * w.heads * w.seq_len
+    el = 2 if w.dtype == "bf16" else 4
+    return {"hash": T * w.head_dim * el + 4 * N, "sort": 16 * N,
+            "attend": N * (2 * w.head_dim * el + 8 + 4 * w.head_dim + 4),
+            "combine": N * (4 * w.head_dim + 8) + T * 4 * w.head_dim}
+
+
+def north_star(w, per, union=False):
+    """The two target branches at this shape: the chunk attention's flops
+    against the dense bf16 matrix-core peak (target 0.40), and the bytes of
+    sort + attention + combine against HBM peak (target 0.60), the bytes
+    counted as this layout moves them and as the fixed counts above."""
+    work = algorithmic(w, union)
+    fixed = survey_bytes(w)
+    t_att = per["attend"] * 1e-3
+    t_path = sum(per[n] for n in ("sort", "attend", "combine")) * 1e-3
+    mine = sum(work[n]["bytes"] for n in ("sort", "attend", "combine"))
+    theirs = sum(fixed[n] for n in ("sort", "attend", "combine"))
+    mfma = work["attend"]["flops"] / t_att / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    hbm = mine / t_path / (HBM_PEAK_GBS * 1e9)
+    hbm_fixed = theirs / t_path / (HBM_PEAK_GBS * 1e9)
+    return {"attend_mfma_frac": round(mfma, 4), "attend_mfma_target": 0.40,
+            "path": "sort + attend + combine", "path_us": round(t_path * 1e6, 2),
+            "path_bytes": mine, "path_hbm_frac": round(hbm, 4),
+            "path_bytes_fixed_counts": theirs, "path_hbm_frac_fixed_counts": round(hbm_fixed, 4),
+            "path_hbm_target": 0.60,
+            "met": bool(mfma >= 0.40 or hbm >= 0.60)}
 
 
 def algorithmic_local(w):
@@ -561,6 +598,9 @@ def main():
                     help="time the headline config only (skip tiny/small/medium/verylong)")
     ap.add_argument("--union", action="store_true",
                     help="set reading of the union over rounds (lsh_chunk_attend_union)")
+    ap.add_argument("--o-format", default="auto", choices=("auto", "f32", "f16_scaled"),
+                    help="per-round output rows between attention and combine (auto: scaled "
+                         "fp16 for bf16 inputs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run plain device copies of known size "
                          "(reference for HBM counter scaling)")
@@ -574,7 +614,8 @@ def main():
     import numpy as np  # noqa: F401
     import torch
     from lsh_sparse_attention_hash_amd import build as lib_build
-    if not os.path.exists(lib_build.LIB):
+    if not lib_build.is_current():
+        log("[bench] liblsh.so is missing or stale: rebuilding")
         lib_build.build()
     from lsh_sparse_attention_hash_amd import binding, synth
 
@@ -585,6 +626,8 @@ def main():
         print(json.dumps(bench_layer(args, binding, torch, synth)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
+    if not w.is_local:
+        w = w.replace(o_format=args.o_format)
     log(f"[bench] workload {w}")
     inputs = synth.make_inputs(w)
     if w.is_local:
@@ -597,11 +640,15 @@ def main():
         copy_calibration(torch)
 
     work = algorithmic(w, args.union)
+    fixed = survey_bytes(w)
     kernels = {}
     for n in names:
         t = per[n] * 1e-3
         kb = {"ms": round(per[n], 5), "median_ms": round(tm["kernel_pct"][n]["median"], 5),
-              "algorithmic_bytes": work[n]["bytes"], "GBps": round(work[n]["bytes"] / t / 1e9, 1)}
+              "algorithmic_bytes": work[n]["bytes"], "GBps": round(work[n]["bytes"] / t / 1e9, 1),
+              "hbm_frac": round(work[n]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+              "fixed_count_bytes": fixed[n],
+              "hbm_frac_fixed_counts": round(fixed[n] / t / 1e9 / HBM_PEAK_GBS, 4)}
         if "flops" in work[n]:
             kb["algorithmic_flops"] = work[n]["flops"]
             kb["TFLOPs"] = round(work[n]["flops"] / t / 1e12, 2)
@@ -640,16 +687,28 @@ def main():
                    "heads": w.heads, "seq_len": w.seq_len,
                    "head_dim": w.head_dim, "n_buckets": w.n_buckets, "n_rounds": w.n_rounds,
                    "chunk_len": w.chunk_len, "causal": w.causal, "self_mask": w.self_mask,
+                   "o_format": "f16_scaled" if w.o16 else "f32",
                    "qk": ("gaussian mixture, %d clusters" % w.n_clusters) if w.n_clusters
                    else "N(0,1)"},
         "step_ms": tm["step_pct"],
         **forward_summary(w, tm, args.union),
         "roofline": roof,
+        "north_star": north_star(w, per, args.union),
         "kernels": kernels,
         "hash_fallback_rows_per_step": tm["fallback_rows"],
         "cpu_baseline": None,
     }
     if not args.union and not args.no_other_configs:
+        if w.dtype == "bf16":
+            # the same shape with the other per-round output format
+            wa = w.replace(o_format="f32" if w.o16 else "f16_scaled")
+            ta = time_forward(args, wa, inputs, binding, torch)
+            result["other_o_format"] = {
+                "o_format": "f16_scaled" if wa.o16 else "f32",
+                "ms_per_step": round(ta["ms"], 5), "step_ms": ta["step_pct"],
+                "value": round(w.batch * w.seq_len / (ta["ms"] * 1e-3), 1),
+                "kernels_ms": {n: round(x, 5) for n, x in ta["per"].items()},
+                "north_star": north_star(wa, ta["per"])}
         result["other_configs"] = other_configs(args, w, binding, torch, synth)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

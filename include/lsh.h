@@ -56,6 +56,14 @@ typedef enum {
 
 typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype;
 
+/* Storage of the per-round outputs o between lsh_chunk_attend and
+ * lsh_unsort_combine (the layouts are given at lsh_chunk_attend). */
+typedef enum {
+  LSH_O_F32 = 0,        /* fp32 rows, for either input dtype (the default) */
+  LSH_O_F16_SCALED = 1  /* bf16 inputs only: fp16 rows with one power-of-two
+                           scale per (batch, head), half the bytes */
+} lsh_o_format;
+
 typedef struct {
   int32_t batch;     /* b */
   int32_t heads;     /* H */
@@ -68,6 +76,8 @@ typedef struct {
   int32_t self_mask; /* 1: a token is never its own key; if no round leaves it
                         any key, its output is its own value */
   int32_t dtype;     /* lsh_dtype of qk, v and rot */
+  int32_t o_format;  /* lsh_o_format of the per-round outputs (0 = fp32 rows);
+                        LSH_O_F16_SCALED with fp32 inputs is LSH_ERR_UNSUPPORTED */
 } lsh_config;
 
 /*
@@ -145,15 +155,16 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets,
  * bf16 inputs use bf16 matrix-core products with fp32 accumulation; fp32
  * inputs use fp32 arithmetic.
  *
- * Layout of o_rounds (written here, read by lsh_unsort_combine):
- *   fp32 inputs: o as fp32 [b][H][R][L][d].
- *   bf16 inputs: a header of 256 fp32 partial maxima of |v| per (b, h)
- *     ([b][H][256], padded to a multiple of 256 bytes), then o as fp16
- *     [b][H][R][L][d] holding o * 2^-k (round to nearest even).  With V the
- *     largest of the (b, h)'s 256 header values and e the smallest integer
- *     with V < 2^e (e = -126 when V < 2^-126), k = max(e - 15, -100).  Each o
- *     is a weighted mean of v rows, so every stored |o| * 2^-k stays within
- *     rounding of 2^15.  o is read back as the fp16 value times 2^k: o
+ * Layout of o_rounds (written here, read by lsh_unsort_combine), chosen by
+ * cfg->o_format:
+ *   LSH_O_F32: o as fp32 [b][H][R][L][d] (bf16 or fp32 inputs).
+ *   LSH_O_F16_SCALED (bf16 inputs): a header of 256 fp32 partial maxima of
+ *     |v| per (b, h) ([b][H][256], padded to a multiple of 256 bytes), then o
+ *     as fp16 [b][H][R][L][d] holding o * 2^-k (round to nearest even).  With
+ *     V the largest of the (b, h)'s 256 header values and e the smallest
+ *     integer with V < 2^e (e = -126 when V < 2^-126), k = max(e - 15, -100).
+ *     Each o is a weighted mean of v rows, so every stored |o| * 2^-k stays
+ *     within rounding of 2^15.  o is read back as the fp16 value times 2^k: o
  *     rounded to 11 significant bits (bf16 has 8), with no overflow.
  */
 lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk,
@@ -163,7 +174,7 @@ lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk,
 
 /* Bytes of the o_rounds buffer of lsh_chunk_attend, lsh_chunk_attend_union
  * and lsh_unsort_combine for cfg (0 for an empty or unsupported problem).
- * The caller allocates it; its layout is given above. */
+ * The caller allocates it; its layout (by cfg->o_format) is given above. */
 size_t lsh_o_rounds_bytes(const lsh_config* cfg);
 
 /* Bytes of device workspace lsh_chunk_attend_union needs for cfg (0 for an

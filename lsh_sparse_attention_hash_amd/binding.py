@@ -15,7 +15,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblsh.so")
+# LSH_LIBRARY may name another build of the same library (the sanitizer
+# tests load a host-side AddressSanitizer build through it)
+LIB_PATH = os.environ.get("LSH_LIBRARY") or os.path.join(_PKG, "liblsh.so")
 
 LSH_OK = 0
 LSH_ERR_INVALID_ARGUMENT = 1
@@ -24,6 +26,8 @@ LSH_ERR_WORKSPACE_TOO_SMALL = 3
 LSH_ERR_HIP = 4
 LSH_F32 = 0
 LSH_BF16 = 1
+LSH_O_F32 = 0
+LSH_O_F16_SCALED = 1
 
 EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_o_rounds_bytes", "lsh_chunk_attend",
            "lsh_unsort_combine", "lsh_union_workspace_bytes", "lsh_chunk_attend_union",
@@ -41,7 +45,7 @@ class LshError(RuntimeError):
 class LshConfig(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "heads", "seq_len", "head_dim", "n_buckets", "n_rounds", "chunk_len",
-        "causal", "self_mask", "dtype")]
+        "causal", "self_mask", "dtype", "o_format")]
 
 
 class LshLayerConfig(ctypes.Structure):
@@ -106,16 +110,18 @@ def library() -> ctypes.CDLL:
 
 
 def make_config(batch, heads, seq_len, n_buckets, n_rounds, causal, self_mask, dtype,
-                head_dim=64, chunk_len=64) -> LshConfig:
+                head_dim=64, chunk_len=64, o_format=LSH_O_F32) -> LshConfig:
     dt = {"bf16": LSH_BF16, "f32": LSH_F32}.get(dtype, dtype)
+    of = {"f32": LSH_O_F32, "f16_scaled": LSH_O_F16_SCALED}.get(o_format, o_format)
     return LshConfig(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len,
-                     int(bool(causal)), int(bool(self_mask)), dt)
+                     int(bool(causal)), int(bool(self_mask)), dt, of)
 
 
 def config_for(w) -> LshConfig:
-    """LshConfig of a synth.Workload."""
+    """LshConfig of a synth.Workload (per-round output format from w.o16)."""
     return make_config(w.batch, w.heads, w.seq_len, w.n_buckets, w.n_rounds, w.causal,
-                       w.self_mask, w.dtype, w.head_dim, w.chunk_len)
+                       w.self_mask, w.dtype, w.head_dim, w.chunk_len,
+                       LSH_O_F16_SCALED if w.o16 else LSH_O_F32)
 
 
 def _ptr(t):
@@ -181,7 +187,7 @@ def lsh_o_rounds_bytes(cfg: LshConfig) -> int:
 
 def _expect_o_rounds(cfg: LshConfig, t):
     """o_rounds is an opaque device byte buffer of lsh_o_rounds_bytes(cfg) bytes
-    (fp32 rows for fp32 inputs; a header and fp16 rows for bf16 inputs)."""
+    (fp32 rows, or a header and fp16 rows for LSH_O_F16_SCALED)."""
     need = lsh_o_rounds_bytes(cfg)
     if not (isinstance(t, torch.Tensor) and t.dtype == torch.uint8 and t.is_contiguous()
             and t.numel() >= need):
@@ -333,7 +339,7 @@ def make_layer_config(w) -> LshLayerConfig:
 def attention_config(lc: LshLayerConfig) -> LshConfig:
     """The LshConfig of the layer's attention (bf16, d_model / 64 heads)."""
     return make_config(lc.batch, lc.d_model // 64, lc.seq_len, lc.n_buckets, lc.n_rounds,
-                       lc.causal, lc.self_mask, "bf16")
+                       lc.causal, lc.self_mask, "bf16", o_format=LSH_O_F16_SCALED)
 
 
 def _layer_shapes(lc):

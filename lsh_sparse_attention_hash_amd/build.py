@@ -8,6 +8,7 @@ linked into lsh_sparse_attention_hash_amd/liblsh.so.
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
 import os
 import shutil
 import subprocess
@@ -27,6 +28,31 @@ HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
             "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC]
+
+
+DIGEST = LIB + ".digest"
+HEADERS = ["lsh_device.h", "lsh_launch.h"]
+
+
+def source_digest() -> str:
+    """Digest of everything the library is built from: the kernel and host
+    sources, the internal headers, include/lsh.h and the compiler flags."""
+    h = hashlib.sha256(" ".join(HIPFLAGS).encode())
+    paths = [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(INCLUDE, "lsh.h")]
+    for path in paths:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def is_current() -> bool:
+    """liblsh.so exists and was built from the sources now in the tree."""
+    try:
+        with open(DIGEST) as f:
+            return os.path.exists(LIB) and f.read().strip() == source_digest()
+    except OSError:
+        return False
 
 
 def hipcc() -> str:
@@ -50,6 +76,7 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
+    digest = source_digest()
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
@@ -59,8 +86,10 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(DIGEST, "w") as f:
+        f.write(digest + "\n")
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} (sources {digest})")
     return LIB
 
 

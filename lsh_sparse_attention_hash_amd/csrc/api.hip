@@ -40,6 +40,11 @@ lsh_status check_config(const lsh_config* cfg, lsh::Shape* s, bool* empty) {
     return fail(LSH_ERR_INVALID_ARGUMENT, "n_rounds %d outside [1, 1024]", c.n_rounds);
   if ((c.causal != 0 && c.causal != 1) || (c.self_mask != 0 && c.self_mask != 1))
     return fail(LSH_ERR_INVALID_ARGUMENT, "causal and self_mask must be 0 or 1");
+  if (c.o_format != LSH_O_F32 && c.o_format != LSH_O_F16_SCALED)
+    return fail(LSH_ERR_INVALID_ARGUMENT, "o_format %d is not LSH_O_F32 or LSH_O_F16_SCALED",
+                c.o_format);
+  if (c.o_format == LSH_O_F16_SCALED && c.dtype != LSH_BF16)
+    return fail(LSH_ERR_UNSUPPORTED, "LSH_O_F16_SCALED needs bf16 inputs");
   if (c.head_dim != lsh::kHeadDim)
     return fail(LSH_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", c.head_dim);
   if (c.chunk_len != lsh::kChunk)
@@ -63,6 +68,7 @@ lsh_status check_config(const lsh_config* cfg, lsh::Shape* s, bool* empty) {
   s->causal = c.causal;
   s->self_mask = c.self_mask;
   s->bf16 = c.dtype == LSH_BF16;
+  s->o16 = c.o_format == LSH_O_F16_SCALED;
   return LSH_OK;
 }
 
@@ -116,6 +122,7 @@ lsh_status check_layer(const lsh_layer_config* cfg, lsh::LayerShape* ls, lsh::Sh
   a.causal = c.causal;
   a.self_mask = c.self_mask;
   a.dtype = LSH_BF16;
+  a.o_format = LSH_O_F16_SCALED;   // the layer's own intermediate, half the bytes
   LSH_TRY(check_config(&a, as, empty));
   const long long rows = (long long)c.batch * c.seq_len;
   if (rows * (c.d_model > c.d_ff ? c.d_model : c.d_ff) >= (1LL << 40))

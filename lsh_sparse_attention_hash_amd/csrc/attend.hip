@@ -19,13 +19,16 @@
 // of other buckets, or past every query under causal masking): in a
 // bucket-sorted window most tiles are such, and skipped tiles add only zeros.
 // The output rows are
-// written as fp16 of o * 2^-k, one power-of-two scale per (batch, head) taken
-// from the largest |v| (vmax_kernel runs first and leaves partial maxima in
-// the header of the output buffer; the fp32 accumulation is unchanged).
+// written as fp32, or (compact format) as fp16 of o * 2^-k with one
+// power-of-two scale per (batch, head) taken from the largest |v|
+// (vmax_kernel runs first and leaves partial maxima in the header of the
+// output buffer; the fp32 accumulation is unchanged).
 // fp32: one workgroup per chunk, four threads per query, fp32 arithmetic and
 // fp32 output rows.
 #include <limits.h>
 #include <math.h>
+
+#include <algorithm>
 
 #include "lsh_device.h"
 #include "lsh_launch.h"
@@ -43,10 +46,11 @@ struct AttendArgs {
   const void* v;
   const int32_t* buckets;
   const int32_t* perm;
-  void* o;               // fp32 rows (fp32 inputs) or fp16 rows (bf16 inputs)
-  const float* vpart;    // bf16 inputs: partial maxima of |v| per (batch, head)
+  void* o;               // fp32 rows, or fp16 rows (compact format)
+  const float* vpart;    // compact format: partial maxima of |v| per (batch, head)
   float* lse;
   int rounds, L, nchunks, cpw, runs_per_seg, causal, self_mask;
+  int64_t blk0;          // fp32 kernel: first block of this launch piece
   // set union over rounds: per-token round keys bucket * (C + 1) + chunk of
   // the token's sorted slot, [b][H][L][ukey_stride] (see union_keys_kernel)
   const int32_t* ukeys;
@@ -156,7 +160,7 @@ __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, 
   }
 }
 
-template <bool CAUSAL, bool SELF, bool UNION = false>
+template <bool CAUSAL, bool SELF, bool UNION, bool O16>
 __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArgs& a, int64_t seg,
                                                   int c, float oscale,
                                                   const int32_t* kkey = nullptr) {
@@ -333,25 +337,33 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
     oacc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, oacc[4], 0, 0, 0);
   }
 
-  // the row written as fp16 of o * 2^-k (the power of two oscale folds into
-  // the reciprocal exactly)
+  // the row written as fp32, or as fp16 of o * 2^-k (the power of two oscale
+  // folds into the reciprocal exactly)
   const float sum = oacc[4][0];
   const float inv = (sum > 0.f ? __builtin_amdgcn_rcpf(sum) : 0.f) * oscale;
   const int64_t slot = (int64_t)c * kChunk + 16 * wave + ql;
-  uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)seg * a.L + slot) * kHeadDim;
+  if (O16) {
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + ((int64_t)seg * a.L + slot) * kHeadDim;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const half2v lo = {(_Float16)(oacc[dt][0] * inv), (_Float16)(oacc[dt][1] * inv)};
-    const half2v hi = {(_Float16)(oacc[dt][2] * inv), (_Float16)(oacc[dt][3] * inv)};
-    *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
-        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    for (int dt = 0; dt < 4; ++dt) {
+      const half2v lo = {(_Float16)(oacc[dt][0] * inv), (_Float16)(oacc[dt][1] * inv)};
+      const half2v hi = {(_Float16)(oacc[dt][2] * inv), (_Float16)(oacc[dt][3] * inv)};
+      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
+  } else {
+    float* orow = static_cast<float*>(a.o) + ((int64_t)seg * a.L + slot) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<float4*>(orow + 16 * dt + 4 * g) =
+          make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
   }
   if (g == 0)
     a.lse[(int64_t)seg * a.L + slot] =
         (mx == -INFINITY) ? -INFINITY : (mx + __builtin_amdgcn_logf(sum)) * kLn2;
 }
 
-template <bool CAUSAL, bool SELF, bool UNION = false>
+template <bool CAUSAL, bool SELF, bool UNION, bool O16>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) AttendLds sm;
   __shared__ __attribute__((aligned(16))) int32_t kkey[UNION ? 128 * kMaxUnionRounds : 4];
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   const int32_t* pm = a.perm + seg * a.L;
   const int32_t* uk = UNION ? a.ukeys + bh * (int64_t)a.L * a.ukey_stride : nullptr;
   // scale of the (batch, head)'s fp16 output rows: 2^-k
-  const float oscale = pow2f(-o_scale_exponent(head_vmax(a.vpart + bh * kVParts)));
+  const float oscale = O16 ? pow2f(-o_scale_exponent(head_vmax(a.vpart + bh * kVParts))) : 1.0f;
   ChunkRegs g;
   if (c0 > 0) {
     gather_chunk<UNION>(g, load_perm_pair(pm, c0 - 1, a.L), xb, vb, bk, uk, a.ukey_stride);
@@ -383,7 +395,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
       if (c + 2 < c1) next = load_perm_pair(pm, c + 2, a.L);
     }
     __syncthreads();
-    attend_chunk_bf16<CAUSAL, SELF, UNION>(sm, a, seg, c, oscale, kkey);
+    attend_chunk_bf16<CAUSAL, SELF, UNION, O16>(sm, a, seg, c, oscale, kkey);
     __syncthreads();
   }
 }
@@ -418,8 +430,9 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
   const int t = threadIdx.x;
   const int qi = t >> 2;      // query of the chunk (scores, outputs)
   const int part = t & 3;     // key residue (scores) / feature block (outputs)
-  const int64_t seg = blockIdx.x / a.nchunks;
-  const int c = blockIdx.x % a.nchunks;
+  const int64_t blk = a.blk0 + blockIdx.x;
+  const int64_t seg = blk / a.nchunks;
+  const int c = (int)(blk % a.nchunks);
   const int64_t bh = seg / a.rounds;
   const float* xb = static_cast<const float*>(a.qk) + bh * (int64_t)a.L * kHeadDim;
   const float* vb = static_cast<const float*>(a.v) + bh * (int64_t)a.L * kHeadDim;
@@ -624,14 +637,27 @@ __global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ 
 }
 
 size_t o_header_bytes(const Shape& s) {
-  if (!s.bf16) return 0;
+  if (!s.o16) return 0;
   const size_t b = (size_t)s.batch * s.heads * kVParts * sizeof(float);
   return (b + 255) & ~(size_t)255;
 }
 
 size_t o_rounds_bytes(const Shape& s) {
   return o_header_bytes(s) +
-         (size_t)s.segments() * s.len * kHeadDim * (s.bf16 ? sizeof(uint16_t) : sizeof(float));
+         (size_t)s.segments() * s.len * kHeadDim * (s.o16 ? sizeof(uint16_t) : sizeof(float));
+}
+
+template <bool UNION, bool O16>
+static void launch_attend_masks(const AttendArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  if (a.causal && a.self_mask)
+    hipLaunchKernelGGL((attend_bf16_kernel<true, true, UNION, O16>), grid, block, 0, stream, a);
+  else if (a.causal)
+    hipLaunchKernelGGL((attend_bf16_kernel<true, false, UNION, O16>), grid, block, 0, stream, a);
+  else if (a.self_mask)
+    hipLaunchKernelGGL((attend_bf16_kernel<false, true, UNION, O16>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attend_bf16_kernel<false, false, UNION, O16>), grid, block, 0, stream, a);
 }
 
 template <bool UNION>
@@ -655,14 +681,20 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
   a.causal = s.causal;
   a.self_mask = s.self_mask;
   const int64_t S = s.segments();
+  a.blk0 = 0;
   if (!s.bf16) {
     a.cpw = 1;
     a.runs_per_seg = a.nchunks;
-    hipLaunchKernelGGL(attend_f32_kernel, dim3((unsigned)(S * a.nchunks)), dim3(256), 0, stream, a);
+    const int64_t nblk = S * a.nchunks;
+    for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks) {
+      a.blk0 = b0;
+      hipLaunchKernelGGL(attend_f32_kernel, dim3((unsigned)std::min(kMaxBlocks, nblk - b0)),
+                         dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
   }
   // the scale of the fp16 rows first: partial maxima of |v| into the header
-  {
+  if (s.o16) {
     const int64_t nparts = (int64_t)s.batch * s.heads * kVParts;
     const int pieces = (s.len + kVParts - 1) / kVParts * (kHeadDim / 8);   // per part
     const uint16_t* vb = static_cast<const uint16_t*>(v);
@@ -688,15 +720,11 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
   cpw = cpw < 1 ? 1 : (cpw > 16 ? 16 : cpw);
   a.cpw = cpw;
   a.runs_per_seg = (a.nchunks + cpw - 1) / cpw;
-  const dim3 grid((unsigned)(S * a.runs_per_seg)), block(256);
-  if (a.causal && a.self_mask)
-    hipLaunchKernelGGL((attend_bf16_kernel<true, true, UNION>), grid, block, 0, stream, a);
-  else if (a.causal)
-    hipLaunchKernelGGL((attend_bf16_kernel<true, false, UNION>), grid, block, 0, stream, a);
-  else if (a.self_mask)
-    hipLaunchKernelGGL((attend_bf16_kernel<false, true, UNION>), grid, block, 0, stream, a);
+  const dim3 grid((unsigned)(S * a.runs_per_seg));
+  if (s.o16)
+    launch_attend_masks<UNION, true>(a, grid, stream);
   else
-    hipLaunchKernelGGL((attend_bf16_kernel<false, false, UNION>), grid, block, 0, stream, a);
+    launch_attend_masks<UNION, false>(a, grid, stream);
   return hipGetLastError();
 }
 

@@ -6,10 +6,13 @@
 // 16 lanes per token (4 features of the 64-wide row each); a 256-thread
 // workgroup covers 16 consecutive tokens of one (batch, head), so y is written
 // with full 256-byte rows while the per-round rows are gathered through
-// inv_perm.  bf16 inputs: the per-round rows are fp16 of o * 2^-k with one k
-// per (batch, head), recovered from the partial maxima of |v| in the header of
-// the per-round buffer; 2^k is applied once, with the normalisation.
+// inv_perm.  The per-round rows are fp32, or (compact format, bf16 inputs)
+// fp16 of o * 2^-k with one k per (batch, head), recovered from the partial
+// maxima of |v| in the header of the per-round buffer; 2^k is applied once,
+// with the normalisation.
 #include <math.h>
+
+#include <algorithm>
 
 #include "lsh_device.h"
 #include "lsh_launch.h"
@@ -28,19 +31,18 @@ __device__ __forceinline__ float4 load_v4<float>(const float* row, int c4) {
   return *reinterpret_cast<const float4*>(row + c4);
 }
 
-// Per-round rows, keyed by the input type T: fp32 rows for fp32 inputs, fp16
-// rows for bf16 inputs (T = uint16_t).
-template <typename T>
+// Per-round rows: fp32, or fp16 in the compact format (O16).
+template <bool O16>
 struct ORows;
 template <>
-struct ORows<float> {
+struct ORows<false> {
   typedef float elem;
   __device__ static float4 load4(const float* row, int c4) {
     return *reinterpret_cast<const float4*>(row + c4);
   }
 };
 template <>
-struct ORows<uint16_t> {
+struct ORows<true> {
   typedef uint16_t elem;
   __device__ static float4 load4(const uint16_t* row, int c4) {
     const uint2 u = *reinterpret_cast<const uint2*>(row + c4);
@@ -51,24 +53,24 @@ struct ORows<uint16_t> {
 
 // 2^k of (batch, head) bh (1 for fp32 rows); every lane of the wave must call
 // it.
-template <typename T>
+template <bool O16>
 __device__ __forceinline__ float o_unscale(const float* vpart, int64_t bh) {
-  if (sizeof(T) == sizeof(float)) return 1.0f;
+  if (!O16) return 1.0f;
   return pow2f(o_scale_exponent(head_vmax(vpart + bh * kVParts)));
 }
 
 // RMAX >= rounds: every round's slot, lse and output row are requested before
 // any is used, so a token's R row gathers are in flight together.
-template <typename T, int RMAX>
+template <typename T, bool O16, int RMAX>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const typename ORows<T>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
+    const typename ORows<O16>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
     const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
-    float* __restrict__ y, int rounds, int L, int64_t total) {
+    float* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
   // Last tokens first: the per-round rows written last by the attention step
   // are the likeliest to still sit in the memory-side cache.
-  const int64_t tok0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * 16;   // < total
+  const int64_t tok0 = (blk0 + gridDim.x - 1 - blockIdx.x) * 16;   // < total
   // the workgroup's 16 tokens lie in one (batch, head) (L is a multiple of 64)
-  const float unscale = o_unscale<T>(vpart, tok0 / L);
+  const float unscale = o_unscale<O16>(vpart, tok0 / L);
   const int64_t tok = tok0 + (threadIdx.x >> 4);
   if (tok >= total) return;
   const int c4 = (threadIdx.x & 15) * 4;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
     l[r] = lse[row[r]];
-    o[r] = ORows<T>::load4(o_rounds + row[r] * kHeadDim, c4);
+    o[r] = ORows<O16>::load4(o_rounds + row[r] * kHeadDim, c4);
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -119,13 +121,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }
 
 // Any number of rounds: a running softmax over the rounds, one round at a time.
-template <typename T>
+template <typename T, bool O16>
 __global__ __launch_bounds__(256) void combine_many_kernel(
-    const typename ORows<T>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
+    const typename ORows<O16>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
     const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
-    float* __restrict__ y, int rounds, int L, int64_t total) {
-  const int64_t tok0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * 16;
-  const float unscale = o_unscale<T>(vpart, tok0 / L);
+    float* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
+  const int64_t tok0 = (blk0 + gridDim.x - 1 - blockIdx.x) * 16;
+  const float unscale = o_unscale<O16>(vpart, tok0 / L);
   const int64_t tok = tok0 + (threadIdx.x >> 4);
   if (tok >= total) return;
   const int c4 = (threadIdx.x & 15) * 4;
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(256) void combine_many_kernel(
       const int64_t seg = seg0 + r;
       const int64_t row = seg * L + clamp_index(inv_perm[seg * L + i], L);
       const float w = expf(lse[row] - mx);
-      const float4 o = ORows<T>::load4(o_rounds + row * kHeadDim, c4);
+      const float4 o = ORows<O16>::load4(o_rounds + row * kHeadDim, c4);
       ws += w;
       acc.x = fmaf(w, o.x, acc.x);
       acc.y = fmaf(w, o.y, acc.y);
@@ -160,38 +162,48 @@ __global__ __launch_bounds__(256) void combine_many_kernel(
   *reinterpret_cast<float4*>(y + tok * kHeadDim + c4) = out;
 }
 
-template <typename T>
+template <typename T, bool O16>
 static void launch_combine_t(const Shape& s, const void* o_buf, const float* lse,
                              const int32_t* inv_perm, const T* v, float* y, hipStream_t stream) {
   const float* vpart = static_cast<const float*>(o_buf);
-  const auto* o_rounds = reinterpret_cast<const typename ORows<T>::elem*>(
+  const auto* o_rounds = reinterpret_cast<const typename ORows<O16>::elem*>(
       static_cast<const char*>(o_buf) + o_header_bytes(s));
   const int64_t total = s.token_heads();
-  const dim3 grid((unsigned)((total + 15) / 16)), block(256);
+  const int64_t nblk = (total + 15) / 16;
+  // pieces of at most kMaxBlocks workgroups, the last piece first (its
+  // workgroups also run last-first)
+  for (int64_t b0 = (nblk - 1) / kMaxBlocks * kMaxBlocks; b0 >= 0; b0 -= kMaxBlocks) {
+    const dim3 grid((unsigned)std::min(kMaxBlocks, nblk - b0)), block(256);
 #define LSH_COMBINE(K)                                                                       \
   hipLaunchKernelGGL(K, grid, block, 0, stream, o_rounds, vpart, lse, inv_perm, v, y, s.rounds, \
-                     s.len, total)
+                     s.len, total, b0)
   if (s.rounds <= 1)
-    LSH_COMBINE((combine_kernel<T, 1>));
+    LSH_COMBINE((combine_kernel<T, O16, 1>));
   else if (s.rounds <= 2)
-    LSH_COMBINE((combine_kernel<T, 2>));
+    LSH_COMBINE((combine_kernel<T, O16, 2>));
   else if (s.rounds <= 4)
-    LSH_COMBINE((combine_kernel<T, 4>));
+    LSH_COMBINE((combine_kernel<T, O16, 4>));
   else if (s.rounds <= 8)
-    LSH_COMBINE((combine_kernel<T, 8>));
+    LSH_COMBINE((combine_kernel<T, O16, 8>));
   else if (s.rounds <= 16)
-    LSH_COMBINE((combine_kernel<T, 16>));
+    LSH_COMBINE((combine_kernel<T, O16, 16>));
   else
-    LSH_COMBINE(combine_many_kernel<T>);
+    LSH_COMBINE((combine_many_kernel<T, O16>));
 #undef LSH_COMBINE
+  }
 }
 
 hipError_t launch_combine(const Shape& s, const void* o_rounds, const float* lse,
                           const int32_t* inv_perm, const void* v, float* y, hipStream_t stream) {
-  if (s.bf16)
-    launch_combine_t(s, o_rounds, lse, inv_perm, static_cast<const uint16_t*>(v), y, stream);
+  if (s.o16)
+    launch_combine_t<uint16_t, true>(s, o_rounds, lse, inv_perm, static_cast<const uint16_t*>(v),
+                                     y, stream);
+  else if (s.bf16)
+    launch_combine_t<uint16_t, false>(s, o_rounds, lse, inv_perm, static_cast<const uint16_t*>(v),
+                                      y, stream);
   else
-    launch_combine_t(s, o_rounds, lse, inv_perm, static_cast<const float*>(v), y, stream);
+    launch_combine_t<float, false>(s, o_rounds, lse, inv_perm, static_cast<const float*>(v), y,
+                                   stream);
   return hipGetLastError();
 }
 

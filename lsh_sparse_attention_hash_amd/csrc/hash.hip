@@ -17,6 +17,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "lsh_device.h"
 #include "lsh_launch.h"
 
@@ -547,11 +549,11 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
 // fp32 inputs: every row in fp64 (one wave per (token, round) row).
 __global__ __launch_bounds__(256) void hash_exact_f32_kernel(
     const float* __restrict__ qk, const float* __restrict__ rot, int32_t* __restrict__ buckets,
-    int heads, int L, int half, int rounds, int64_t rows) {
+    int heads, int L, int half, int rounds, int64_t rows, int64_t blk0) {
   __shared__ double xs[4][kHeadDim];
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t row = (blk0 + blockIdx.x) * 4 + wave;
   if (row >= rows) return;
   // row indexes buckets[b][H][R][L]
   const int i = (int)(row % L);
@@ -581,9 +583,12 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
   }
   const int half = s.buckets / 2;
   if (!s.bf16) {
-    hipLaunchKernelGGL(hash_exact_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                       stream, static_cast<const float*>(qk), static_cast<const float*>(rot),
-                       buckets, s.heads, s.len, half, s.rounds, rows);
+    const int64_t nblk = (rows + 3) / 4;
+    for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks)
+      hipLaunchKernelGGL(hash_exact_f32_kernel, dim3((unsigned)std::min(kMaxBlocks, nblk - b0)),
+                         dim3(256), 0, stream, static_cast<const float*>(qk),
+                         static_cast<const float*>(rot), buckets, s.heads, s.len, half, s.rounds,
+                         rows, b0);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((int64_t)(s.len + kHashTokWG - 1) / kHashTokWG * s.heads * s.batch));

@@ -18,6 +18,8 @@
 // the row sums of the rounded probabilities).  fp32: one thread per query.
 #include <math.h>
 
+#include <algorithm>
+
 #include "lsh_device.h"
 #include "lsh_launch.h"
 
@@ -35,6 +37,7 @@ struct LocalArgs {
   float* y;
   float* lse;
   int L, nchunks, before, after;
+  int64_t blk0;   // first block of this launch piece
 };
 
 struct LocalLds {
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void local_bf16_kernel(LocalArgs a) {
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
   const int ql = lane & 15;
-  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t blk = a.blk0 + xcd_logical_block(blockIdx.x, gridDim.x);
   const int64_t bh = blk / a.nchunks;
   const int c = (int)(blk % a.nchunks);
   const int k0 = c - min(c, a.before);
@@ -254,8 +257,9 @@ __global__ __launch_bounds__(64) void local_f32_kernel(LocalArgs a, int causal, 
   __shared__ float vw[kChunk][kHeadDim];
   __shared__ float kinv[kChunk];
   const int lane = lane_id();
-  const int64_t bh = blockIdx.x / a.nchunks;
-  const int c = blockIdx.x % a.nchunks;
+  const int64_t blk = a.blk0 + blockIdx.x;
+  const int64_t bh = blk / a.nchunks;
+  const int c = (int)(blk % a.nchunks);
   const int k0 = c - min(c, a.before);
   const int k1 = causal ? c : c + min(a.nchunks - 1 - c, a.after);
   const float* xb = static_cast<const float*>(a.qk) + bh * (int64_t)a.L * kHeadDim;
@@ -318,8 +322,8 @@ __global__ __launch_bounds__(64) void local_f32_kernel(LocalArgs a, int causal, 
 }
 
 template <int NPRE>
-static hipError_t launch_local_bf16(const Shape& s, const LocalArgs& a, unsigned grid,
-                                    hipStream_t stream) {
+static void launch_local_bf16(const Shape& s, const LocalArgs& a, unsigned grid,
+                              hipStream_t stream) {
   if (s.causal && s.self_mask)
     hipLaunchKernelGGL((local_bf16_kernel<true, true, NPRE>), dim3(grid), dim3(256), 0, stream, a);
   else if (s.causal)
@@ -328,7 +332,6 @@ static hipError_t launch_local_bf16(const Shape& s, const LocalArgs& a, unsigned
     hipLaunchKernelGGL((local_bf16_kernel<false, true, NPRE>), dim3(grid), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((local_bf16_kernel<false, false, NPRE>), dim3(grid), dim3(256), 0, stream, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_local(const Shape& s, int before, int after, const void* qk, const void* v,
@@ -343,14 +346,19 @@ hipError_t launch_local(const Shape& s, int before, int after, const void* qk, c
   // a window wider than the sequence is the whole sequence
   a.before = before < a.nchunks ? before : a.nchunks;
   a.after = after < a.nchunks ? after : a.nchunks;
-  const unsigned grid = (unsigned)(s.token_heads() / kChunk);
-  if (!s.bf16) {
-    hipLaunchKernelGGL(local_f32_kernel, dim3(grid), dim3(64), 0, stream, a, s.causal, s.self_mask);
-    return hipGetLastError();
+  const int64_t nblk = s.token_heads() / kChunk;
+  for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks) {
+    a.blk0 = b0;
+    const unsigned grid = (unsigned)std::min(kMaxBlocks, nblk - b0);
+    if (!s.bf16)
+      hipLaunchKernelGGL(local_f32_kernel, dim3(grid), dim3(64), 0, stream, a, s.causal,
+                         s.self_mask);
+    else if (a.before + 1 + (s.causal ? 0 : a.after) <= 3)
+      launch_local_bf16<3>(s, a, grid, stream);
+    else
+      launch_local_bf16<1>(s, a, grid, stream);
   }
-  if (a.before + 1 + (s.causal ? 0 : a.after) <= 3)
-    return launch_local_bf16<3>(s, a, grid, stream);
-  return launch_local_bf16<1>(s, a, grid, stream);
+  return hipGetLastError();
 }
 
 }  // namespace lsh

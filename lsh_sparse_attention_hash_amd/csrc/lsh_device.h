@@ -16,6 +16,11 @@ constexpr int kHeadDim = 64;   // d
 constexpr int kChunk = 64;     // m
 constexpr int kWave = 64;      // CDNA wavefront
 
+// One dispatch may hold fewer than 2^32 work-items.  Kernels whose grid grows
+// with the problem are launched in pieces of at most kMaxBlocks workgroups
+// (2^30 work-items at 256 per workgroup), each told its first block.
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;
+
 // 16-byte global/LDS load and store through uint4.
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);

@@ -10,7 +10,8 @@ namespace lsh {
 
 struct Shape {
   int batch, heads, len, buckets, rounds, causal, self_mask;
-  bool bf16;
+  bool bf16;   // qk, v, rot are bf16 (else fp32)
+  bool o16;    // per-round outputs as fp16 rows with a per-(batch, head) scale (bf16 only)
   int64_t segments() const { return (int64_t)batch * heads * rounds; }
   int64_t token_heads() const { return (int64_t)batch * heads * len; }
 };
@@ -24,7 +25,7 @@ size_t sort_workspace_bytes(const Shape& s);
 hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, int32_t* inv_perm,
                        void* workspace, hipStream_t stream);
 
-// Per-round outputs.  fp32 inputs: fp32 rows [S][L][64].  bf16 inputs: a
+// Per-round outputs.  fp32 rows [S][L][64] (any input dtype), or with o16: a
 // header of kVParts partial maxima of |v| per (batch, head) (fp32, padded to
 // 256 bytes), then fp16 rows [S][L][64] holding o * 2^-k, with k the
 // (batch, head)'s scale exponent (o_scale_exponent of the header's maximum;

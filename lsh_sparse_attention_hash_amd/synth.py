@@ -65,6 +65,15 @@ class Workload:
     # its window; None for the LSH workloads
     look_before: "int | None" = None
     look_after: "int | None" = None
+    # storage of the per-round outputs between the attention and the combine:
+    # "f32" rows, or "f16_scaled" (bf16 inputs only); "auto" = f16_scaled for
+    # bf16 inputs, f32 for fp32 inputs
+    o_format: str = "auto"
+
+    @property
+    def o16(self) -> bool:
+        """Per-round outputs stored as scaled fp16 rows."""
+        return self.dtype == "bf16" and self.o_format in ("auto", "f16_scaled")
 
     @property
     def is_local(self) -> bool:

@@ -14,10 +14,13 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session", autouse=True)
 def built_libraries():
-    """Build liblsh.so and the oracle only if they are missing."""
+    """Build liblsh.so if it is missing or was built from other sources than
+    those in the tree (its recorded source digest differs), and the oracle if
+    it is missing or older than its source."""
     from lsh_sparse_attention_hash_amd import build as lib_build
     from oracle import oracle
-    if not os.path.exists(lib_build.LIB):
+    if not lib_build.is_current():
+        print("liblsh.so is missing or stale: rebuilding", flush=True)
         lib_build.build()
     oracle.build(force=False)
     yield

@@ -1,8 +1,8 @@
 """Host-side reading of the per-round output buffer of lsh_chunk_attend, from
 the layout the C ABI documents (include/lsh.h):
 
-* fp32 inputs: fp32 rows [b][H][R][L][64];
-* bf16 inputs: a header of 256 fp32 partial maxima of |v| per (b, h)
+* LSH_O_F32 (any input dtype): fp32 rows [b][H][R][L][64];
+* LSH_O_F16_SCALED (bf16 inputs): a header of 256 fp32 partial maxima of |v| per (b, h)
   ([b][H][256], padded to a multiple of 256 bytes), then fp16 rows
   [b][H][R][L][64] holding o * 2^-k, where k = max(e - 15, -100) and e is the
   smallest integer with max(header of (b, h)) < 2^e (e = -126 below 2^-126).
@@ -17,7 +17,7 @@ V_PARTS = 256
 
 
 def header_bytes(w):
-    if w.dtype != "bf16":
+    if not w.o16:
         return 0
     n = w.batch * w.heads * V_PARTS * 4
     return (n + 255) // 256 * 256
@@ -43,7 +43,7 @@ def read_o_rounds(buf, w):
     buf = np.asarray(buf).view(np.uint8).ravel()
     shape = (w.batch, w.heads, w.n_rounds, w.seq_len, w.head_dim)
     n = int(np.prod(shape))
-    if w.dtype != "bf16":
+    if not w.o16:
         return buf[: n * 4].view(np.float32).reshape(shape).copy()
     hb = header_bytes(w)
     o = buf[hb: hb + n * 2].view(np.float16).reshape(shape).astype(np.float32)

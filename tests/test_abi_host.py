@@ -118,19 +118,38 @@ def test_workspace_bytes_cover_the_count_tables():
 
 
 def test_per_round_buffer_size():
-    """fp32 inputs: fp32 rows; bf16 inputs: 256 fp32 partial maxima per
-    (batch, head), padded to a multiple of 256 bytes, then fp16 rows."""
+    """LSH_O_F32 (either input dtype): fp32 rows; LSH_O_F16_SCALED (bf16
+    inputs): 256 fp32 partial maxima per (batch, head), padded to a multiple
+    of 256 bytes, then fp16 rows."""
     for b, H, L, R, dt in ((1, 8, 65536, 8, B.LSH_BF16), (2, 3, 192, 5, B.LSH_BF16),
                            (1, 1, 1024, 1, B.LSH_F32), (3, 2, 448, 3, B.LSH_F32)):
-        c = cfg(batch=b, heads=H, seq_len=L, n_rounds=R, dtype=dt)
         rows = b * H * R * L * 64
+        c = cfg(batch=b, heads=H, seq_len=L, n_rounds=R, dtype=dt)
+        assert c.o_format == B.LSH_O_F32            # the zero default
+        assert B.lsh_o_rounds_bytes(c) == 4 * rows
+        c = cfg(batch=b, heads=H, seq_len=L, n_rounds=R, dtype=dt, o_format=B.LSH_O_F16_SCALED)
         if dt == B.LSH_BF16:
             header = -(-(b * H * 256 * 4) // 256) * 256
             assert B.lsh_o_rounds_bytes(c) == header + 2 * rows
         else:
-            assert B.lsh_o_rounds_bytes(c) == 4 * rows
+            assert B.lsh_o_rounds_bytes(c) == 0     # unsupported with fp32 inputs
     assert B.lsh_o_rounds_bytes(cfg(seq_len=0)) == 0
     assert B.lsh_o_rounds_bytes(cfg(head_dim=32)) == 0
+
+
+def test_o_format_is_validated():
+    lib = B.library()
+    for kw, status in ((dict(o_format=2), B.LSH_ERR_INVALID_ARGUMENT),
+                       (dict(o_format=-1), B.LSH_ERR_INVALID_ARGUMENT),
+                       (dict(o_format=B.LSH_O_F16_SCALED, dtype=B.LSH_F32),
+                        B.LSH_ERR_UNSUPPORTED)):
+        c = cfg(**kw)
+        assert call_hash(c) == status
+        assert lib.lsh_chunk_attend(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    None) == status
+        assert lib.lsh_unsort_combine(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None) == status
+        assert b"o_format" in lib.lsh_last_error() or b"F16" in lib.lsh_last_error()
 
 
 def test_empty_problems_are_no_ops():
@@ -266,3 +285,4 @@ def test_layer_calls_check_pointers_workspace_and_flags():
         B.LSH_ERR_INVALID_ARGUMENT
     e = layer_cfg(seq_len=0)
     assert lib.lsh_reversible_forward(ctypes.byref(e), None, *([None] * 5), 0, None) == B.LSH_OK
+
