@@ -4,11 +4,10 @@ Bar (from the method's contract): bucket ids, perm and inv_perm bit-exact;
 o_rounds, lse and y within max abs error 1e-5 for fp32 inputs and 2e-2 for
 bf16 inputs; lse = -inf exactly where the oracle's is.
 
-Small and medium problems are compared element by element in full.  The two
-largest workloads run at full size in the launch configuration the benchmark
-times; there the oracle checks a seeded sample of rows of every step (the
-integer steps are also checked in full where the oracle can afford it), each
-step fed with the GPU's own (already verified) inputs.
+Every workload, the two largest benchmark shapes included, is compared
+element by element in full against the oracle's own forward, in the launch
+configuration the benchmark times, and for bf16 inputs in both per-round
+output formats (fp32 rows and scaled fp16 rows).
 """
 import os
 import sys
@@ -18,7 +17,7 @@ import pytest
 import torch
 
 from lsh_sparse_attention_hash_amd import synth
-from o_rounds_layout import header, read_o_rounds
+from o_rounds_layout import header, header_bytes, read_o_rounds
 from oracle import oracle
 
 pytestmark = pytest.mark.gpu
@@ -68,32 +67,41 @@ def assert_close(got, want, tol, what):
     return err
 
 
-def full_parity(B, w):
+def full_parity(B, w, formats=("auto",)):
+    """Every output of the GPU forward against the oracle's own fp64 forward,
+    element by element; once per per-round output format in `formats`
+    ("auto", "f32", "f16_scaled"), all against the same oracle result."""
     say(f"[parity] {w}")
     inp = synth.make_inputs(w)
-    f = run_gpu(B, w, inp)
     qk = synth.to_f64(inp["qk"], w.dtype)
     v = synth.to_f64(inp["v"], w.dtype)
     rot = synth.to_f64(inp["rot"], w.dtype)
     ref = oracle.forward(qk, v, rot, w.n_buckets, w.n_rounds, w.chunk_len, w.causal, w.self_mask)
     tol = TOL[w.dtype]
-    assert np.array_equal(host(f.buckets), ref["buckets"]), "buckets differ"
-    assert np.array_equal(host(f.perm), ref["perm"]), "perm differs"
-    assert np.array_equal(host(f.inv_perm), ref["inv_perm"]), "inv_perm differs"
-    assert_close_lse(host(f.lse), ref["lse"], tol, "lse")
-    o_gpu = read_o_rounds(host(f.o_rounds), w)
-    assert_close(o_gpu, ref["o_rounds"], tol, "o_rounds")
-    err = assert_close(host(f.y), ref["y"], tol, "y")
-    # the combine step alone, on the GPU's own per-round outputs
-    y2 = oracle.combine(o_gpu, host(f.lse), host(f.inv_perm), v)
-    assert_close(host(f.y), y2, 1e-5, "combine on identical inputs")
-    say(f"[parity] {w.name}: y max abs err {err:.3g}, fallback rows {int(host(f.fallback_rows)[0])}")
-    return f
+    for fmt in formats:
+        wf = w.replace(o_format=fmt)
+        f = run_gpu(B, wf, inp)
+        assert np.array_equal(host(f.buckets), ref["buckets"]), "buckets differ"
+        assert np.array_equal(host(f.perm), ref["perm"]), "perm differs"
+        assert np.array_equal(host(f.inv_perm), ref["inv_perm"]), "inv_perm differs"
+        assert_close_lse(host(f.lse), ref["lse"], tol, "lse")
+        o_gpu = read_o_rounds(host(f.o_rounds), wf)
+        err_o = assert_close(o_gpu, ref["o_rounds"], tol, "o_rounds")
+        err = assert_close(host(f.y), ref["y"], tol, "y")
+        # the combine step alone, on the GPU's own per-round outputs
+        y2 = oracle.combine(o_gpu, host(f.lse), host(f.inv_perm), v)
+        assert_close(host(f.y), y2, 1e-5, "combine on identical inputs")
+        say(f"[parity] {w.name} ({'f16_scaled' if wf.o16 else 'f32'} rows): o max abs err "
+            f"{err_o:.3g}, y max abs err {err:.3g}, fallback rows "
+            f"{int(host(f.fallback_rows)[0])} of {w.token_rounds}")
+        del f, o_gpu, y2
+    return ref
 
 
 @pytest.mark.parametrize("name", ["tiny", "small", "medium"])
 def test_workload_full_parity(B, name):
-    full_parity(B, synth.WORKLOADS[name])
+    w = synth.WORKLOADS[name]
+    full_parity(B, w, ("auto", "f32") if w.dtype == "bf16" else ("auto",))
 
 
 EDGE = {
@@ -128,7 +136,8 @@ EDGE = {
 
 @pytest.mark.parametrize("name", sorted(EDGE))
 def test_edge_case_parity(B, name):
-    full_parity(B, EDGE[name])
+    w = EDGE[name]
+    full_parity(B, w, ("auto", "f32") if w.dtype == "bf16" else ("auto",))
 
 
 
@@ -215,7 +224,6 @@ def test_per_round_output_scale(B):
     raw = host(f.o_rounds)
     hdr = header(raw, w)
     assert np.array_equal(hdr.max(axis=2).astype(np.float64), np.abs(v).max(axis=(2, 3)))
-    from o_rounds_layout import header_bytes
     n = w.batch * w.heads * w.n_rounds * w.seq_len * w.head_dim
     stored = raw[header_bytes(w): header_bytes(w) + 2 * n].view(np.float16)
     assert np.abs(stored.astype(np.float64)).max() <= 2.0 ** 15 * (1 + 2.0 ** -10)
@@ -244,7 +252,15 @@ def test_scaled_inputs_parity(B, log2_scale):
     ref = oracle.forward(scaled, synth.to_f64(inp["v"], "bf16"), synth.to_f64(inp["rot"], "bf16"),
                          w.n_buckets, w.n_rounds, w.chunk_len, w.causal, w.self_mask)
     assert np.array_equal(host(f.buckets), ref["buckets"])
-    assert_close_lse(host(f.lse), ref["lse"], 2e-2 * max(1.0, 2.0 ** log2_scale), "lse")
+    # scores of size ~2^30 carry the fp32 relative error of their 64-term dot
+    # products (about 64 * 2^-24 of |x_i|), so lse is held to 2e-2 plus a
+    # relative 4e-5 of its size
+    got, want = host(f.lse), ref["lse"]
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))
+    fin = ~np.isneginf(want)
+    bound = 2e-2 + 4e-5 * np.abs(want[fin])
+    excess = (np.abs(got[fin] - want[fin]) / bound).max(initial=0.0)
+    assert excess <= 1.0, f"lse error {excess:.3g} times its bound"
     assert_close(host(f.y), ref["y"], 2e-2, "y")
     say(f"[scaled 2^{log2_scale}] fallback rows {int(host(f.fallback_rows)[0])}")
 
@@ -284,63 +300,74 @@ def test_hash_settles_more_uncertain_rows_than_one_list_holds(B):
 
 
 # --------------------------------------------------------------- full size
-def sampled_parity(B, w, n_hash, n_rows, seed):
-    say(f"[parity-full] {w}")
-    inp = synth.make_inputs(w)
-    f = run_gpu(B, w, inp)
-    tol = TOL[w.dtype]
-    g = np.random.default_rng(seed)
-    qk = synth.to_f64(inp["qk"], w.dtype)
-    rot = synth.to_f64(inp["rot"], w.dtype)
-    bk = host(f.buckets)
-    idx = g.integers(0, bk.size, n_hash)
-    ref_b = oracle.hash_rows(qk, rot, w.n_buckets, w.n_rounds, idx)
-    assert np.array_equal(bk.ravel()[idx], ref_b), "sampled buckets differ"
-    say(f"[parity-full] {w.name}: {n_hash} sampled buckets exact")
-    perm, inv = oracle.sort(bk)
-    assert np.array_equal(host(f.perm), perm), "perm differs"
-    assert np.array_equal(host(f.inv_perm), inv), "inv_perm differs"
-    say(f"[parity-full] {w.name}: perm / inv_perm exact")
-    v = synth.to_f64(inp["v"], w.dtype)
-    rows = g.integers(0, bk.size, n_rows)
-    o_ref, lse_ref = oracle.attend_rows(qk, v, bk, perm, w.n_buckets, w.chunk_len, w.causal,
-                                        w.self_mask, rows)
-    lse = host(f.lse).ravel()[rows]
-    assert_close_lse(lse, lse_ref, tol, "lse")
-    o_all = read_o_rounds(host(f.o_rounds), w)
-    o = o_all.reshape(-1, w.head_dim)[rows]
-    err_o = assert_close(o, o_ref, tol, "o_rounds")
-    toks = g.integers(0, w.batch * w.heads * w.seq_len, n_rows)
-    y_ref = oracle.combine_rows(o_all, host(f.lse), inv, v, toks)
-    y = host(f.y).reshape(-1, w.head_dim)[toks]
-    assert_close(y, y_ref, 1e-5, "combine rows")
-    say(f"[parity-full] {w.name}: o err {err_o:.3g}, fallback rows {int(host(f.fallback_rows)[0])}")
+# The two largest benchmark shapes in the launch configuration the benchmark
+# times, every output element against the oracle's full fp64 forward: every
+# bucket id, perm and inv_perm entry bit-exact, every lse, per-round row and y
+# within tolerance, in both per-round output formats.  The oracle takes a few
+# seconds (Long) to some tens of seconds (Very long) on the host's cores.
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["long", "verylong"])
+def test_full_size_parity(B, name):
+    full_parity(B, synth.WORKLOADS[name], ("auto", "f32"))
 
 
-def test_long_full_size_sampled(B):
-    sampled_parity(B, synth.WORKLOADS["long"], n_hash=20000, n_rows=20000, seed=31)
+def _o_rows(f, w, h):
+    """Per-round rows of head h (batch 0) as raw bytes, and its header part."""
+    raw = f.o_rounds
+    hb = header_bytes(w)
+    row_bytes = w.n_rounds * w.seq_len * w.head_dim * (2 if w.o16 else 4)
+    rows = raw[hb + h * row_bytes: hb + (h + 1) * row_bytes]
+    hdr = raw[h * 1024: (h + 1) * 1024] if w.o16 else raw[:0]
+    return rows, hdr
 
 
-def test_verylong_full_size_sampled(B):
-    sampled_parity(B, synth.WORKLOADS["verylong"], n_hash=4000, n_rows=20000, seed=32)
+def test_head_alone_equals_head_inside_eight_and_repeats(B):
+    """Determinism across launch geometries: head 5 of the Long shape run on
+    its own (H = 1: other sort tiles, attention run lengths and grids) gives
+    the same bits in every output as inside the H = 8 run; ten repeats of the
+    H = 8 run give the same bits as the first."""
+    w8 = synth.WORKLOADS["long"]
+    inp = synth.make_inputs(w8)
+    h = 5
+    f8 = run_gpu(B, w8, inp)
+    first = [t.clone() for t in (f8.buckets, f8.perm, f8.inv_perm, f8.o_rounds, f8.lse, f8.y)]
+    w1 = w8.replace(heads=1)
+    one = {"qk": inp["qk"][:, h:h + 1].copy(), "v": inp["v"][:, h:h + 1].copy(),
+           "rot": inp["rot"][h:h + 1].copy()}
+    f1 = run_gpu(B, w1, one)
+    for name in ("buckets", "perm", "inv_perm", "lse", "y"):
+        assert torch.equal(getattr(f8, name)[:, h:h + 1], getattr(f1, name)), name
+    rows8, hdr8 = _o_rows(f8, w8, h)
+    rows1, hdr1 = _o_rows(f1, w1, 0)
+    assert torch.equal(rows8, rows1), "per-round rows"
+    assert torch.equal(hdr8, hdr1), "per-round header"
+    del f1
+    for rep in range(10):
+        f8.run(B.to_device(inp["qk"], w8.dtype), B.to_device(inp["v"], w8.dtype),
+               B.to_device(inp["rot"], w8.dtype))
+        torch.cuda.synchronize()
+        for a, t in zip(first, (f8.buckets, f8.perm, f8.inv_perm, f8.o_rounds, f8.lse, f8.y)):
+            assert torch.equal(a, t), f"repeat {rep}"
+    say("[determinism] head alone == head in eight; ten repeats identical")
 
 
-def test_long_end_to_end_rows(B):
-    """End to end at full size: y of sampled tokens from the oracle's own
-    hash -> sort -> attend -> combine of the heads they belong to (one head's
-    oracle work is affordable)."""
-    w = synth.WORKLOADS["long"].replace(heads=1)
-    inp = synth.make_inputs(synth.WORKLOADS["long"])
-    inp = {"qk": inp["qk"][:, :1].copy(), "v": inp["v"][:, :1].copy(),
-           "rot": inp["rot"][:1].copy()}
-    f = run_gpu(B, w, inp)
-    qk = synth.to_f64(inp["qk"], w.dtype)
-    v = synth.to_f64(inp["v"], w.dtype)
-    rot = synth.to_f64(inp["rot"], w.dtype)
-    bk = oracle.hash(qk, rot, w.n_buckets, w.n_rounds)
-    assert np.array_equal(host(f.buckets), bk)
-    perm, inv = oracle.sort(bk)
-    o, lse = oracle.attend(qk, v, bk, perm, w.n_buckets, w.chunk_len, w.causal, w.self_mask)
-    toks = np.random.default_rng(33).integers(0, w.seq_len, 4000)
-    y_ref = oracle.combine_rows(o, lse, inv, v, toks)
-    assert_close(host(f.y).reshape(-1, 64)[toks], y_ref, TOL["bf16"], "y")
+def test_fp32_hash_beyond_one_dispatch(B):
+    """2^26 (token, round) rows of fp32 inputs: the exact hash runs one wave
+    per row, 2^32 work-items in all, more than one dispatch may hold; the
+    library launches it in pieces.  Sampled rows and both ends against the
+    oracle."""
+    L, R = 65536, 1024
+    w = synth.Workload("f32_many_rows", 1, 1, L, 64, 2, R, 64, False, False, "f32", 42)
+    g = np.random.default_rng(43)
+    qk = g.standard_normal((1, 1, L, 64)).astype(np.float32)
+    rot = g.standard_normal((1, R, 1, 64)).astype(np.float32)
+    cfg = B.config_for(w)
+    bk = torch.empty((1, 1, R, L), dtype=torch.int32, device="cuda")
+    B.lsh_hash(cfg, torch.from_numpy(qk).cuda(), torch.from_numpy(rot).cuda(), bk)
+    torch.cuda.synchronize()
+    got = bk.cpu().numpy().ravel()
+    idx = np.concatenate([np.arange(4096), got.size - 1 - np.arange(4096),
+                          g.integers(0, got.size, 20000)])
+    ref = oracle.hash_rows(qk.astype(np.float64), rot.astype(np.float64), 2, R, idx)
+    assert np.array_equal(got[idx], ref)
+    assert set(np.unique(got)) <= {0, 1}
