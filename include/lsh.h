@@ -131,6 +131,25 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * lsh_sort_static_scratch -- lsh_sort without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid allocation).
+ *
+ *   cfg, buckets, perm, inv_perm   as for lsh_sort
+ *
+ * Same results as lsh_sort.  The count tables live in a static array of
+ * 32 MiB of device memory inside the library, one per GPU, held until the
+ * process ends; nothing is allocated by the call.  A configuration whose
+ * lsh_sort_workspace_bytes(cfg) exceeds 32 MiB returns
+ * LSH_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  Every call on one
+ * GPU shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, or different threads) race and must be serialised by the caller.
+ * The array's address on a GPU is looked up on the first call there.
+ */
+lsh_status lsh_sort_static_scratch(const lsh_config* cfg, const int32_t* buckets,
+                                   int32_t* perm, int32_t* inv_perm, void* stream);
+
+/*
  * lsh_chunk_attend -- attention inside chunks of the bucket-sorted sequence.
  * Follows: Reformer study note, sections "LSH Attention" (candidate set
  * N_LSH(i) = same-bucket keys; y_i = softmax-weighted sum of v_j over it with

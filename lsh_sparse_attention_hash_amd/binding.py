@@ -29,7 +29,8 @@ LSH_BF16 = 1
 LSH_O_F32 = 0
 LSH_O_F16_SCALED = 1
 
-EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_o_rounds_bytes", "lsh_chunk_attend",
+EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_sort_static_scratch",
+           "lsh_o_rounds_bytes", "lsh_chunk_attend",
            "lsh_unsort_combine", "lsh_union_workspace_bytes", "lsh_chunk_attend_union",
            "lsh_local_attend", "lsh_project_qkv", "lsh_project_out", "lsh_ffn_workspace_bytes",
            "lsh_ffn", "lsh_layer_workspace_bytes", "lsh_reversible_forward",
@@ -70,6 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsh_sort_workspace_bytes.argtypes = [cfgp]
     lib.lsh_sort_workspace_bytes.restype = SZ
     lib.lsh_sort.argtypes = [cfgp, P, P, P, P, SZ, P]
+    lib.lsh_sort_static_scratch.argtypes = [cfgp, P, P, P, P]
     lib.lsh_o_rounds_bytes.argtypes = [cfgp]
     lib.lsh_o_rounds_bytes.restype = SZ
     lib.lsh_chunk_attend.argtypes = [cfgp, P, P, P, P, P, P, P]
@@ -89,7 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsh_layer_workspace_bytes.restype = SZ
     lib.lsh_reversible_forward.argtypes = [lcp, lwp, P, P, P, P, P, SZ, P]
     lib.lsh_reversible_inverse.argtypes = [lcp, lwp, P, P, P, P, P, SZ, P]
-    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
+    for f in ("lsh_hash", "lsh_sort", "lsh_sort_static_scratch", "lsh_chunk_attend", "lsh_unsort_combine",
               "lsh_local_attend", "lsh_chunk_attend_union", "lsh_project_qkv", "lsh_project_out",
               "lsh_ffn", "lsh_reversible_forward", "lsh_reversible_inverse"):
         getattr(lib, f).restype = I32
@@ -179,6 +181,16 @@ def lsh_sort(cfg: LshConfig, buckets, perm, inv_perm, workspace, stream=None):
     _check("lsh_sort", _lib.lsh_sort(ctypes.byref(cfg), _ptr(buckets), _ptr(perm), _ptr(inv_perm),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+
+
+def lsh_sort_static_scratch(cfg: LshConfig, buckets, perm, inv_perm, stream=None):
+    """lsh_sort with the library's static scratch (no workspace argument)."""
+    shape = (cfg.batch, cfg.heads, cfg.n_rounds, cfg.seq_len)
+    for t, n in ((buckets, "buckets"), (perm, "perm"), (inv_perm, "inv_perm")):
+        _expect(t, shape, torch.int32, n)
+    _check("lsh_sort_static_scratch",
+           _lib.lsh_sort_static_scratch(ctypes.byref(cfg), _ptr(buckets), _ptr(perm),
+                                        _ptr(inv_perm), _stream(stream)))
 
 
 def lsh_o_rounds_bytes(cfg: LshConfig) -> int:

@@ -181,6 +181,30 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm
                   "lsh_sort");
 }
 
+lsh_status lsh_sort_static_scratch(const lsh_config* cfg, const int32_t* buckets,
+                                   int32_t* perm, int32_t* inv_perm, void* stream) {
+  lsh::Shape s;
+  bool empty = false;
+  LSH_TRY(check_config(cfg, &s, &empty));
+  if (empty) return ok();
+  LSH_TRY(check_ptr(buckets, "buckets"));
+  LSH_TRY(check_ptr(perm, "perm"));
+  LSH_TRY(check_ptr(inv_perm, "inv_perm"));
+  const size_t need = lsh::sort_workspace_bytes(s);
+  if (need > lsh::static_sort_scratch_bytes())
+    return fail(LSH_ERR_WORKSPACE_TOO_SMALL,
+                "the sort needs %zu bytes of scratch, the static scratch holds %zu", need,
+                lsh::static_sort_scratch_bytes());
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int device = 0;
+  hipError_t e = st ? hipStreamGetDevice(st, &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return launched(e, "lsh_sort_static_scratch: device of the stream");
+  void* ws = nullptr;
+  e = lsh::static_sort_scratch(device, &ws);
+  if (e != hipSuccess) return launched(e, "lsh_sort_static_scratch: scratch address");
+  return launched(lsh::launch_sort(s, buckets, perm, inv_perm, ws, st), "lsh_sort_static_scratch");
+}
+
 lsh_status lsh_chunk_attend(const lsh_config* cfg, const void* qk, const void* v,
                             const int32_t* buckets, const int32_t* perm, void* o_rounds,
                             float* lse, void* stream) {

@@ -24,6 +24,10 @@ int sort_tile(const Shape& s);
 size_t sort_workspace_bytes(const Shape& s);
 hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, int32_t* inv_perm,
                        void* workspace, hipStream_t stream);
+// The library's static device scratch for the sort: its size, and its device
+// address on `device` (looked up on the first call for that device).
+size_t static_sort_scratch_bytes();
+hipError_t static_sort_scratch(int device, void** ptr);
 
 // Per-round outputs.  fp32 rows [S][L][64] (any input dtype), or with o16: a
 // header of kVParts partial maxima of |v| per (batch, head) (fp32, padded to

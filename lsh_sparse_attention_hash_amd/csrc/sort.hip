@@ -15,6 +15,8 @@
 //            through per-bucket LDS masks, or ballots over the key bits for
 //            B > 2048), so the scatter is stable.
 // Workspace: cnt[S][tiles][B] (counts, then tile prefixes) and base[S][B].
+#include <mutex>
+
 #include "lsh_device.h"
 #include "lsh_launch.h"
 
@@ -340,6 +342,41 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
     hipLaunchKernelGGL(sort_scatter_kernel<false>, dim3((unsigned)(S * ntiles)), dim3(64), lds,
                        stream, buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
+// The sort's count tables in the library's own device memory, for callers
+// that cannot allocate.  One array per GPU, alive until the process ends;
+// every call on that GPU shares it, so calls that overlap on one GPU race.
+// Its contents on entry do not matter: the count pass writes every table
+// entry the scatter reads.  In host code `scratch` names a host-side stand-in:
+// kernels are given the device address looked up once per device below.
+constexpr size_t kStaticSortScratch = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticSortScratch];
+
+size_t static_sort_scratch_bytes() { return kStaticSortScratch; }
+
+hipError_t static_sort_scratch(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != device ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 }  // namespace lsh

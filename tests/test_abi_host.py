@@ -286,3 +286,21 @@ def test_layer_calls_check_pointers_workspace_and_flags():
     e = layer_cfg(seq_len=0)
     assert lib.lsh_reversible_forward(ctypes.byref(e), None, *([None] * 5), 0, None) == B.LSH_OK
 
+
+def test_static_scratch_sort_validates_before_any_launch():
+    """lsh_sort_static_scratch rejects bad arguments like lsh_sort, and a
+    configuration whose count tables exceed its 32 MiB static scratch with
+    LSH_ERR_WORKSPACE_TOO_SMALL, all on the host."""
+    lib = B.library()
+    c = cfg()
+    assert lib.lsh_sort_static_scratch(ctypes.byref(c), None, FAKE, FAKE, None) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    assert lib.lsh_sort_static_scratch(ctypes.byref(cfg(n_buckets=7)), FAKE, FAKE, FAKE,
+                                       None) == B.LSH_ERR_INVALID_ARGUMENT
+    big = cfg(batch=1, heads=8, seq_len=131072, n_buckets=16384, n_rounds=8)
+    assert B.lsh_sort_workspace_bytes(big) > 32 << 20
+    assert lib.lsh_sort_static_scratch(ctypes.byref(big), FAKE, FAKE, FAKE, None) == \
+        B.LSH_ERR_WORKSPACE_TOO_SMALL
+    assert b"static scratch" in lib.lsh_last_error()
+    empty = cfg(seq_len=0)
+    assert lib.lsh_sort_static_scratch(ctypes.byref(empty), None, None, None, None) == B.LSH_OK

@@ -1,0 +1,62 @@
+"""lsh_sort_static_scratch (the sort that allocates nothing: its count tables
+live in a static device array inside the library) against lsh_sort with a
+caller workspace, through the C ABI: bit-identical perm and inv_perm (and
+both equal to the oracle's sort) on two calls in a row, the second on a
+smaller input, so the second call runs on the array the first one left
+behind."""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from lsh_sparse_attention_hash_amd import synth
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lsh_sparse_attention_hash_amd import binding
+    return binding
+
+
+def _buckets(B, w):
+    inp = synth.make_inputs(w)
+    cfg = B.config_for(w)
+    bk = torch.empty((w.batch, w.heads, w.n_rounds, w.seq_len), dtype=torch.int32, device="cuda")
+    B.lsh_hash(cfg, B.to_device(inp["qk"], w.dtype), B.to_device(inp["rot"], w.dtype), bk)
+    return cfg, bk
+
+
+def test_static_scratch_sort_equals_workspace_sort(B):
+    lib = B.library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for name in ("long", "medium"):            # the second call is the smaller one
+        w = synth.WORKLOADS[name]
+        say(f"[no-alloc] {w}")
+        cfg, bk = _buckets(B, w)
+        ref_perm, ref_inv = torch.empty_like(bk), torch.empty_like(bk)
+        ws = torch.empty(max(16, B.lsh_sort_workspace_bytes(cfg)), dtype=torch.uint8,
+                         device="cuda")
+        B.lsh_sort(cfg, bk, ref_perm, ref_inv, ws)
+        perm = torch.full_like(bk, -1)
+        inv = torch.full_like(bk, -1)
+        st = lib.lsh_sort_static_scratch(ctypes.byref(cfg), ctypes.c_void_p(bk.data_ptr()),
+                                         ctypes.c_void_p(perm.data_ptr()),
+                                         ctypes.c_void_p(inv.data_ptr()), stream)
+        assert st == B.LSH_OK, lib.lsh_last_error()
+        torch.cuda.synchronize()
+        assert torch.equal(perm, ref_perm) and torch.equal(inv, ref_inv)
+        p, i = oracle.sort(bk.cpu().numpy())
+        assert np.array_equal(perm.cpu().numpy(), p) and np.array_equal(inv.cpu().numpy(), i)
+        say(f"[no-alloc] {name}: perm and inv_perm equal the workspace sort and the oracle")
