@@ -1,20 +1,31 @@
 // sort.hip -- stable counting sort of every (batch, head, round) segment by
 // bucket id (Reformer study note, section "Sorting and Chunking": tokens are
 // sorted by hash bucket so each bucket becomes contiguous).  Because positions
-// enter in increasing order and the scatter is stable, the result is the
-// order of the unique key (bucket, original position).
+// enter in increasing order and every ranking step keeps that order, the
+// result is the order of the unique key (bucket, original position).
 //
-// Four launches per call (two for segments of at most 16,384 tokens whose
+// B <= 2048: two launches.
+//   wide_count    one workgroup per (segment, tile of up to 16,384 keys):
+//                 LDS histogram of the tile -> cnt[S][tiles][B]
+//   wide_scatter  one workgroup of W waves per (segment, tile): each wave
+//                 ranks its share of the tile in position order (per-wave LDS
+//                 bucket masks), the workgroup turns the counts into tile-local
+//                 bucket starts and global slots (bucket base plus the counts of
+//                 the segment's earlier tiles, from cnt), writes inv_perm in
+//                 position order and stages the tile's sorted positions in LDS
+//                 so that perm leaves in runs of consecutive slots.
+// B > 2048: four launches (two for segments of at most 16,384 tokens whose
 // tile histograms fit in LDS: prefix, one workgroup per segment, does the
 // first three):
 //   count    one workgroup per (segment, tile): LDS histogram of the tile
 //   scan_t   one thread per (segment, bucket): exclusive prefix over tiles
 //   scan_b   one workgroup per segment: exclusive prefix over bucket totals
 //   scatter  one wave per (segment, tile): walks the tile in order, 64 keys
-//            at a time; equal keys inside a batch are ranked by lane (found
-//            through per-bucket LDS masks, or ballots over the key bits for
-//            B > 2048), so the scatter is stable.
-// Workspace: cnt[S][tiles][B] (counts, then tile prefixes) and base[S][B].
+//            at a time; equal keys inside a batch are ranked by lane through
+//            ballots over the key bits, so the scatter is stable.
+// Workspace: cnt[S][tiles][B] (B <= 2048); cnt[S][tiles][B] (counts, then
+// tile prefixes) and base[S][B] (B > 2048).
+#include <algorithm>
 #include <mutex>
 
 #include "lsh_device.h"
@@ -22,7 +33,35 @@
 
 namespace lsh {
 
+// Wide tiles (B <= 2048): the tile is the largest of 16,384 ... 1,024 keys
+// that still gives at least 256 workgroups (longer tiles write perm in longer
+// runs; the workgroups must still cover the chip), with W waves of up to 32
+// batches of 64 keys and per-wave bucket tables for up to NB buckets.
+constexpr int kWideMaxBuckets = 2048;
+
+struct WidePlan {
+  int tile, waves, nbmax, nbat;
+};
+
+static WidePlan wide_plan(const Shape& s) {
+  WidePlan p;
+  p.nbmax = s.buckets <= 256 ? 256 : (s.buckets <= 1024 ? 1024 : 2048);
+  const int cap = p.nbmax == 256 ? 4096 : (p.nbmax == 1024 ? 16384 : 8192);
+  p.tile = 1024;
+  while (p.tile < cap && s.segments() * ((s.len + 2 * p.tile - 1) / (2 * p.tile)) >= 256)
+    p.tile *= 2;
+  if (p.nbmax == 256)
+    p.waves = p.tile >= 4096 ? 8 : 4;
+  else if (p.nbmax == 1024)
+    p.waves = p.tile >= 8192 ? 8 : 4;
+  else
+    p.waves = 4;
+  p.nbat = p.tile / (kWave * p.waves);
+  return p;
+}
+
 int sort_tile(const Shape& s) {
+  if (s.buckets <= kWideMaxBuckets) return wide_plan(s).tile;
   // at least max(1024, B) keys per tile keeps the count table no larger than
   // the keys; large calls double it up to 4096 while they would have more
   // than 1024 tiles (fewer, longer scatter waves)
@@ -42,6 +81,7 @@ size_t sort_workspace_bytes(const Shape& s) {
   const int64_t S = s.segments();
   const int64_t T = sort_tiles(s);
   const size_t cnt = (size_t)S * T * s.buckets * sizeof(int32_t);
+  if (s.buckets <= kWideMaxBuckets) return cnt;
   const size_t base = (size_t)S * s.buckets * sizeof(int32_t);
   return ((cnt + 255) & ~(size_t)255) + base;
 }
@@ -82,8 +122,9 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
 // Loads are issued eight tiles at a time so their latencies overlap.
 __global__ __launch_bounds__(256) void sort_scan_tiles_kernel(int32_t* __restrict__ cnt,
                                                              int32_t* __restrict__ totals, int nb,
-                                                             int ntiles, int64_t nbins_total) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                                             int ntiles, int64_t nbins_total,
+                                                             int64_t blk0) {
+  const int64_t g = (blk0 + blockIdx.x) * blockDim.x + threadIdx.x;
   if (g >= nbins_total) return;
   const int64_t seg = g / nb;
   const int bin = (int)(g % nb);
@@ -202,27 +243,18 @@ __global__ __launch_bounds__(kPrefixThreads) void sort_prefix_kernel(
   }
 }
 
-// One wave per (segment, tile).  The tile's keys are first loaded into
-// registers (kScatterBatches loads in flight per lane), then ranked 64 at a
-// time in position order; each key's slot is its bucket's running offset (LDS)
-// plus its rank among the equal keys of lower lanes.  The lanes holding equal
-// keys are found
-//   MASK:  through LDS -- every lane ORs its lane bit into its bucket's 64-bit
-//          mask, reads the mask back (a wave's LDS operations take effect in
-//          order, so the read sees the whole batch), and the group's last lane
-//          advances the bucket's offset and clears the mask (B <= 2048);
-//   else:  by intersecting the ballots of every key bit.
+// One wave per (segment, tile) (B > 2048).  The tile's keys are first loaded
+// into registers (kScatterBatches loads in flight per lane), then ranked 64 at
+// a time in position order; each key's slot is its bucket's running offset
+// (LDS) plus its rank among the equal keys of lower lanes, found by
+// intersecting the ballots of every key bit.
 constexpr int kScatterBatches = 32;   // keys taken 32 batches of 64 at a time
-constexpr int kMaskMatchMaxBuckets = 2048;
 
-template <bool MASK>
 __global__ __launch_bounds__(64) void sort_scatter_kernel(
     const int32_t* __restrict__ buckets, const int32_t* __restrict__ cnt,
     const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int L, int nb, int nbits, int tile, int ntiles) {
-  extern __shared__ uint64_t smem[];
-  uint64_t* mask = smem;                                              // [nb] (MASK)
-  int32_t* run = MASK ? reinterpret_cast<int32_t*>(smem + nb) : reinterpret_cast<int32_t*>(smem);
+  extern __shared__ int32_t run[];   // [nb] running slot of each bucket
   const int lane = lane_id();
   // each XCD scatters whole segments, so a segment's perm lines fill up in one
   // L2 before they are written back
@@ -249,10 +281,7 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int i = i0 + kWave * u + lane;
-      if (i < nb) {
-        run[i] = bv[u] + pv[u];
-        if (MASK) mask[i] = 0;
-      }
+      if (i < nb) run[i] = bv[u] + pv[u];
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -270,34 +299,18 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
       const int i = i0 + lane;
       const bool valid = i < hi;
       const int k = valid ? clamp_bucket(key[b], nb) : 0;
-      uint64_t peers;
-      int32_t start = 0;
-      if (MASK) {
-        if (valid) __hip_atomic_fetch_or(&mask[k], 1ull << lane, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-        __builtin_amdgcn_wave_barrier();
-        peers = 0;
-        if (valid) {
-          peers = __hip_atomic_load(&mask[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          start = run[k];
-        }
-      } else {
-        peers = __ballot(valid);
-        for (int bit = 0; bit < nbits; ++bit) {
-          const bool set = (k >> bit) & 1;
-          const uint64_t ones = __ballot(set);
-          peers &= set ? ones : ~ones;
-        }
-        start = valid ? run[k] : 0;
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (k >> bit) & 1;
+        const uint64_t ones = __ballot(set);
+        peers &= set ? ones : ~ones;
       }
+      const int32_t start = valid ? run[k] : 0;
       const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
       const int n = __popcll(peers);
       __builtin_amdgcn_wave_barrier();
-      if (valid && rank == n - 1) {
-        run[k] = start + n;
-        if (MASK) __hip_atomic_store(&mask[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
+      if (valid && rank == n - 1) run[k] = start + n;
       __builtin_amdgcn_wave_barrier();
       if (valid) {
         const int32_t slot = start + rank;
@@ -308,15 +321,265 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide tiles (B <= 2048).  One workgroup of W waves per (segment, tile of
+// W * 64 * nbat keys, nbat <= 32 batches of 64 per wave, at most 16,384 keys).
+//   1. each wave ranks its own nbat batches in position order: equal keys of
+//      a batch are found through the wave's own per-bucket LDS masks, and a
+//      key's rank is the wave's running count of its bucket plus its rank
+//      among the equal keys of lower lanes;
+//   2. the per-wave counts become per-wave exclusive prefixes; the tile's
+//      bucket starts are a block scan of the tile's counts, and the global
+//      slot of the tile's first key of bucket b (bucket base plus the counts
+//      of the segment's earlier tiles, both from the count table) is kept
+//      as delta[b] = that slot - start[b];
+//   3. every key's tile-local sorted index q goes into LDS (stage[q] = its
+//      tile-local position and bucket), and inv_perm is written at once, in
+//      position order (coalesced);
+//   4. perm is written from the stage in sorted order: consecutive threads
+//      write consecutive slots wherever a bucket's run in the tile continues,
+//      instead of one scattered 4-byte store per key.
+// The count table comes from sort_wide_count_kernel (one launch before).
+// NBMAX: the largest bucket count of the instance (per-wave tables in LDS).
+constexpr int kWideMaxBatches = 32;
+constexpr int kWidePosBits = 14;          // tile-local positions < 2^14
+constexpr int kWideMaxTile = 1 << kWidePosBits;
+constexpr int kWideCountThreads = 1024;
+
+__global__ __launch_bounds__(kWideCountThreads) void sort_wide_count_kernel(
+    const int32_t* __restrict__ buckets, int32_t* __restrict__ cnt, int L, int nb, int tile,
+    int ntiles) {
+  __shared__ int32_t hist[kWideMaxBuckets];
+  const int64_t seg = blockIdx.x / ntiles;
+  const int t = blockIdx.x % ntiles;
+  for (int i = threadIdx.x; i < nb; i += kWideCountThreads) hist[i] = 0;
+  __syncthreads();
+  const int lo = t * tile;
+  const int hi = min(L, lo + tile);
+  const int32_t* bk = buckets + seg * L;
+  // sixteen keys per thread requested before any is counted (clamped indices)
+  for (int i0 = lo; i0 < hi; i0 += kWideCountThreads * 16) {
+    int32_t k[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) k[u] = bk[min(i0 + kWideCountThreads * u + (int)threadIdx.x, hi - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i0 + kWideCountThreads * u + (int)threadIdx.x < hi)
+        atomicAdd(&hist[clamp_bucket(k[u], nb)], 1);
+  }
+  __syncthreads();
+  int32_t* out = cnt + (seg * ntiles + t) * (int64_t)nb;
+  for (int i = threadIdx.x; i < nb; i += kWideCountThreads) out[i] = hist[i];
+}
+
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+template <int W, int NBMAX>
+__global__ __launch_bounds__(kWave * W) void sort_wide_scatter_kernel(
+    const int32_t* __restrict__ buckets, const int32_t* __restrict__ cnt,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, int L, int nb, int tile,
+    int ntiles, int nbat) {
+  constexpr int kNbMax = NBMAX;                    // largest bucket count
+  constexpr int kThreads = kWave * W;
+  // masks [W][kNbMax] during ranking; afterwards the stage [tile] (aliased)
+  __shared__ __attribute__((aligned(16))) uint64_t region[W * kNbMax];
+  __shared__ int32_t cw_all[W * kNbMax];            // per-wave counts, then prefixes
+  __shared__ int32_t bstart[kNbMax], delta[kNbMax], total[kNbMax];
+  __shared__ int32_t part[2 * W];
+  // the stage (tile-local sorted positions) fits the mask region: tiles of
+  // at most 2 * W * NBMAX keys
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid >> 6;
+  // each XCD takes a contiguous range of (segment, tile): the runs of
+  // neighbouring tiles of one segment fill the same perm lines in one L2
+  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t seg = blk / ntiles;
+  const int t = (int)(blk % ntiles);
+  const int lo = t * tile;
+  const int hi = min(L, lo + tile);
+  const int32_t* bk = buckets + seg * L;
+  uint64_t* mask = region + w * nb;
+  int32_t* cw = cw_all + w * nb;
+  for (int i = lane; i < nb; i += kWave) {
+    mask[i] = 0;
+    cw[i] = 0;
+  }
+  // batch j of wave w: tile positions (w * nbat + j) * 64 + lane; the loads
+  // are issued together (clamped into the tile; a batch past the tile's end
+  // is skipped whole, L being a multiple of 64)
+  const int wlo = lo + w * nbat * kWave;
+  int key[kWideMaxBatches], rk[kWideMaxBatches];
+#pragma unroll
+  for (int j = 0; j < kWideMaxBatches; ++j)
+    key[j] = bk[min(wlo + min(j, nbat - 1) * kWave + lane, hi - 1)];
+#pragma unroll
+  for (int j = 0; j < kWideMaxBatches; ++j) key[j] = clamp_bucket(key[j], nb);
+  __builtin_amdgcn_wave_barrier();
+
+  // 1. ranks inside the wave, batch by batch in position order.  A wave's LDS
+  // operations take effect in order, so each lane's read of its bucket's mask
+  // sees the bits of the whole batch.
+#pragma unroll
+  for (int j = 0; j < kWideMaxBatches; ++j) {
+    if (j >= nbat || wlo + j * kWave >= hi) continue;   // uniform
+    const int k = key[j];
+    __hip_atomic_fetch_or(&mask[k], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t peers = __hip_atomic_load(&mask[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int c = cw[k];
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+    const int n = __popcll(peers);
+    rk[j] = c + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (rank == n - 1) {
+      cw[k] = c + n;
+      __hip_atomic_store(&mask[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // 2. thread tid owns buckets [tid * per, tid * per + per)
+  const int per = (nb + kThreads - 1) / kThreads;
+  const int32_t* ct = cnt + seg * (int64_t)ntiles * nb;
+  int my_tc = 0, my_tot = 0;
+  for (int q = 0; q < per; ++q) {
+    const int b = tid * per + q;
+    if (b >= nb) break;
+    int run = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) {
+      const int v = cw_all[w2 * nb + b];
+      cw_all[w2 * nb + b] = run;
+      run += v;
+    }
+    // the counts of b in every tile of the segment, eight loads in flight
+    int pre = 0, tot = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ct[(int64_t)min(t0 + u, ntiles - 1) * nb + b];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t2 = t0 + u;
+        pre += t2 < t ? v[u] : 0;
+        tot += t2 < ntiles ? v[u] : 0;
+      }
+    }
+    bstart[b] = run;   // for now: the tile's count of b
+    delta[b] = pre;    // for now: the counts of b in the segment's earlier tiles
+    total[b] = tot;
+    my_tc += run;
+    my_tot += tot;
+  }
+  const int inc_tc = wave_inclusive_sum(my_tc);
+  const int inc_tot = wave_inclusive_sum(my_tot);
+  if (lane == kWave - 1) {
+    part[w] = inc_tc;
+    part[W + w] = inc_tot;
+  }
+  __syncthreads();
+  int run_tc = inc_tc - my_tc, run_tot = inc_tot - my_tot;
+#pragma unroll
+  for (int w2 = 0; w2 < W; ++w2) {
+    if (w2 < w) {
+      run_tc += part[w2];
+      run_tot += part[W + w2];
+    }
+  }
+  for (int q = 0; q < per; ++q) {
+    const int b = tid * per + q;
+    if (b >= nb) break;
+    const int c = bstart[b], pre = delta[b], tot = total[b];
+    bstart[b] = run_tc;
+    delta[b] = run_tot + pre - run_tc;   // bucket base + earlier tiles - tile start
+    run_tc += c;
+    run_tot += tot;
+  }
+  __syncthreads();
+
+  // 3. tile-local sorted index of every key: stage it, write inv_perm
+  int32_t* stage = reinterpret_cast<int32_t*>(region);
+  int32_t* ip = inv_perm + seg * L;
+#pragma unroll
+  for (int j = 0; j < kWideMaxBatches; ++j) {
+    if (j >= nbat || wlo + j * kWave >= hi) continue;   // uniform
+    const int k = key[j];
+    const int q = bstart[k] + cw[k] + rk[j];
+    const int i = wlo + j * kWave + lane;
+    stage[q] = (i - lo) | (k << kWidePosBits);
+    ip[i] = delta[k] + q;
+  }
+  __syncthreads();
+
+  // 4. perm in sorted order, runs of consecutive slots per bucket
+  int32_t* pm = perm + seg * L;
+  const int n = hi - lo;
+  for (int q0 = 0; q0 < n; q0 += kThreads * 4) {
+    int e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = stage[min(q0 + kThreads * u + tid, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + kThreads * u + tid;
+      if (q < n) {
+        const int k = e[u] >> kWidePosBits;
+        pm[clamp_index(delta[k] + q, L)] = lo + (e[u] & (kWideMaxTile - 1));
+      }
+    }
+  }
+}
+
+template <int W, int NBMAX>
+static void launch_wide_scatter(dim3 grid, hipStream_t stream, const int32_t* buckets,
+                                const int32_t* cnt, int32_t* perm, int32_t* inv_perm, int L,
+                                int nb, int tile, int ntiles, int nbat) {
+  hipLaunchKernelGGL((sort_wide_scatter_kernel<W, NBMAX>), grid, dim3(kWave * W), 0, stream,
+                     buckets, cnt, perm, inv_perm, L, nb, tile, ntiles, nbat);
+}
+
 hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, int32_t* inv_perm,
                        void* workspace, hipStream_t stream) {
   const int64_t S = s.segments();
   const int tile = sort_tile(s);
   const int ntiles = (int)sort_tiles(s);
   const int nb = s.buckets;
+  int32_t* cnt = static_cast<int32_t*>(workspace);
+  if (nb <= kWideMaxBuckets) {
+    const WidePlan p = wide_plan(s);
+    const dim3 grid((unsigned)(S * ntiles));
+    hipLaunchKernelGGL(sort_wide_count_kernel, grid, dim3(kWideCountThreads), 0, stream, buckets,
+                       cnt, s.len, nb, tile, ntiles);
+    if (p.nbmax == 256 && p.waves == 8)
+      launch_wide_scatter<8, 256>(grid, stream, buckets, cnt, perm, inv_perm, s.len, nb, tile,
+                                  ntiles, p.nbat);
+    else if (p.nbmax == 256)
+      launch_wide_scatter<4, 256>(grid, stream, buckets, cnt, perm, inv_perm, s.len, nb, tile,
+                                  ntiles, p.nbat);
+    else if (p.nbmax == 1024 && p.waves == 8)
+      launch_wide_scatter<8, 1024>(grid, stream, buckets, cnt, perm, inv_perm, s.len, nb, tile,
+                                   ntiles, p.nbat);
+    else if (p.nbmax == 1024)
+      launch_wide_scatter<4, 1024>(grid, stream, buckets, cnt, perm, inv_perm, s.len, nb, tile,
+                                   ntiles, p.nbat);
+    else
+      launch_wide_scatter<4, 2048>(grid, stream, buckets, cnt, perm, inv_perm, s.len, nb, tile,
+                                   ntiles, p.nbat);
+    return hipGetLastError();
+  }
   int nbits = 0;
   while ((1 << nbits) < nb) ++nbits;
-  int32_t* cnt = static_cast<int32_t*>(workspace);
   const size_t cnt_bytes = ((size_t)S * ntiles * nb * sizeof(int32_t) + 255) & ~(size_t)255;
   int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cnt_bytes);
   const size_t lds = (size_t)nb * sizeof(int32_t);
@@ -329,18 +592,16 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
   } else {
     hipLaunchKernelGGL(sort_count_kernel, dim3((unsigned)(S * ntiles)), dim3(256), lds, stream,
                        buckets, cnt, s.len, nb, tile, ntiles);
+    // one thread per (segment, bucket), in launch pieces
     const int64_t nbins = S * nb;
-    hipLaunchKernelGGL(sort_scan_tiles_kernel, dim3((unsigned)((nbins + 255) / 256)), dim3(256),
-                       0, stream, cnt, base, nb, ntiles, nbins);
+    const int64_t nblk = (nbins + 255) / 256;
+    for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks)
+      hipLaunchKernelGGL(sort_scan_tiles_kernel, dim3((unsigned)std::min(kMaxBlocks, nblk - b0)),
+                         dim3(256), 0, stream, cnt, base, nb, ntiles, nbins, b0);
     hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base, nb);
   }
-  if (nb <= kMaskMatchMaxBuckets)
-    hipLaunchKernelGGL(sort_scatter_kernel<true>, dim3((unsigned)(S * ntiles)), dim3(64),
-                       (size_t)nb * (sizeof(uint64_t) + sizeof(int32_t)), stream, buckets, cnt,
-                       base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
-  else
-    hipLaunchKernelGGL(sort_scatter_kernel<false>, dim3((unsigned)(S * ntiles)), dim3(64), lds,
-                       stream, buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)(S * ntiles)), dim3(64), lds, stream,
+                     buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
   return hipGetLastError();
 }
 

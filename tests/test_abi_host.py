@@ -101,20 +101,36 @@ def test_workspace_too_small():
         B.LSH_ERR_WORKSPACE_TOO_SMALL
 
 
+def _sort_tile(S, L, nb):
+    """The sort's tile: for B <= 2048 the largest of 1,024 .. 16,384 keys (at
+    most 4,096 for B <= 256 and 8,192 for B > 1,024) that leaves at least 256
+    tiles in all; otherwise max(1024, B) doubled up to 4,096 while there would
+    be more than 1,024 tiles."""
+    if nb <= 2048:
+        cap = 4096 if nb <= 256 else (16384 if nb <= 1024 else 8192)
+        tile = 1024
+        while tile < cap and S * -(-L // (2 * tile)) >= 256:
+            tile *= 2
+        return tile
+    tile = 1024
+    while tile < nb:
+        tile *= 2
+    while tile < 4096 and S * L // tile > 1024:
+        tile *= 2
+    return tile
+
+
 def test_workspace_bytes_cover_the_count_tables():
     for L, nb, R in ((1024, 16, 1), (4096, 64, 2), (65536, 1024, 8), (524288, 8192, 2),
-                     (2048, 16384, 1)):
+                     (2048, 16384, 1), (16384, 2048, 4), (192, 38, 3)):
         c = cfg(seq_len=L, n_buckets=nb, n_rounds=R, heads=4)
         S = 4 * R
-        # tiles of max(1024, B) keys, doubled up to 4096 while there would
-        # be more than 1024 of them
-        tile = 1024
-        while tile < nb:
-            tile *= 2
-        while tile < 4096 and S * L // tile > 1024:
-            tile *= 2
-        tiles = -(-L // tile)
-        assert B.lsh_sort_workspace_bytes(c) >= 4 * S * nb * (tiles + 1)
+        tiles = -(-L // _sort_tile(S, L, nb))
+        need = 4 * S * nb * tiles + (4 * S * nb if nb > 2048 else 0)   # counts (+ bases)
+        assert B.lsh_sort_workspace_bytes(c) >= need
+    # the headline shape: 16,384-key tiles, 1 MiB of counts
+    assert B.lsh_sort_workspace_bytes(cfg(seq_len=65536, n_buckets=1024, n_rounds=8,
+                                          heads=8)) == 64 * 4 * 1024 * 4
 
 
 def test_per_round_buffer_size():
