@@ -7,12 +7,14 @@
 // two largest |x R_j| as packed keys (magnitude bits with the direction's
 // offset in its tile in the low mantissa bits) and the tile of the largest.
 // A row is accepted only when the gap between the two best candidates exceeds
-// twice a proven bound on the fp32 accumulation error (plus the fp64 rounding
-// of the defining sum), so that its bucket is provably the one of the fp64
+// twice a bound on the fp32 accumulation error (plus the fp64 rounding of the
+// defining sum), so that its bucket is provably the one of the fp64
 // definition; the winner's sign then comes from an exact-sign dot product.
-// Other rows are listed in LDS and recomputed in fp64, in the defining order,
-// by the whole workgroup once its rounds are done.  fp32 inputs are scored in
-// fp64 directly.
+// Other rows are marked (with a lower bound on their best score) and settled
+// by a second kernel, which scores them again with per-direction error bounds
+// and recomputes the few directions that can reach the maximum in fp64, in
+// the defining order.  fp32 inputs are
+// scored in fp64 directly.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -73,198 +75,6 @@ __device__ int exact_bucket(const double* x, const T* rot_hr, int half) {
 }
 
 // ---------------------------------------------------------------------------
-// Rows the fp32 margin cannot certify are settled in fp64 by the whole
-// workgroup once its rounds are done: thread t owns directions t, t + 256,
-// ... of the row's rotation and loads each as 8 x 16 B.  Each direction's sum
-// runs k ascending from 0.0 (the products of two bf16 values are exact, so
-// the fused multiply-add rounds exactly like the defining sum).
-constexpr int kSettleCap = 1024;   // rows listed per workgroup; the rest are marked in place
-
-__device__ __forceinline__ void settle_take(double s, int j, double& best, int& besti) {
-  if (s > best || (s == best && j < besti)) { best = s; besti = j; }
-}
-
-__device__ __forceinline__ double dot_fp64(const uint4 (&r)[8], const uint32_t (&xw)[kHeadDim / 2]) {
-  double acc = 0.0;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t xv = xw[4 * c + e];
-      acc = fma((double)bf16lo(xv), (double)bf16lo(w[e]), acc);
-      acc = fma((double)bf16hi(xv), (double)bf16hi(w[e]), acc);
-    }
-  }
-  return acc;
-}
-
-__device__ __forceinline__ void load_dir(uint4 (&r)[8], const uint16_t* rhr, int j) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) r[c] = load16(rhr + (size_t)j * kHeadDim + 8 * c);
-}
-
-struct SettleLds {
-  double wbest[2][kHashWaves];   // per-wave winners, double-buffered by row parity
-  int wbesti[2][kHashWaves];
-  float wlow[2][kHashWaves];     // per-wave lower bounds on the best |score|
-};
-
-// fp32 score x.R_j (exact bf16 products, fp32 sums) and an upper bound e_j
-// on its distance from the definition: the fp32 bound 64 * 2^-22 * 1.01 *
-// sum_k |x_k R_kj| of the main loop (the sum itself taken in fp32, with 2^-10
-// of slack), plus flush-to-zero slack.
-__device__ __forceinline__ void score_fp32(const uint4 (&r)[8], const uint32_t (&xw)[kHeadDim / 2],
-                                           float& s, float& ej) {
-  float acc = 0.f, aacc = 0.f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xw[4 * c + e]),
-                                            __builtin_bit_cast(bf16x2, w[e]), acc, false);
-      aacc = __builtin_amdgcn_fdot2_f32_bf16(
-          __builtin_bit_cast(bf16x2, xw[4 * c + e] & 0x7fff7fffu),
-          __builtin_bit_cast(bf16x2, w[e] & 0x7fff7fffu), aacc, false);
-    }
-  }
-  s = acc;
-  ej = aacc * (64.0f * 0x1p-22f * 1.01f * (1.0f + 0x1p-10f)) + 0x1p-117f;
-}
-
-// Row e's bucket: the first maximum among the four waves' winners.
-__device__ __forceinline__ void settle_pick(const SettleLds& sl, int e, uint32_t ent,
-                                            int32_t* out_bh, int tok0, int L) {
-  double best = sl.wbest[e & 1][0];
-  int besti = sl.wbesti[e & 1][0];
-#pragma unroll
-  for (int w = 1; w < kHashWaves; ++w) settle_take(sl.wbest[e & 1][w], sl.wbesti[e & 1][w], best, besti);
-  out_bh[(size_t)(ent >> 8) * L + tok0 + (int)(ent & 255u)] = besti;
-}
-
-// Settles list[0..n): entry (r << 8) | t is token tok0 + t of round r, whose
-// x is row t of xsm (bf16, kRowStride apart).  Called by all threads of the
-// workgroup; every listed row is written when it returns.
-//
-// Two passes per row.  The first scores every direction in fp32 with its
-// bound e_j, and the workgroup takes the largest lower bound |s_j| - e_j of
-// the best |score|.  Only directions whose upper bound |s_j| + e_j reaches
-// it can hold the maximum of [xR; -xR] or tie with it; the second pass
-// recomputes those in fp64 in the defining order and keeps the first
-// maximum.  Each thread remembers its best upper bound (and direction) and
-// its second best; when the second best also reaches the lower bound (rare)
-// the thread scans its directions again.
-// Inlined: as a called function its register saves would raise the kernel's
-// register count for the main loop as well.
-__device__ __forceinline__ void settle_rows(const uint32_t* list, int n, const uint16_t* xsm,
-                                            const uint16_t* rot_h, int32_t* out_bh, int tok0,
-                                            int L, int half, SettleLds& sl) {
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int iters = (half + kHashTokWG - 1) / kHashTokWG;
-  const size_t rot_round = (size_t)half * kHeadDim;
-  for (int e = 0; e < n; ++e) {
-    const uint32_t ent = list[e];
-    const int t = (int)(ent & 255u);
-    const uint16_t* rhr = rot_h + (size_t)(ent >> 8) * rot_round;
-    uint32_t xw[kHeadDim / 2];   // x as packed bf16 pairs
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 u = *reinterpret_cast<const uint4*>(xsm + t * kRowStride + 8 * c);
-      xw[4 * c] = u.x;
-      xw[4 * c + 1] = u.y;
-      xw[4 * c + 2] = u.z;
-      xw[4 * c + 3] = u.w;
-    }
-
-    // pass 1: fp32 scores; the next direction's row is in flight meanwhile
-    float low = -INFINITY, up1 = -INFINITY, up2 = -INFINITY;
-    int j1 = -1;
-    uint4 rv[8];
-    if ((int)threadIdx.x < half) load_dir(rv, rhr, threadIdx.x);
-    for (int it = 0; it < iters; ++it) {
-      const int j = threadIdx.x + it * kHashTokWG;
-      uint4 rn[8];
-      const bool next = j + kHashTokWG < half;
-      if (next) load_dir(rn, rhr, j + kHashTokWG);
-      if (j < half) {
-        float sc, ej;
-        score_fp32(rv, xw, sc, ej);
-        const float up = fabsf(sc) + ej;
-        low = fmaxf(low, fabsf(sc) - ej);
-        if (up > up1) {
-          up2 = up1;
-          up1 = up;
-          j1 = j;
-        } else {
-          up2 = fmaxf(up2, up);
-        }
-      }
-      if (next) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) rv[c] = rn[c];
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) low = fmaxf(low, __shfl_xor(low, off));
-    if (lane == 0) sl.wlow[e & 1][wave] = low;
-    __syncthreads();
-    if (threadIdx.x == 0 && e > 0) settle_pick(sl, e - 1, list[e - 1], out_bh, tok0, L);
-#pragma unroll
-    for (int w = 0; w < kHashWaves; ++w) low = fmaxf(low, sl.wlow[e & 1][w]);
-
-    // pass 2: the directions that can reach the maximum, in fp64
-    double best = -INFINITY;
-    int besti = INT_MAX;
-    if (j1 >= 0 && up1 >= low) {
-      // opaque to the compiler, so the widened x is not hoisted (64 doubles
-      // would not fit beside the main loop's registers)
-#pragma unroll
-      for (int q = 0; q < kHeadDim / 2; ++q) asm volatile("" : "+v"(xw[q]));
-      uint4 r1[8];
-      load_dir(r1, rhr, j1);
-      const double sd = dot_fp64(r1, xw);
-      settle_take(sd, j1, best, besti);
-      settle_take(-sd, j1 + half, best, besti);
-    }
-    if (up2 >= low) {
-      for (int it = 0; it < iters; ++it) {
-        const int j = threadIdx.x + it * kHashTokWG;
-        if (j >= half || j == j1) continue;
-        uint4 r2[8];
-        load_dir(r2, rhr, j);
-        float sc, ej;
-        score_fp32(r2, xw, sc, ej);
-        if (fabsf(sc) + ej >= low) {
-#pragma unroll
-          for (int q = 0; q < kHeadDim / 2; ++q) asm volatile("" : "+v"(xw[q]));
-          const double sd = dot_fp64(r2, xw);
-          settle_take(sd, j, best, besti);
-          settle_take(-sd, j + half, best, besti);
-        }
-      }
-    }
-    // larger value wins, lower index on equal values: a total order, so any
-    // reduction tree finds the first maximum
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const double ob = __shfl_xor(best, off);
-      const int oi = __shfl_xor(besti, off);
-      settle_take(ob, oi, best, besti);
-    }
-    if (lane == 0) {
-      sl.wbest[e & 1][wave] = best;
-      sl.wbesti[e & 1][wave] = besti;
-    }
-    // the four waves' winners of this row are combined after the next row's
-    // first barrier (or the barrier below after the last row)
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && n > 0) settle_pick(sl, n - 1, list[n - 1], out_bh, tok0, L);
-}
-
-// ---------------------------------------------------------------------------
 // Keys: the fp32 score with its 5 low mantissa bits replaced by the direction's
 // offset inside its 32-direction tile (the lane-half bit 4 of that offset is
 // added after the halves merge).  Magnitude keys |key| order like |score| up to
@@ -300,15 +110,13 @@ __device__ __forceinline__ void stage_store(uint16_t* dst, const uint4 (&buf)[4]
   }
 }
 
-__global__ __launch_bounds__(256) void hash_bf16_kernel(
+// At most 128 VGPRs (the second bound): four waves per SIMD hide more of the
+// matrix-core and LDS latency than three with more registers each.
+__global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
     const uint16_t* __restrict__ qk, const uint16_t* __restrict__ rot,
-    int32_t* __restrict__ buckets, uint32_t* __restrict__ fallback_rows, int heads, int L,
-    int half, int rounds) {
+    int32_t* __restrict__ buckets, int heads, int L, int half, int rounds) {
   __shared__ __attribute__((aligned(16))) uint16_t rs[2][kStageRows * kRowStride];
   __shared__ float gram_part[kHashWaves];
-  __shared__ uint32_t settle_list[kSettleCap];
-  __shared__ int settle_n, settle_over;
-  __shared__ SettleLds settle_lds;
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -321,13 +129,6 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
   const int h = (int)(bh % heads);
   const int tok_wave = bx * kHashTokWG + wave * kHashTokWave;
   const uint16_t* xbase = qk + bh * (size_t)L * kHeadDim;
-  const uint16_t* rot_h = rot + (size_t)h * rounds * half * kHeadDim;
-  int32_t* out_bh = buckets + bh * rounds * (size_t)L;
-  const int tok0 = bx * kHashTokWG;
-  if (threadIdx.x == 0) {
-    settle_n = 0;
-    settle_over = 0;
-  }
 
   // B operand (x^T, k x token): lane holds x[token = lane%32][k = 8*(lane/32) + 16*ks + 0..7].
   // All eight pieces are requested before any is used.  The descriptor covers
@@ -495,55 +296,290 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
       const int bucket = pos ? (int)jstar : (int)jstar + half;
 
       const int tok = tok_wave + nb * 32 + (lane & 31);
-      // rows the fp32 margin cannot certify are listed and settled in fp64
-      // later, so no wave waits on them inside the round
-      if (lane < 32 && tok < L) {
-        if (cert) {
-          bout[tok] = bucket;
-        } else {
-          const int k = atomicAdd(&settle_n, 1);
-          if (k < kSettleCap) {
-            settle_list[k] = ((uint32_t)r << 8) | (uint32_t)(tok - tok0);
-          } else {   // list full: marked in place, found again below
-            bout[tok] = -1;
-            settle_over = 1;
+      // Rows the fp32 margin cannot certify are settled by hash_settle_kernel,
+      // so no wave waits on them.  Such a row's entry holds the bitwise
+      // complement of a lower bound on its best |x.R_j| (negative: the bound
+      // is >= 0): lower1 <= |t_j*| <= |s_j*| + E for the defining sum s_j*,
+      // less 2^-20 of lower1 for the rounding of this subtraction.
+      const float lower = fmaxf(lower1 - E - lower1 * 0x1p-20f, 0.0f);
+      if (lane < 32 && tok < L) bout[tok] = cert ? bucket : (int)~__float_as_uint(lower);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Settling the rows the main kernel could not certify.  Their entries hold
+// ~bits(b) for a lower bound b >= 0 on the row's best |x.R_j| (negative
+// values; certified buckets are >= 0).  One workgroup per (segment, range of
+// kSettleRange rows) lists the marked rows of its range and settles them
+// kSettleBlock at a time against the segment's rotation, so that each
+// direction row is read once per block of rows instead of once per row:
+//   1. on the matrix cores (v_mfma_f32_16x16x32_bf16: 16 directions x 16
+//      rows per product, exact bf16 products and fp32 sums), the score t_j of
+//      every direction and A_j = sum_k |x_k| |R_kj| from the products of the
+//      absolute values.  e_j = 64 * 2^-22 * 1.01 * (1 + 2^-10) * A_j + 2^-116
+//      bounds |t_j - s_j| for the defining fp64 sum s_j: the main loop's
+//      bound with sum_k |x_k R_kj| in place of |x| max_j |R_j| (1 + 2^-10
+//      covers A_j's own rounding, 2^-116 the flush-to-zero slack of both
+//      sums).  Only directions with |t_j| + e_j >= b can hold the maximum of
+//      [x R ; -x R] or tie with it; they are listed in LDS;
+//   2. the listed directions are recomputed in fp64 in the defining order (k
+//      ascending from 0; the products of two bf16 values are exact, so a
+//      fused multiply-add rounds like the defining sum), and each row keeps
+//      the first maximum (lowest index among equal values): an LDS maximum
+//      over the values (nonnegative doubles order like their bit patterns),
+//      then an LDS minimum over the indices that reach it.  A block with more
+//      candidates than the list holds (rows whose scores all tie, such as
+//      all-zero x) is settled by computing every direction in fp64.
+// Each wave takes every fourth 16-direction tile, with the next kSettleDepth
+// tiles of its share in flight.
+constexpr int kSettleRange = 8192;    // rows scanned per workgroup
+constexpr int kSettleList = 2048;     // rows listed per pass (more: another pass)
+constexpr int kSettleBlock = 16;      // rows settled together (one MFMA column block)
+constexpr int kSettleThreads = 256;
+constexpr int kSettleDepth = 8;       // tiles in flight per wave
+constexpr int kSettleCands = 2048;    // listed candidate (row, direction) pairs per block
+constexpr float kSettleErr = 64.0f * 0x1p-22f * 1.01f * (1.0f + 0x1p-10f);
+
+// x . R_j in fp64, k ascending from 0.0 (the defining sum).
+__device__ __forceinline__ double dot_fp64(const uint4 (&r)[8], const uint32_t (&xw)[kHeadDim / 2]) {
+  double acc = 0.0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t xv = xw[4 * c + e];
+      acc = fma((double)bf16lo(xv), (double)bf16lo(w[e]), acc);
+      acc = fma((double)bf16hi(xv), (double)bf16hi(w[e]), acc);
+    }
+  }
+  return acc;
+}
+
+// Row `row`'s candidate pair +s_j (index j) and -s_j (index j + half) in
+// fp64: the larger value |s_j| as order-preserving bits, offered to the row's
+// maximum; returns the index that holds it (j when s_j >= 0).
+__device__ __forceinline__ uint64_t settle_value(const uint16_t* rhr, int j, int half,
+                                                 const uint16_t* xrow, int& index) {
+  uint4 rv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) rv[c] = load16(rhr + (size_t)j * kHeadDim + 8 * c);
+  uint32_t xw[kHeadDim / 2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint4 u = load16(xrow + 8 * c);
+    xw[4 * c] = u.x;
+    xw[4 * c + 1] = u.y;
+    xw[4 * c + 2] = u.z;
+    xw[4 * c + 3] = u.w;
+  }
+  const double sd = dot_fp64(rv, xw);
+  index = sd < 0.0 ? j + half : j;
+  return (uint64_t)__double_as_longlong(fabs(sd));
+}
+
+__device__ __forceinline__ bf16x8 abs_bf16x8(bf16x8 v) {
+  uint4 u = __builtin_bit_cast(uint4, v);
+  u.x &= 0x7fff7fffu;
+  u.y &= 0x7fff7fffu;
+  u.z &= 0x7fff7fffu;
+  u.w &= 0x7fff7fffu;
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// A operand of tile t (directions 16 t .. 16 t + 15): lane l holds
+// R[direction 16 t + l % 16][k = 8 (l / 16) + 32 ks .. + 7] for ks = 0, 1.
+// Directions past half (and tiles past the last) read as zero.
+struct SettleTile {
+  bf16x8 a[2];
+};
+
+__device__ __forceinline__ void settle_load(SettleTile& tl, __amdgpu_buffer_rsrc_t rsrc, int t) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    tl.a[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    rsrc, (uint32_t)((16 * t + (lane & 15)) * kHeadDim * 2 + (lane >> 4) * 16 + ks * 64),
+                    0, 0));
+}
+
+// acc[i] = t_j, aacc[i] = A_j of direction 16 t + 4 (l / 16) + i and block row l % 16.
+__device__ __forceinline__ void settle_scores(const SettleTile& tl, const bf16x8 (&xf)[2],
+                                              const bf16x8 (&xa)[2], f32x4& acc, f32x4& aacc) {
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  aacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl.a[ks], xf[ks], acc, 0, 0, 0);
+    aacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abs_bf16x8(tl.a[ks]), xa[ks], aacc, 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kSettleThreads, 2) void hash_settle_kernel(
+    const uint16_t* __restrict__ qk, const uint16_t* __restrict__ rot,
+    int32_t* __restrict__ buckets, uint32_t* __restrict__ fallback_rows, int heads, int L,
+    int half, int rounds, int nranges, int64_t blk0) {
+  __shared__ int32_t list[kSettleList];
+  __shared__ float lbound[kSettleList];            // the listed rows' lower bounds
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kSettleBlock * kRowStride];
+  __shared__ uint32_t cand[kSettleCands];          // (row << 16) | direction
+  __shared__ uint64_t cval[kSettleCands];          // their fp64 values (bits)
+  __shared__ int cidx[kSettleCands];               // and the indices holding them
+  __shared__ uint64_t rowmax[kSettleBlock];
+  __shared__ int rowidx[kSettleBlock];
+  __shared__ int nlist, ncand;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  // each XCD takes a contiguous range of (segment, row range): its L2 holds
+  // the rotations of few segments
+  const int64_t blk = blk0 + xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t seg = blk / nranges;
+  const int range = (int)(blk % nranges);
+  const int r = (int)(seg % rounds);
+  const int64_t bh = seg / rounds;
+  const int h = (int)(bh % heads);
+  const int lo = range * kSettleRange;
+  const int hi = min(L, lo + kSettleRange);
+  int32_t* bk = buckets + seg * L;
+  const uint16_t* xb = qk + bh * (size_t)L * kHeadDim;
+  const uint16_t* rhr = rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(rhr), (short)0, half * kHeadDim * (int)sizeof(uint16_t), kBufferWord3);
+  const int ntiles = (half + 15) / 16;
+  const int nmine = (ntiles - wave + kHashWaves - 1) / kHashWaves;   // tiles wave + 4 q, q < nmine
+  const int row = lane & 15;          // the block row this lane scores
+  const int dir0 = 4 * (lane >> 4);   // its first direction inside a tile
+  uint32_t settled = 0;
+
+  // Passes of at most kSettleList rows: a pass's rows are no longer marked
+  // when the next pass scans the range (this workgroup's own writes, ordered
+  // by the barriers); a pass that listed every marked row is the last.
+  for (;;) {
+    if (tid == 0) nlist = 0;
+    __syncthreads();
+    {  // the marked rows of the range: every load of a thread in flight at once
+      constexpr int kPer = kSettleRange / kSettleThreads;
+      int32_t v[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) v[u] = bk[min(lo + kSettleThreads * u + tid, hi - 1)];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int i = lo + kSettleThreads * u + tid;
+        if (i < hi && v[u] < 0) {
+          const int k = atomicAdd(&nlist, 1);
+          if (k < kSettleList) {
+            list[k] = i;
+            lbound[k] = __uint_as_float(~(uint32_t)v[u]);
           }
         }
       }
     }
-  }
-  __syncthreads();   // the list is complete and the staging buffer is free
-  const int n = min(settle_n, kSettleCap);
-  if (n == 0) return;
-  // the workgroup's x rows (still in registers) into LDS, for the fp64 pass
-  uint16_t* xsm = &rs[0][0];   // 256 rows of kRowStride
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      store16(&xsm[(wave * kHashTokWave + nb * 32 + (lane & 31)) * kRowStride + 8 * (lane >> 5) + 16 * ks],
-              __builtin_bit_cast(uint4, xf[nb][ks]));
-  __syncthreads();
-  settle_rows(settle_list, n, xsm, rot_h, out_bh, tok0, L, half, settle_lds);
-  uint32_t settled = n;
-  if (settle_over) {
-    // Only when more than kSettleCap rows of this workgroup were uncertain:
-    // collect the rows marked -1 round by round (this workgroup's own
-    // writes, visible after the barrier) and settle them.
-    for (int r = 0; r < rounds; ++r) {
-      if (threadIdx.x == 0) settle_n = 0;
+    __syncthreads();
+    const int n = min(nlist, kSettleList);
+    const bool more = nlist > kSettleList;   // rows left for another pass
+    if (n == 0) break;
+    settled += n;
+
+    for (int b0 = 0; b0 < n; b0 += kSettleBlock) {
+      const int nrows = min(kSettleBlock, n - b0);
+      if (tid < kSettleBlock * 8) {   // the block's x rows into LDS (rows past nrows zero)
+        const int rr = tid >> 3, piece = tid & 7;
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (rr < nrows) u = load16(xb + (size_t)list[b0 + rr] * kHeadDim + 8 * piece);
+        store16(&xs[rr * kRowStride + 8 * piece], u);
+      }
+      if (tid < kSettleBlock) {
+        rowmax[tid] = 0ull;
+        rowidx[tid] = INT_MAX;
+      }
+      if (tid == 0) ncand = 0;
       __syncthreads();
-      const int tok = tok0 + threadIdx.x;
-      if (tok < L && out_bh[(size_t)r * L + tok] < 0)
-        settle_list[atomicAdd(&settle_n, 1)] = ((uint32_t)r << 8) | threadIdx.x;
+      // B operand: lane l holds x[row l % 16][k = 8 (l / 16) + 32 ks .. + 7]
+      bf16x8 xf[2], xa[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        xf[ks] = as_bf16x8(load16(&xs[row * kRowStride + 8 * (lane >> 4) + 32 * ks]));
+        xa[ks] = abs_bf16x8(xf[ks]);
+      }
+      const bool live = row < nrows;
+      const float lowr = lbound[b0 + min(row, nrows - 1)];
+
+      // 1. the directions that can reach the maximum, listed.  Tiles past the
+      // wave's share read as zero and fall outside [0, half): steps of
+      // kSettleDepth tiles run whole, with no branch between the loads.
+      SettleTile ring[kSettleDepth];
+#pragma unroll
+      for (int d = 0; d < kSettleDepth; ++d) settle_load(ring[d], rsrc, wave + kHashWaves * d);
+      for (int q0 = 0; q0 < nmine; q0 += kSettleDepth) {
+#pragma unroll
+        for (int d = 0; d < kSettleDepth; ++d) {
+          const int q = q0 + d;
+          f32x4 acc, aacc;
+          settle_scores(ring[d], xf, xa, acc, aacc);
+          settle_load(ring[d], rsrc, wave + kHashWaves * (q + kSettleDepth));
+          const int j0 = 16 * (wave + kHashWaves * q) + dir0;
+          uint32_t hit = 0;   // bit i: direction j0 + i can reach the maximum
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = fmaf(aacc[i], kSettleErr, 0x1p-116f);
+            hit |= (live && j0 + i < half && fabsf(acc[i]) + e >= lowr) ? 1u << i : 0u;
+          }
+          if (hit) {   // rare
+            const int k = atomicAdd(&ncand, __popc(hit));
+            int m = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if ((hit >> i) & 1u) {
+                if (k + m < kSettleCands) cand[k + m] = ((uint32_t)row << 16) | (uint32_t)(j0 + i);
+                ++m;
+              }
+            }
+          }
+        }
+      }
       __syncthreads();
-      const int m = settle_n;
-      if (m) settle_rows(settle_list, m, xsm, rot_h, out_bh, tok0, L, half, settle_lds);
-      settled += m;
-      __syncthreads();   // the list and settle_n are rewritten for the next round
+      const int nc = ncand;
+      // 2. fp64 values; each row's largest, then the lowest index holding it
+      if (nc <= kSettleCands) {
+        for (int k = tid; k < nc; k += kSettleThreads) {
+          const int rr = (int)(cand[k] >> 16), j = (int)(cand[k] & 0xffffu);
+          int index;
+          const uint64_t v = settle_value(rhr, j, half, &xs[rr * kRowStride], index);
+          cval[k] = v;
+          cidx[k] = index;
+          atomicMax((unsigned long long*)&rowmax[rr], (unsigned long long)v);
+        }
+        __syncthreads();
+        for (int k = tid; k < nc; k += kSettleThreads) {
+          const int rr = (int)(cand[k] >> 16);
+          if (cval[k] == rowmax[rr]) atomicMin(&rowidx[rr], cidx[k]);
+        }
+      } else {
+        // every direction of every row in fp64 (all scores of some row tie)
+        for (int k = tid; k < nrows * half; k += kSettleThreads) {
+          const int rr = k / half, j = k % half;
+          int index;
+          const uint64_t v = settle_value(rhr, j, half, &xs[rr * kRowStride], index);
+          atomicMax((unsigned long long*)&rowmax[rr], (unsigned long long)v);
+        }
+        __syncthreads();
+        for (int k = tid; k < nrows * half; k += kSettleThreads) {
+          const int rr = k / half, j = k % half;
+          int index;
+          const uint64_t v = settle_value(rhr, j, half, &xs[rr * kRowStride], index);
+          if (v == rowmax[rr]) atomicMin(&rowidx[rr], index);
+        }
+      }
+      __syncthreads();
+      if (tid < nrows) bk[list[b0 + tid]] = rowidx[tid];
+      __syncthreads();   // xs, the lists and the row tables are rewritten next
     }
+    if (!more) break;
   }
-  if (fallback_rows && threadIdx.x == 0 && settled) atomicAdd(fallback_rows, settled);
+  if (fallback_rows && tid == 0 && settled) atomicAdd(fallback_rows, settled);
 }
 
 // fp32 inputs: every row in fp64 (one wave per (token, round) row).
@@ -594,7 +630,14 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
   const dim3 grid((unsigned)((int64_t)(s.len + kHashTokWG - 1) / kHashTokWG * s.heads * s.batch));
   hipLaunchKernelGGL(hash_bf16_kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
-                     fallback_rows, s.heads, s.len, half, s.rounds);
+                     s.heads, s.len, half, s.rounds);
+  const int nranges = (s.len + kSettleRange - 1) / kSettleRange;
+  const int64_t nblk = s.segments() * nranges;
+  for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks)
+    hipLaunchKernelGGL(hash_settle_kernel, dim3((unsigned)std::min(kMaxBlocks, nblk - b0)),
+                       dim3(kSettleThreads), 0, stream, static_cast<const uint16_t*>(qk),
+                       static_cast<const uint16_t*>(rot), buckets, fallback_rows, s.heads, s.len,
+                       half, s.rounds, nranges, b0);
   return hipGetLastError();
 }
 

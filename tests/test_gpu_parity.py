@@ -299,6 +299,26 @@ def test_hash_settles_more_uncertain_rows_than_one_list_holds(B):
     assert int(host(f.fallback_rows)[0]) >= 256 * 8
 
 
+def test_hash_settle_many_rows_and_all_tied_blocks(B):
+    """One segment of 8,192 tokens whose 7,000 all-zero rows tie in every
+    direction: more uncertain rows than one pass of the settle lists (several
+    passes over the range), and blocks whose every direction reaches the
+    bound (settled by computing every direction in fp64); the other rows carry
+    integer ties.  Against the oracle."""
+    L = 8192
+    w = synth.Workload("settle_passes", 1, 1, L, 64, 512, 1, 64, True, True, "bf16", 44)
+    g = np.random.default_rng(45)
+    qk = g.integers(-2, 3, size=(1, 1, L, 64)).astype(np.float32)
+    qk[0, 0, g.permutation(L)[:7000]] = 0.0
+    rot = g.integers(-1, 2, size=(1, 1, 256, 64)).astype(np.float32)
+    inp = {"qk": synth.bf16_bits(qk), "v": synth.bf16_bits(g.standard_normal(qk.shape)),
+           "rot": synth.bf16_bits(rot)}
+    f = run_gpu(B, w, inp)
+    ref = oracle.hash(synth.to_f64(inp["qk"], "bf16"), synth.to_f64(inp["rot"], "bf16"), 512, 1)
+    assert np.array_equal(host(f.buckets), ref)
+    assert int(host(f.fallback_rows)[0]) >= 7000
+
+
 # --------------------------------------------------------------- full size
 # The two largest benchmark shapes in the launch configuration the benchmark
 # times, every output element against the oracle's full fp64 forward: every
