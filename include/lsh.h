@@ -178,10 +178,11 @@ lsh_status lsh_sort_static_scratch(const lsh_config* cfg, const int32_t* buckets
  * cfg->o_format:
  *   LSH_O_F32: o as fp32 [b][H][R][L][d] (bf16 or fp32 inputs).
  *   LSH_O_F16_SCALED (bf16 inputs): a header of 256 fp32 partial maxima of
- *     |v| per (b, h) ([b][H][256], padded to a multiple of 256 bytes), then o
- *     as fp16 [b][H][R][L][d] holding o * 2^-k (round to nearest even).  With
- *     V the largest of the (b, h)'s 256 header values and e the smallest
- *     integer with V < 2^e (e = -126 when V < 2^-126), k = max(e - 15, -100).
+ *     |v| per (b, h) ([b][H][256]) followed by the int32 exponent k of each
+ *     (b, h) ([b][H]), padded to a multiple of 256 bytes, then o as fp16
+ *     [b][H][R][L][d] holding o * 2^-k (round to nearest even).  With V the
+ *     largest of the (b, h)'s 256 partial maxima and e the smallest integer
+ *     with V < 2^e (e = -126 when V < 2^-126), k = max(e - 15, -100).
  *     Each o is a weighted mean of v rows, so every stored |o| * 2^-k stays
  *     within rounding of 2^15.  o is read back as the fp16 value times 2^k: o
  *     rounded to 11 significant bits (bf16 has 8), with no overflow.

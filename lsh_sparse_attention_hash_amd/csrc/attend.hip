@@ -22,7 +22,8 @@
 // written as fp32, or (compact format) as fp16 of o * 2^-k with one
 // power-of-two scale per (batch, head) taken from the largest |v|
 // (vmax_kernel runs first and leaves partial maxima in the header of the
-// output buffer; the fp32 accumulation is unchanged).
+// output buffer; the first workgroup of each head adds k itself to the
+// header for the combine; the fp32 accumulation is unchanged).
 // fp32: one workgroup per chunk, four threads per query, fp32 arithmetic and
 // fp32 output rows.
 #include <limits.h>
@@ -48,6 +49,7 @@ struct AttendArgs {
   const int32_t* perm;
   void* o;               // fp32 rows, or fp16 rows (compact format)
   const float* vpart;    // compact format: partial maxima of |v| per (batch, head)
+  int32_t* hexp;         // compact format: scale exponent k per (batch, head)
   float* lse;
   int rounds, L, nchunks, cpw, runs_per_seg, causal, self_mask;
   int64_t blk0;          // fp32 kernel: first block of this launch piece
@@ -378,8 +380,14 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   const int32_t* bk = a.buckets + seg * a.L;
   const int32_t* pm = a.perm + seg * a.L;
   const int32_t* uk = UNION ? a.ukeys + bh * (int64_t)a.L * a.ukey_stride : nullptr;
-  // scale of the (batch, head)'s fp16 output rows: 2^-k
-  const float oscale = O16 ? pow2f(-o_scale_exponent(head_vmax(a.vpart + bh * kVParts))) : 1.0f;
+  // scale of the (batch, head)'s fp16 output rows: 2^-k; the head's first
+  // workgroup records k for the combine
+  float oscale = 1.0f;
+  if (O16) {
+    const int k = o_scale_exponent(head_vmax(a.vpart + bh * kVParts));
+    oscale = pow2f(-k);
+    if (seg % a.rounds == 0 && run == 0 && threadIdx.x == 0) a.hexp[bh] = k;
+  }
   ChunkRegs g;
   if (c0 > 0) {
     gather_chunk<UNION>(g, load_perm_pair(pm, c0 - 1, a.L), xb, vb, bk, uk, a.ukey_stride);
@@ -638,7 +646,8 @@ __global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ 
 
 size_t o_header_bytes(const Shape& s) {
   if (!s.o16) return 0;
-  const size_t b = (size_t)s.batch * s.heads * kVParts * sizeof(float);
+  // partial maxima [b][H][kVParts] fp32, then exponents [b][H] int32
+  const size_t b = (size_t)s.batch * s.heads * (kVParts * sizeof(float) + sizeof(int32_t));
   return (b + 255) & ~(size_t)255;
 }
 
@@ -674,6 +683,8 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
   a.perm = perm;
   a.o = static_cast<char*>(o_rounds) + o_header_bytes(s);
   a.vpart = static_cast<const float*>(o_rounds);
+  a.hexp = reinterpret_cast<int32_t*>(static_cast<float*>(o_rounds) +
+                                      (int64_t)s.batch * s.heads * kVParts);
   a.lse = lse;
   a.rounds = s.rounds;
   a.L = s.len;

@@ -7,9 +7,8 @@
 // workgroup covers 16 consecutive tokens of one (batch, head), so y is written
 // with full 256-byte rows while the per-round rows are gathered through
 // inv_perm.  The per-round rows are fp32, or (compact format, bf16 inputs)
-// fp16 of o * 2^-k with one k per (batch, head), recovered from the partial
-// maxima of |v| in the header of the per-round buffer; 2^k is applied once,
-// with the normalisation.
+// fp16 of o * 2^-k with one k per (batch, head), read from the header of the
+// per-round buffer; 2^k is applied once, with the normalisation.
 #include <math.h>
 
 #include <algorithm>
@@ -51,26 +50,25 @@ struct ORows<true> {
   }
 };
 
-// 2^k of (batch, head) bh (1 for fp32 rows); every lane of the wave must call
-// it.
+// 2^k of (batch, head) bh (1 for fp32 rows).
 template <bool O16>
-__device__ __forceinline__ float o_unscale(const float* vpart, int64_t bh) {
+__device__ __forceinline__ float o_unscale(const int32_t* hexp, int64_t bh) {
   if (!O16) return 1.0f;
-  return pow2f(o_scale_exponent(head_vmax(vpart + bh * kVParts)));
+  return pow2f(hexp[bh]);
 }
 
 // RMAX >= rounds: every round's slot, lse and output row are requested before
 // any is used, so a token's R row gathers are in flight together.
 template <typename T, bool O16, int RMAX>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const typename ORows<O16>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
+    const typename ORows<O16>::elem* __restrict__ o_rounds, const int32_t* __restrict__ hexp,
     const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
     float* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
   // Last tokens first: the per-round rows written last by the attention step
   // are the likeliest to still sit in the memory-side cache.
   const int64_t tok0 = (blk0 + gridDim.x - 1 - blockIdx.x) * 16;   // < total
   // the workgroup's 16 tokens lie in one (batch, head) (L is a multiple of 64)
-  const float unscale = o_unscale<O16>(vpart, tok0 / L);
+  const float unscale = o_unscale<O16>(hexp, tok0 / L);
   const int64_t tok = tok0 + (threadIdx.x >> 4);
   if (tok >= total) return;
   const int c4 = (threadIdx.x & 15) * 4;
@@ -123,11 +121,11 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // Any number of rounds: a running softmax over the rounds, one round at a time.
 template <typename T, bool O16>
 __global__ __launch_bounds__(256) void combine_many_kernel(
-    const typename ORows<O16>::elem* __restrict__ o_rounds, const float* __restrict__ vpart,
+    const typename ORows<O16>::elem* __restrict__ o_rounds, const int32_t* __restrict__ hexp,
     const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
     float* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
   const int64_t tok0 = (blk0 + gridDim.x - 1 - blockIdx.x) * 16;
-  const float unscale = o_unscale<O16>(vpart, tok0 / L);
+  const float unscale = o_unscale<O16>(hexp, tok0 / L);
   const int64_t tok = tok0 + (threadIdx.x >> 4);
   if (tok >= total) return;
   const int c4 = (threadIdx.x & 15) * 4;
@@ -165,7 +163,8 @@ __global__ __launch_bounds__(256) void combine_many_kernel(
 template <typename T, bool O16>
 static void launch_combine_t(const Shape& s, const void* o_buf, const float* lse,
                              const int32_t* inv_perm, const T* v, float* y, hipStream_t stream) {
-  const float* vpart = static_cast<const float*>(o_buf);
+  const int32_t* hexp = reinterpret_cast<const int32_t*>(static_cast<const float*>(o_buf) +
+                                                         (int64_t)s.batch * s.heads * kVParts);
   const auto* o_rounds = reinterpret_cast<const typename ORows<O16>::elem*>(
       static_cast<const char*>(o_buf) + o_header_bytes(s));
   const int64_t total = s.token_heads();
@@ -175,7 +174,7 @@ static void launch_combine_t(const Shape& s, const void* o_buf, const float* lse
   for (int64_t b0 = (nblk - 1) / kMaxBlocks * kMaxBlocks; b0 >= 0; b0 -= kMaxBlocks) {
     const dim3 grid((unsigned)std::min(kMaxBlocks, nblk - b0)), block(256);
 #define LSH_COMBINE(K)                                                                       \
-  hipLaunchKernelGGL(K, grid, block, 0, stream, o_rounds, vpart, lse, inv_perm, v, y, s.rounds, \
+  hipLaunchKernelGGL(K, grid, block, 0, stream, o_rounds, hexp, lse, inv_perm, v, y, s.rounds, \
                      s.len, total, b0)
   if (s.rounds <= 1)
     LSH_COMBINE((combine_kernel<T, O16, 1>));

@@ -3,9 +3,10 @@ the layout the C ABI documents (include/lsh.h):
 
 * LSH_O_F32 (any input dtype): fp32 rows [b][H][R][L][64];
 * LSH_O_F16_SCALED (bf16 inputs): a header of 256 fp32 partial maxima of |v| per (b, h)
-  ([b][H][256], padded to a multiple of 256 bytes), then fp16 rows
-  [b][H][R][L][64] holding o * 2^-k, where k = max(e - 15, -100) and e is the
-  smallest integer with max(header of (b, h)) < 2^e (e = -126 below 2^-126).
+  ([b][H][256]) and the int32 exponent k of each (b, h) ([b][H]), padded to a
+  multiple of 256 bytes, then fp16 rows [b][H][R][L][64] holding o * 2^-k,
+  where k = max(e - 15, -100) and e is the smallest integer with the largest
+  partial maximum of (b, h) < 2^e (e = -126 below 2^-126).
 
 The values come back as fp32, which holds fp16 * 2^k exactly.
 """
@@ -19,7 +20,7 @@ V_PARTS = 256
 def header_bytes(w):
     if not w.o16:
         return 0
-    n = w.batch * w.heads * V_PARTS * 4
+    n = w.batch * w.heads * (V_PARTS * 4 + 4)
     return (n + 255) // 256 * 256
 
 
@@ -36,6 +37,13 @@ def header(buf, w):
     """The [b][H][256] partial maxima (bf16 inputs)."""
     n = w.batch * w.heads * V_PARTS
     return np.asarray(buf[: n * 4]).view(np.float32).reshape(w.batch, w.heads, V_PARTS)
+
+
+def head_exponents(buf, w):
+    """The [b][H] int32 exponents that follow the partial maxima."""
+    n = w.batch * w.heads
+    return np.asarray(buf).view(np.uint8).ravel()[n * V_PARTS * 4: n * V_PARTS * 4 + n * 4].view(
+        np.int32).reshape(w.batch, w.heads)
 
 
 def read_o_rounds(buf, w):

@@ -135,8 +135,8 @@ def test_workspace_bytes_cover_the_count_tables():
 
 def test_per_round_buffer_size():
     """LSH_O_F32 (either input dtype): fp32 rows; LSH_O_F16_SCALED (bf16
-    inputs): 256 fp32 partial maxima per (batch, head), padded to a multiple
-    of 256 bytes, then fp16 rows."""
+    inputs): 256 fp32 partial maxima and one int32 exponent per (batch,
+    head), padded to a multiple of 256 bytes, then fp16 rows."""
     for b, H, L, R, dt in ((1, 8, 65536, 8, B.LSH_BF16), (2, 3, 192, 5, B.LSH_BF16),
                            (1, 1, 1024, 1, B.LSH_F32), (3, 2, 448, 3, B.LSH_F32)):
         rows = b * H * R * L * 64
@@ -145,7 +145,7 @@ def test_per_round_buffer_size():
         assert B.lsh_o_rounds_bytes(c) == 4 * rows
         c = cfg(batch=b, heads=H, seq_len=L, n_rounds=R, dtype=dt, o_format=B.LSH_O_F16_SCALED)
         if dt == B.LSH_BF16:
-            header = -(-(b * H * 256 * 4) // 256) * 256
+            header = -(-(b * H * (256 * 4 + 4)) // 256) * 256
             assert B.lsh_o_rounds_bytes(c) == header + 2 * rows
         else:
             assert B.lsh_o_rounds_bytes(c) == 0     # unsupported with fp32 inputs

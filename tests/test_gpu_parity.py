@@ -192,15 +192,27 @@ def test_empty_problem_is_a_no_op(B):
     del z
 
 
+def _defined_o_bytes(f, w):
+    """The bytes of the per-round buffer the layout defines (the header's
+    partial maxima and exponents, and the rows; not the header's padding)."""
+    raw = host(f.o_rounds)
+    if not w.o16:
+        return raw
+    used = w.batch * w.heads * (256 * 4 + 4)
+    return np.concatenate([raw[:used], raw[header_bytes(w):]])
+
+
 def test_repeat_runs_are_bitwise_identical(B):
     w = synth.WORKLOADS["small"]
     inp = synth.make_inputs(w)
     a = run_gpu(B, w, inp)
-    outs = [host(t).copy() for t in (a.buckets, a.perm, a.inv_perm, a.o_rounds, a.lse, a.y)]
+    outs = [host(t).copy() for t in (a.buckets, a.perm, a.inv_perm, a.lse, a.y)]
+    o_a = _defined_o_bytes(a, w).copy()
     for _ in range(3):
         b = run_gpu(B, w, inp)
-        for x, t in zip(outs, (b.buckets, b.perm, b.inv_perm, b.o_rounds, b.lse, b.y)):
+        for x, t in zip(outs, (b.buckets, b.perm, b.inv_perm, b.lse, b.y)):
             assert np.array_equal(x, host(t))
+        assert np.array_equal(o_a, _defined_o_bytes(b, w))
 
 
 def test_per_round_output_scale(B):
@@ -224,6 +236,9 @@ def test_per_round_output_scale(B):
     raw = host(f.o_rounds)
     hdr = header(raw, w)
     assert np.array_equal(hdr.max(axis=2).astype(np.float64), np.abs(v).max(axis=(2, 3)))
+    from o_rounds_layout import head_exponents, scale_exponent
+    assert np.array_equal(head_exponents(raw, w),
+                          [[scale_exponent(float(x)) for x in row] for row in hdr.max(axis=2)])
     n = w.batch * w.heads * w.n_rounds * w.seq_len * w.head_dim
     stored = raw[header_bytes(w): header_bytes(w) + 2 * n].view(np.float16)
     assert np.abs(stored.astype(np.float64)).max() <= 2.0 ** 15 * (1 + 2.0 ** -10)
