@@ -66,9 +66,11 @@ def algorithmic(w, union=False):
     }
     if union:
         # round-key table: built from buckets and inv_perm (8 B per token-round
-        # read, stride keys per token written), then gathered with every key row
-        stride = (w.n_rounds + 3) // 4 * 4
-        out["attend"]["bytes"] += 8 * N + 4 * stride * T + 4 * stride * N
+        # read, the keys of rounds 0 .. R-2 per token written: 4, 8 or 16 per
+        # token), then gathered with every key row of round r for rounds 0 .. r-1
+        R = w.n_rounds
+        stride = 4 if R <= 5 else (8 if R <= 9 else 16)
+        out["attend"]["bytes"] += 8 * N + 4 * stride * T + 4 * T * (R * (R - 1) // 2)
     return out
 
 

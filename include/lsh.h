@@ -213,11 +213,14 @@ size_t lsh_union_workspace_bytes(const lsh_config* cfg);
  *   workspace  device scratch of at least lsh_union_workspace_bytes(cfg)
  *              bytes (else LSH_ERR_WORKSPACE_TOO_SMALL); contents ignored
  *
- * As lsh_chunk_attend, except that the score of key j for query i is
- * s_ij - log(c_ij), c_ij = the number of rounds in which j is a key of i
- * (same bucket, j's sorted slot in the window of i's chunk; c_ij >= 1).
- * lsh_unsort_combine of these outputs is then the softmax of s_ij over the
- * set union of the rounds' keys.  Supports n_rounds <= 16 and
+ * As lsh_chunk_attend, except that round r keeps a key j of query i only if
+ * j is a key of i in no round before r (a key of i in round r' is one with
+ * the same bucket and a sorted slot in the window of i's chunk, under the
+ * causal and self rules): every key of the union is attended once, in the
+ * first round that finds it, and a round whose keys were all found earlier
+ * gives lse = -inf and o = 0.  lsh_unsort_combine of these outputs is then
+ * the softmax of s_ij over the set union of the rounds' keys.  Supports
+ * n_rounds <= 16 and
  * n_buckets * (seq_len / 64 + 1) < 2^31 (else LSH_ERR_UNSUPPORTED).
  */
 lsh_status lsh_chunk_attend_union(const lsh_config* cfg, const void* qk,

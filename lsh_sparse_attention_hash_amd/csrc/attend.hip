@@ -70,7 +70,7 @@ constexpr int kVRowDw = kVStride / 2;   // 68
 __device__ __forceinline__ int vt_col(int d, int kdw) { return kdw ^ (8 * ((d >> 4) & 3)); }
 
 struct AttendLds {
-  uint16_t xs[128 * kXStride];
+  uint16_t xs[128 * kXStride];   // row padding: round keys 0..3 of the set union
   uint32_t vt[kHeadDim * kVRowDw];
   float kinv[128];     // log2(e) / (max(|x_j|, eps) * sqrt(d))
   int32_t kbk[128];    // bucket of the key
@@ -87,43 +87,70 @@ struct ChunkRegs {
   uint4 uk;                 // set union: 4 round keys of key 2*(t/8) + (t%8)/4
 };
 
-__device__ __forceinline__ int2 load_perm_pair(const int32_t* pm, int c, int L) {
-  int2 p = *reinterpret_cast<const int2*>(pm + (size_t)c * kChunk + 2 * (threadIdx.x >> 3));
-  p.x = clamp_index(p.x, L);
-  p.y = clamp_index(p.y, L);
-  return p;
+// The perm entries of this thread's key pair in chunk c, as stored (clamped
+// where they are used, so that the load is not waited for here).
+__device__ __forceinline__ int2 load_perm_pair(const int32_t* pm, int c) {
+  return *reinterpret_cast<const int2*>(pm + (size_t)c * kChunk + 2 * (threadIdx.x >> 3));
 }
 
-template <bool UNION = false>
-__device__ __forceinline__ void gather_chunk(ChunkRegs& g, int2 pos, const uint16_t* xb,
-                                             const uint16_t* vb, const int32_t* bk,
-                                             const int32_t* uk = nullptr, int ustride = 0) {
+// Set union: the round keys of rounds 0 .. rnd-1 of the chunk's tokens (at
+// the clamped positions pos of this thread's key pair), one 16-byte block of a
+// table row per thread.  The load is unconditional (a guarded load would be
+// waited for at once): a thread whose block is not needed loads a block of the
+// same row, and in round 0 (no earlier round) every thread loads the table's
+// first block.  (pos is taken by value: a choice between two fields of the
+// register struct would be compiled as a choice of addresses, moving the
+// struct to scratch memory.)
+template <int UR>
+__device__ __forceinline__ uint4 gather_round_keys(int2 pos, const int32_t* uk, int rnd) {
   const int dblk = threadIdx.x & 7;
-  if (UNION) {
-    const int blk4 = 4 * (dblk & 3);
-    const int tok = (dblk >> 2) ? pos.y : pos.x;
-    g.uk = blk4 < ustride ? load16(uk + (size_t)tok * ustride + blk4) : make_uint4(0, 0, 0, 0);
-  }
+  const int blk4 = min(4 * (dblk & 3), UR - 4);
+  const int tok = (dblk >> 2) ? pos.y : pos.x;
+  return load16(uk + (rnd > 0 ? (size_t)tok * UR + blk4 : 0));
+}
+
+// The x and v rows, bucket ids and positions of a chunk (and with UKEY its
+// round keys for the set union).
+template <int UR = 0, bool UKEY = true>
+__device__ __forceinline__ void gather_chunk(ChunkRegs& g, int2 pos, int L, const uint16_t* xb,
+                                             const uint16_t* vb, const int32_t* bk,
+                                             const int32_t* uk = nullptr, int rnd = 0) {
+  const int dblk = threadIdx.x & 7;
+  pos.x = clamp_index(pos.x, L);
+  pos.y = clamp_index(pos.y, L);
   g.pos = pos;
-  g.xa = load16(xb + (size_t)pos.x * kHeadDim + 8 * dblk);
-  g.xc = load16(xb + (size_t)pos.y * kHeadDim + 8 * dblk);
-  g.va = load16(vb + (size_t)pos.x * kHeadDim + 8 * dblk);
-  g.vc = load16(vb + (size_t)pos.y * kHeadDim + 8 * dblk);
+  const size_t ra = (size_t)(pos.x * (kHeadDim / 8) + dblk) * 8;   // elements, < 2^31 * 8
+  const size_t rc = (size_t)(pos.y * (kHeadDim / 8) + dblk) * 8;
+  g.xa = load16(xb + ra);
+  g.xc = load16(xb + rc);
+  g.va = load16(vb + ra);
+  g.vc = load16(vb + rc);
   g.ba = bk[pos.x];
   g.bc = bk[pos.y];
+  if (UR > 0 && UKEY) g.uk = gather_round_keys<UR>(pos, uk, rnd);
+}
+
+// Set union: block b (rounds 4b .. 4b+3) of the round keys of window row
+// `row`.  Block 0 lives in the 16 padding bytes of the row's x copy, the rest
+// in kkey ([128][UR - 4]), which keeps the workgroup's LDS within 40 KB at
+// UR = 8 (four workgroups per CU).
+template <int UR>
+__device__ __forceinline__ int32_t* ukey_block(AttendLds& sm, int32_t* kkey, int row, int b) {
+  return b == 0 ? reinterpret_cast<int32_t*>(&sm.xs[row * kXStride + kHeadDim])
+                : &kkey[row * (UR - 4) + 4 * (b - 1)];
 }
 
 // Write a gathered chunk c into LDS half (c & 1): x rows, V transposed, and
 // per-key scale, bucket and position (and the round keys for the set union).
-template <bool UNION = false>
+template <int UR = 0>
 __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, int c,
-                                             int32_t* kkey = nullptr) {
+                                             int32_t* kkey = nullptr, int rnd = 0) {
   const int tid = threadIdx.x;
   const int p = tid >> 3;          // key pair 0..31
   const int dblk = tid & 7;        // 16-byte column block
   const int row = 64 * (c & 1) + 2 * p;
-  if (UNION)
-    store16(&kkey[(row + (dblk >> 2)) * kMaxUnionRounds + 4 * (dblk & 3)], g.uk);
+  if (UR > 0 && 4 * (dblk & 3) < UR && 4 * (dblk & 3) < rnd)
+    store16(ukey_block<UR>(sm, kkey, row + (dblk >> 2), dblk & 3), g.uk);
   store16(&sm.xs[row * kXStride + 8 * dblk], g.xa);
   store16(&sm.xs[(row + 1) * kXStride + 8 * dblk], g.xc);
   const uint32_t wa[4] = {g.va.x, g.va.y, g.va.z, g.va.w};
@@ -162,10 +189,10 @@ __device__ __forceinline__ void commit_chunk(AttendLds& sm, const ChunkRegs& g, 
   }
 }
 
-template <bool CAUSAL, bool SELF, bool UNION, bool O16>
+template <bool CAUSAL, bool SELF, int UR, bool O16>
 __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArgs& a, int64_t seg,
-                                                  int c, float oscale,
-                                                  const int32_t* kkey = nullptr) {
+                                                  int c, float oscale, int rnd = 0,
+                                                  int32_t* kkey = nullptr) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;          // 16-lane group
@@ -180,19 +207,6 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
   for (int ks = 0; ks < 2; ++ks) qf[ks] = as_bf16x8(load16(&sm.xs[qrow * kXStride + 8 * g + 32 * ks]));
   const int qb = sm.kbk[qrow];
   const int qp = sm.kpos[qrow];
-  int32_t kq[kMaxUnionRounds];   // set union: the query's round keys
-  if (UNION) {
-#pragma unroll
-    for (int q4 = 0; q4 < kMaxUnionRounds; q4 += 4) {
-      const int4 w = *reinterpret_cast<const int4*>(&kkey[qrow * kMaxUnionRounds + q4]);
-      kq[q4] = w.x; kq[q4 + 1] = w.y; kq[q4 + 2] = w.z; kq[q4 + 3] = w.w;
-    }
-    // rounds past the last never match: keys are >= -2, so a difference from
-    // 2^30 is never 0 or 1
-#pragma unroll
-    for (int q = 0; q < kMaxUnionRounds; ++q)
-      if (q >= a.rounds) kq[q] = 1 << 30;
-  }
 
   // Tiles of the window (16 keys each) that hold no key any query of this
   // wave can keep are skipped: a key whose bucket lies outside the range of
@@ -266,23 +280,30 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
       const float sc = acc[i] * kva[i];
       s[t][i] = ok ? sc : -INFINITY;
     }
-    if (UNION && __ballot(oka[0] || oka[1] || oka[2] || oka[3])) {
-      // key j of the union weighs once: its score loses log2 of the number of
-      // rounds in which it is a candidate of this query (same bucket, and its
-      // sorted slot in the query's chunk or the one before: key difference 0 or 1)
+    if (UR > 0 && rnd > 0 && __ballot(oka[0] || oka[1] || oka[2] || oka[3])) {
+      // each key of the union is attended in the first round that finds it:
+      // it is left out here if an earlier round has it as a candidate of this
+      // query (same bucket, and its sorted slot in the query's chunk or the
+      // one before: round-key difference 0 or 1).  Query round keys of rounds
+      // from rnd on are replaced by 2^30, which never matches (keys >= -2).
+      // (any difference <= 1 iff the smallest, as unsigned, is)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int32_t* kk = &kkey[(row4 + i) * kMaxUnionRounds];
-        int cnt = 0;
+        uint32_t dmin = ~0u;
 #pragma unroll
-        for (int q4 = 0; q4 < kMaxUnionRounds; q4 += 4) {
-          if (q4 >= a.rounds) break;
-          const int4 w = *reinterpret_cast<const int4*>(kk + q4);
-          const int wk[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) cnt += (uint32_t)(kq[q4 + e] - wk[e]) <= 1u ? 1 : 0;
+        for (int q4 = 0; q4 < UR; q4 += 4) {
+          if (q4 < rnd) {
+            int4 kq = *reinterpret_cast<const int4*>(ukey_block<UR>(sm, kkey, qrow, q4 / 4));
+            if (q4 + 1 >= rnd) kq.y = 1 << 30;
+            if (q4 + 2 >= rnd) kq.z = 1 << 30;
+            if (q4 + 3 >= rnd) kq.w = 1 << 30;
+            const int4 w = *reinterpret_cast<const int4*>(ukey_block<UR>(sm, kkey, row4 + i, q4 / 4));
+            dmin = min(min(dmin, (uint32_t)(kq.x - w.x)),
+                       min(min((uint32_t)(kq.y - w.y), (uint32_t)(kq.z - w.z)),
+                           (uint32_t)(kq.w - w.w)));
+          }
         }
-        if (oka[i]) s[t][i] -= __builtin_amdgcn_logf((float)cnt);
+        if (dmin <= 1u) s[t][i] = -INFINITY;
       }
     }
   }
@@ -365,13 +386,31 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
         (mx == -INFINITY) ? -INFINITY : (mx + __builtin_amdgcn_logf(sum)) * kLn2;
 }
 
-template <bool CAUSAL, bool SELF, bool UNION, bool O16>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
+// Set union: the rounds of a head differ in cost (round r tests the r rounds
+// before it), and under xcd_interleaved_block XCD x works through units x,
+// x + 8, x + 16, ...  Rotating each group of 8 units by its group index gives
+// XCD x unit (x + g) % 8 of group g, so over 8 groups every XCD takes each
+// position in a group (each round, for 8 rounds per head) once.  A bijection
+// on [0, units).
+__device__ __forceinline__ int64_t rotate_in_group(int64_t unit, int64_t units) {
+  if (units % kXcds != 0) return unit;
+  const int64_t g = unit / kXcds;
+  return g * kXcds + (unit + g) % kXcds;
+}
+
+// Four workgroups (waves per SIMD) per CU: at most 128 VGPRs and 40 KB of
+// LDS each; the 16-wide round-key table of the set union needs more LDS.
+template <bool CAUSAL, bool SELF, int UR, bool O16>
+__global__ __launch_bounds__(256, UR > 8 ? 3 : 4) void attend_bf16_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) AttendLds sm;
-  __shared__ __attribute__((aligned(16))) int32_t kkey[UNION ? 128 * kMaxUnionRounds : 4];
-  const int64_t blk = xcd_interleaved_block(blockIdx.x, gridDim.x / a.runs_per_seg, a.runs_per_seg);
+  __shared__ __attribute__((aligned(16))) int32_t kkey[UR > 4 ? 128 * (UR - 4) : 4];
+  const int64_t units = gridDim.x / a.runs_per_seg;
+  int64_t blk = xcd_interleaved_block(blockIdx.x, units, a.runs_per_seg);
+  if (UR > 0)
+    blk = rotate_in_group(blk / a.runs_per_seg, units) * a.runs_per_seg + blk % a.runs_per_seg;
   const int64_t seg = blk / a.runs_per_seg;
   const int run = (int)(blk % a.runs_per_seg);
+  const int rnd = UR > 0 ? (int)(seg % a.rounds) : 0;
   const int c0 = run * a.cpw;
   const int c1 = min(a.nchunks, c0 + a.cpw);
   const int64_t bh = seg / a.rounds;
@@ -379,7 +418,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   const uint16_t* vb = static_cast<const uint16_t*>(a.v) + bh * (int64_t)a.L * kHeadDim;
   const int32_t* bk = a.buckets + seg * a.L;
   const int32_t* pm = a.perm + seg * a.L;
-  const int32_t* uk = UNION ? a.ukeys + bh * (int64_t)a.L * a.ukey_stride : nullptr;
+  const int32_t* uk = UR > 0 ? a.ukeys + bh * (int64_t)a.L * UR : nullptr;
   // scale of the (batch, head)'s fp16 output rows: 2^-k; the head's first
   // workgroup records k for the combine
   float oscale = 1.0f;
@@ -390,20 +429,30 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttendArgs a) {
   }
   ChunkRegs g;
   if (c0 > 0) {
-    gather_chunk<UNION>(g, load_perm_pair(pm, c0 - 1, a.L), xb, vb, bk, uk, a.ukey_stride);
-    commit_chunk<UNION>(sm, g, c0 - 1, kkey);
+    gather_chunk<UR>(g, load_perm_pair(pm, c0 - 1), a.L, xb, vb, bk, uk, rnd);
+    commit_chunk<UR>(sm, g, c0 - 1, kkey, rnd);
   }
-  gather_chunk<UNION>(g, load_perm_pair(pm, c0, a.L), xb, vb, bk, uk, a.ukey_stride);
-  int2 next = make_int2(0, 0);
-  if (c0 + 1 < c1) next = load_perm_pair(pm, c0 + 1, a.L);
+  gather_chunk<UR>(g, load_perm_pair(pm, c0), a.L, xb, vb, bk, uk, rnd);
+  // perm entries of the chunk after next, requested without a condition (the
+  // last chunk's again at the end of the run) so that no wait is forced; in
+  // the loop through a descriptor of the run's perm entries, so the address is
+  // a scalar base plus this thread's 32-bit offset
+  int2 next = load_perm_pair(pm, min(c0 + 1, c1 - 1));
+  const __amdgpu_buffer_rsrc_t prun = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(pm + (size_t)c0 * kChunk), (short)0, (c1 - c0) * kChunk * 4, kBufferWord3);
+  const int poff = 8 * (threadIdx.x >> 3);
   for (int c = c0; c < c1; ++c) {
-    commit_chunk<UNION>(sm, g, c, kkey);
+    commit_chunk<UR>(sm, g, c, kkey, rnd);
     if (c + 1 < c1) {
-      gather_chunk<UNION>(g, next, xb, vb, bk, uk, a.ukey_stride);   // chunk c+1, in flight
-      if (c + 2 < c1) next = load_perm_pair(pm, c + 2, a.L);
+      // chunk c+1, in flight during chunk c (its round keys are requested after
+      // chunk c: held across it they would push the kernel past 128 VGPRs)
+      gather_chunk<UR, false>(g, next, a.L, xb, vb, bk, uk, rnd);
+      next = __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(
+                                          prun, poff, (min(c + 2, c1 - 1) - c0) * kChunk * 4, 0));
     }
     __syncthreads();
-    attend_chunk_bf16<CAUSAL, SELF, UNION, O16>(sm, a, seg, c, oscale, kkey);
+    attend_chunk_bf16<CAUSAL, SELF, UR, O16>(sm, a, seg, c, oscale, rnd, kkey);
+    if (UR > 0 && c + 1 < c1) g.uk = gather_round_keys<UR>(g.pos, uk, rnd);
     __syncthreads();
   }
 }
@@ -454,6 +503,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
   for (int k = 0; k < kHeadDim / 4; ++k)
     xq[k] = *reinterpret_cast<const float4*>(xb + (int64_t)qp * kHeadDim + 4 * k);
   const int32_t* uq = a.ukeys ? a.ukeys + (bh * a.L + qp) * a.ukey_stride : nullptr;
+  const int rnd = (int)(seg % a.rounds);   // set union: rounds 0 .. rnd-1 come first
 
   float m = -INFINITY, l = 0.f;
   float o[16];
@@ -498,13 +548,13 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
       }
       float s = ((d0 + d1) + (d2 + d3)) * kinv[kk];
       const int kp = kpos[kk];
-      const bool keep = kbk[kk] == qb && !(a.causal && kp > qp) && !(a.self_mask && kp == qp);
+      bool keep = kbk[kk] == qb && !(a.causal && kp > qp) && !(a.self_mask && kp == qp);
       if (keep && uq) {
-        // set union over rounds: the key weighs once over all rounds
+        // set union over rounds: the key is attended in the first round that
+        // finds it, so it is left out if an earlier round has it as a
+        // candidate (round-key difference 0 or 1)
         const int32_t* uj = a.ukeys + (bh * a.L + kp) * a.ukey_stride;
-        int cnt = 0;
-        for (int r = 0; r < a.rounds; ++r) cnt += (uint32_t)(uq[r] - uj[r]) <= 1u ? 1 : 0;
-        s -= logf((float)cnt);
+        for (int r = 0; r < rnd; ++r) keep = keep && (uint32_t)(uq[r] - uj[r]) > 1u;
       }
       sc[i] = keep ? s : -INFINITY;
       mh = fmaxf(mh, sc[i]);
@@ -550,7 +600,9 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
   if (part == 0) a.lse[seg * a.L + slot] = (m == -INFINITY) ? -INFINITY : m + logf(l);
 }
 
-int union_key_stride(const Shape& s) { return (s.rounds + 3) & ~3; }
+// Round r needs the keys of rounds 0 .. r-1 only, so the table holds rounds
+// 0 .. R-2, padded to 4, 8 or 16 entries per token.
+int union_key_stride(const Shape& s) { return s.rounds <= 5 ? 4 : s.rounds <= 9 ? 8 : kMaxUnionRounds; }
 
 size_t union_workspace_bytes(const Shape& s) {
   return (size_t)s.token_heads() * union_key_stride(s) * sizeof(int32_t);
@@ -656,17 +708,25 @@ size_t o_rounds_bytes(const Shape& s) {
          (size_t)s.segments() * s.len * kHeadDim * (s.o16 ? sizeof(uint16_t) : sizeof(float));
 }
 
-template <bool UNION, bool O16>
+template <int UR, bool O16>
 static void launch_attend_masks(const AttendArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(256);
   if (a.causal && a.self_mask)
-    hipLaunchKernelGGL((attend_bf16_kernel<true, true, UNION, O16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<true, true, UR, O16>), grid, block, 0, stream, a);
   else if (a.causal)
-    hipLaunchKernelGGL((attend_bf16_kernel<true, false, UNION, O16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<true, false, UR, O16>), grid, block, 0, stream, a);
   else if (a.self_mask)
-    hipLaunchKernelGGL((attend_bf16_kernel<false, true, UNION, O16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<false, true, UR, O16>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attend_bf16_kernel<false, false, UNION, O16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attend_bf16_kernel<false, false, UR, O16>), grid, block, 0, stream, a);
+}
+
+template <int UR>
+static void launch_attend_stride(const AttendArgs& a, bool o16, dim3 grid, hipStream_t stream) {
+  if (o16)
+    launch_attend_masks<UR, true>(a, grid, stream);
+  else
+    launch_attend_masks<UR, false>(a, grid, stream);
 }
 
 template <bool UNION>
@@ -732,10 +792,14 @@ static hipError_t launch_attend_impl(const Shape& s, const void* qk, const void*
   a.cpw = cpw;
   a.runs_per_seg = (a.nchunks + cpw - 1) / cpw;
   const dim3 grid((unsigned)(S * a.runs_per_seg));
-  if (s.o16)
-    launch_attend_masks<UNION, true>(a, grid, stream);
+  if (!UNION)
+    launch_attend_stride<0>(a, s.o16, grid, stream);
+  else if (a.ukey_stride == 4)
+    launch_attend_stride<4>(a, s.o16, grid, stream);
+  else if (a.ukey_stride == 8)
+    launch_attend_stride<8>(a, s.o16, grid, stream);
   else
-    launch_attend_masks<UNION, false>(a, grid, stream);
+    launch_attend_stride<kMaxUnionRounds>(a, s.o16, grid, stream);
   return hipGetLastError();
 }
 
@@ -751,12 +815,13 @@ hipError_t launch_attend_union(const Shape& s, const void* qk, const void* v,
   int32_t* keys = static_cast<int32_t*>(workspace);
   const int64_t total = s.token_heads();
   const dim3 kgrid((unsigned)((total + 255) / 256)), kblock(256);
-  if (s.rounds <= 4)
+  const int stride = union_key_stride(s);
+  if (stride == 4)
     hipLaunchKernelGGL(union_keys_kernel<4>, kgrid, kblock, 0, stream, buckets, inv_perm, keys,
-                       s.rounds, union_key_stride(s), s.len, s.buckets, total);
-  else if (s.rounds <= 8)
+                       s.rounds, stride, s.len, s.buckets, total);
+  else if (stride == 8)
     hipLaunchKernelGGL(union_keys_kernel<8>, kgrid, kblock, 0, stream, buckets, inv_perm, keys,
-                       s.rounds, union_key_stride(s), s.len, s.buckets, total);
+                       s.rounds, stride, s.len, s.buckets, total);
   else
     hipLaunchKernelGGL(union_keys_kernel<kMaxUnionRounds>, kgrid, kblock, 0, stream, buckets,
                        inv_perm, keys, s.rounds, union_key_stride(s), s.len, s.buckets, total);

@@ -81,9 +81,6 @@ __device__ int exact_bucket(const double* x, const T* rot_hr, int half) {
 // that truncation; the tile of the running maximum is tracked per lane.
 constexpr uint32_t kKeyMask = ~31u;
 
-// Raw buffer descriptor word 3 for gfx9 (32-bit data format; no swizzle): a
-// load at a byte offset past the descriptor's size returns zero.
-constexpr int kBufferWord3 = 0x00020000;
 
 // Stage st of a round: rows [128 st, 128 st + 128) of the rotation, 1024
 // pieces of 16 B, 4 per thread.  The descriptor covers only the stage's rows

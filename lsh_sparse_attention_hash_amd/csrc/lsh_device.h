@@ -21,6 +21,10 @@ constexpr int kWave = 64;      // CDNA wavefront
 // (2^30 work-items at 256 per workgroup), each told its first block.
 constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 
+// Raw buffer descriptor word 3 for gfx9 (32-bit data format; no swizzle): a
+// load at a byte offset past the descriptor's size returns zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 // 16-byte global/LDS load and store through uint4.
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);

@@ -39,7 +39,8 @@
  *     leaves any candidate, y_i = v_i (the token attends only to itself);
  *   - rounds combine as a multiset: a key found in k rounds counts k times
  *     (oracle_lsh_attend); oracle_lsh_attend_union gives the set reading
- *     instead, where every key of the union counts once.
+ *     instead, where every key of the union counts once: it is attended in
+ *     the first round in which it is a candidate and left out of later ones.
  *
  * Layouts (all row-major, all arrays owned by the caller):
  *   qk, v      [batch][heads][L][d]            double
@@ -217,28 +218,29 @@ static double norm2(const double* x, int d) {
   return sqrt(acc);
 }
 
-/* Number of rounds r' in which key j is a candidate of query i (the same
- * bucket and, in round r', a sorted slot inside the window of i's chunk; the
- * causal and self rules do not depend on the round). */
-static int rounds_sharing(const shape_t* s, const int32_t* buckets,
-                          const int32_t* inv_perm, int64_t bh, int i, int j) {
-  int count = 0;
-  for (int r = 0; r < s->rounds; ++r) {
-    const int64_t seg = bh * s->rounds + r;
+/* 1 when key j is a candidate of query i in some round before round r (the
+ * same bucket and, in that round, a sorted slot inside the window of i's
+ * chunk; the causal and self rules do not depend on the round, and j already
+ * satisfies them as a candidate of round r). */
+static int found_earlier(const shape_t* s, const int32_t* buckets,
+                         const int32_t* inv_perm, int64_t bh, int r, int i,
+                         int j) {
+  for (int q = 0; q < r; ++q) {
+    const int64_t seg = bh * s->rounds + q;
     const int32_t* bk = buckets + seg * s->len;
     const int32_t* ip = inv_perm + seg * s->len;
     if (bk[i] != bk[j]) continue;
     const int c = ip[i] / s->chunk;
     const int first = (c > 0) ? (c - 1) * s->chunk : 0;
-    if (ip[j] >= first && ip[j] < (c + 1) * s->chunk) ++count;
+    if (ip[j] >= first && ip[j] < (c + 1) * s->chunk) return 1;
   }
-  return count;
+  return 0;
 }
 
 /* o (length d) and lse of one query row.  With inv_perm == NULL the rounds
- * are a multiset; otherwise (set semantics of the union over rounds) the
- * score of key j is lowered by log c_ij, c_ij = rounds_sharing(i, j) >= 1, so
- * that after the round combine every key of the union weighs once. */
+ * are a multiset; otherwise (set semantics of the union over rounds) a key is
+ * attended only in the first round in which it is a candidate of the query,
+ * so that after the round combine every key of the union weighs once. */
 static void attend_one(const shape_t* s, const double* qk, const double* v,
                        const int32_t* buckets, const int32_t* perm,
                        const int32_t* inv_perm, int64_t seg, int slot,
@@ -248,7 +250,14 @@ static void attend_one(const shape_t* s, const double* qk, const double* v,
   const double* xs = qk + bh * (int64_t)s->len * d;
   const double* vs = v + bh * (int64_t)s->len * d;
   const int i = perm[seg * s->len + slot];
-  const int n = candidates(s, buckets, perm, seg, slot, cand);
+  int n = candidates(s, buckets, perm, seg, slot, cand);
+  if (inv_perm) {
+    const int r = (int)(seg % s->rounds);
+    int kept = 0;
+    for (int a = 0; a < n; ++a)
+      if (!found_earlier(s, buckets, inv_perm, bh, r, i, cand[a])) cand[kept++] = cand[a];
+    n = kept;
+  }
   for (int k = 0; k < d; ++k) o[k] = 0.0;
   if (n == 0) { *lse = -INFINITY; return; }
   const double* xi = xs + (int64_t)i * d;
@@ -261,8 +270,6 @@ static void attend_one(const shape_t* s, const double* qk, const double* v,
     double nj = norm2(xj, d);
     if (nj < ORACLE_NORM_EPS) nj = ORACLE_NORM_EPS;
     score[a] = dot / nj * inv_sqrt_d;
-    if (inv_perm)
-      score[a] -= log((double)rounds_sharing(s, buckets, inv_perm, bh, i, cand[a]));
     if (score[a] > mx) mx = score[a];
   }
   double sum = 0.0;
@@ -336,10 +343,11 @@ int oracle_lsh_attend(int batch, int heads, int len, int dim, int n_buckets,
 
 /* Set semantics of the union over rounds (Reformer study note, "Multiple
  * Hash Rounds": N(i) is the union over r of the per-round neighbourhoods, as
- * a set): per-round o and lse (sorted order, like oracle_lsh_attend) with
- * every candidate's score lowered by the log of the number of rounds in
- * which it is a candidate.  oracle_lsh_combine of these is the softmax over
- * the set union.  inv_perm as returned by oracle_lsh_sort. */
+ * a set): per-round o and lse (sorted order, like oracle_lsh_attend) where
+ * round r keeps only the candidates that are not candidates of the same query
+ * in any round before r, so each key of the union is attended exactly once,
+ * in the first round that finds it.  oracle_lsh_combine of these is the
+ * softmax over the set union.  inv_perm as returned by oracle_lsh_sort. */
 int oracle_lsh_attend_union_rows(int batch, int heads, int len, int dim,
                                  int n_buckets, int rounds, int chunk,
                                  int causal, int self_mask, const double* qk,

@@ -206,9 +206,10 @@ def attend_rows(qk, v, buckets, perm, n_buckets: int, chunk: int, causal: bool,
 
 def attend_union(qk, v, buckets, perm, inv_perm, n_buckets: int, chunk: int, causal: bool,
                  self_mask: bool):
-    """Per-round (o_rounds, lse), sorted order, with each candidate's score
-    lowered by the log of the number of rounds that share it; combine() of
-    these is the softmax over the SET union of the rounds' candidates."""
+    """Per-round (o_rounds, lse), sorted order, where each candidate is
+    attended only in the first round in which it is a candidate of the query
+    (later rounds leave it out); combine() of these is the softmax over the
+    SET union of the rounds' candidates."""
     qk, v, bk, pm, ip = _f64(qk), _f64(v), _i32(buckets), _i32(perm), _i32(inv_perm)
     b, h, L, d = _dims(qk)
     R = bk.shape[2]

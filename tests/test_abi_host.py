@@ -231,7 +231,9 @@ def test_union_attend_limits_and_workspace():
     lib = B.library()
     c = cfg()
     need = B.lsh_union_workspace_bytes(c)
-    assert need == 1 * 2 * 256 * 4 * 4          # rounds padded to 4 keys per token
+    assert need == 1 * 2 * 256 * 4 * 4          # rounds before the last, padded to 4 keys
+    for R, keys in ((5, 4), (6, 8), (9, 8), (10, 16), (16, 16)):
+        assert B.lsh_union_workspace_bytes(cfg(n_rounds=R)) == 2 * 256 * keys * 4
     args = [FAKE] * 7
     assert lib.lsh_chunk_attend_union(ctypes.byref(c), *args, FAKE, need - 1, None) == \
         B.LSH_ERR_WORKSPACE_TOO_SMALL

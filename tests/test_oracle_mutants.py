@@ -56,15 +56,21 @@ MUTANTS = {
     "self_only_returns_zero": (
         "for (int k = 0; k < d; ++k) y[k] = v[(bh * L + i) * d + k];",
         "for (int k = 0; k < d; ++k) y[k] = 0.0;"),
-    "union_without_count_correction": (
-        "      score[a] -= log((double)rounds_sharing(s, buckets, inv_perm, bh, i, cand[a]));",
-        "      score[a] -= 0.0;"),
-    "union_counts_every_round": (
+    "union_keeps_keys_of_earlier_rounds": (
+        "      if (!found_earlier(s, buckets, inv_perm, bh, r, i, cand[a])) cand[kept++] = cand[a];",
+        "      cand[kept++] = cand[a];"),
+    "union_earlier_round_ignores_bucket": (
         "    if (bk[i] != bk[j]) continue;\n    const int c = ip[i] / s->chunk;",
         "    const int c = ip[i] / s->chunk;"),
-    "union_window_without_predecessor": (
-        "    const int first = (c > 0) ? (c - 1) * s->chunk : 0;",
-        "    const int first = c * s->chunk;"),
+    "union_earlier_window_without_predecessor": (
+        "    const int first = (c > 0) ? (c - 1) * s->chunk : 0;\n    if (ip[j] >= first",
+        "    const int first = c * s->chunk;\n    if (ip[j] >= first"),
+    # attending each key in its LAST round gives the same y: only the
+    # per-round pins can tell
+    "union_keeps_keys_in_their_last_round": (
+        "  for (int q = 0; q < r; ++q) {", "  for (int q = r + 1; q < s->rounds; ++q) {"),
+    "union_drops_the_own_round": (
+        "  for (int q = 0; q < r; ++q) {", "  for (int q = 0; q <= r; ++q) {"),
     "local_ignores_following_chunks": (
         "const int c_hi = (c + after < nchunks - 1) ? c + after : nchunks - 1;",
         "const int c_hi = c;"),

@@ -518,23 +518,46 @@ def test_union_with_one_round_is_the_multiset_path():
 
 
 def test_union_of_identical_rounds_is_one_round():
-    """R copies of one rotation: the union is the single round's set, so the
-    per-round outputs equal the one-round outputs and y is one round's."""
+    """R copies of one rotation: every key of the union is found in round 0,
+    so round 0's outputs are the one-round outputs, the later rounds keep no
+    key (lse = -inf, o = 0) and y is one round's."""
     L, d, m = 256, 64, 64
     x = rand(93, 1, 1, L, d)
     v = rand(94, 1, 1, L, d)
     one = rand(95, 1, 1, 8, d)
     out = oracle.forward_union(x, v, np.repeat(one, 3, axis=1), 16, 3, m, True, True)
     ref = oracle.forward(x, v, one, 16, 1, m, True, True)
-    for r in range(3):
-        np.testing.assert_allclose(out["o_rounds"][:, :, r], ref["o_rounds"][:, :, 0],
-                                   rtol=0, atol=1e-13)
-        lse = out["lse"][:, :, r]
-        fin = ~np.isneginf(ref["lse"][:, :, 0])
-        # every key is shared by all 3 rounds: each round's sum is a third of it
-        np.testing.assert_allclose(lse[fin] + math.log(3), ref["lse"][:, :, 0][fin],
-                                   rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(out["o_rounds"][:, :, 0], ref["o_rounds"][:, :, 0])
+    np.testing.assert_array_equal(out["lse"][:, :, 0], ref["lse"][:, :, 0])
+    assert np.isneginf(out["lse"][:, :, 1:]).all()
+    assert not out["o_rounds"][:, :, 1:].any()
     np.testing.assert_allclose(out["y"], ref["y"], rtol=0, atol=1e-13)
+
+
+def test_union_keeps_each_key_in_its_first_round():
+    """Per round, the keys kept are the round's candidates that no earlier
+    round of the same query has (dense sets from the definition); each round's
+    o and lse are the softmax over that set, and the sets partition the union."""
+    L, d, m, R, B = 256, 64, 64, 4, 4
+    x = rand(100, 1, 1, L, d)
+    v = rand(101, 1, 1, L, d)
+    rot = rand(102, 1, R, B // 2, d)
+    out = oracle.forward_union(x, v, rot, B, R, m, True, True)
+    cand = np_round_candidates(out["buckets"][0, 0], out["perm"][0, 0], L, m, True, True)
+    seen = np.zeros((L, L), bool)
+    dropped = 0
+    for r in range(R):
+        kept = cand[r] & ~seen
+        dropped += int((cand[r] & seen).sum())
+        seen |= cand[r]
+        o, lse = np_masked_softmax_attention(x[0, 0], v[0, 0], kept)
+        fin = ~np.isneginf(lse)
+        o[~fin] = 0.0                                    # a round with no key gives o = 0
+        slot = out["inv_perm"][0, 0, r]
+        np.testing.assert_allclose(out["o_rounds"][0, 0, r][slot], o, rtol=0, atol=1e-12)
+        assert np.array_equal(np.isneginf(out["lse"][0, 0, r][slot]), ~fin)
+        np.testing.assert_allclose(out["lse"][0, 0, r][slot][fin], lse[fin], rtol=0, atol=1e-12)
+    assert dropped > 0                                   # later rounds do drop keys
 
 
 def test_union_rows_match_full():
