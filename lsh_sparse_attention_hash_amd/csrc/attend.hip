@@ -548,14 +548,18 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendArgs a) {
       }
       float s = ((d0 + d1) + (d2 + d3)) * kinv[kk];
       const int kp = kpos[kk];
-      bool keep = kbk[kk] == qb && !(a.causal && kp > qp) && !(a.self_mask && kp == qp);
+      const bool keep = kbk[kk] == qb && !(a.causal && kp > qp) && !(a.self_mask && kp == qp);
+      int seen = 0;
       if (keep && uq) {
         // set union over rounds: the key is attended in the first round that
         // finds it, so it is left out if an earlier round has it as a
         // candidate (round-key difference 0 or 1)
         const int32_t* uj = a.ukeys + (bh * a.L + kp) * a.ukey_stride;
-        for (int r = 0; r < rnd; ++r) keep = keep && (uint32_t)(uq[r] - uj[r]) > 1u;
+#pragma unroll 1
+        for (int r = 0; r < rnd; ++r) seen += (uint32_t)(uq[r] - uj[r]) <= 1u ? 1 : 0;
       }
+      if (seen) s = -INFINITY;   // (as a select of the score: a combined condition
+                                 // made the compiler move this kernel to scratch)
       sc[i] = keep ? s : -INFINITY;
       mh = fmaxf(mh, sc[i]);
     }

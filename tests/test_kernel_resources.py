@@ -1,0 +1,75 @@
+"""Register and scratch budget of the gfx950 kernels, read from the compiler's
+resource report (hipcc -Rpass-analysis=kernel-resource-usage, device code
+only; no GPU needed).
+
+A kernel whose registers spill to scratch memory, or whose register count
+drops its occupancy, can lose most of its speed without changing a single
+output bit, so the parity tests cannot see it.  This pins both: no kernel
+uses scratch except the listed set-union forms (spills of a few registers in
+the fp32-row and less common mask forms), and the kernels of the benchmarked
+path keep four waves per SIMD."""
+import concurrent.futures
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from lsh_sparse_attention_hash_amd import build as lib_build
+
+# set-union attention with an 8-key round table, fp32 rows or no masks: a
+# few registers spill (bytes per lane)
+SCRATCH_ALLOWED = {
+    "_ZN3lsh18attend_bf16_kernelILb0ELb0ELi8ELb1EEEvNS_10AttendArgsE": 32,
+    "_ZN3lsh18attend_bf16_kernelILb1ELb1ELi8ELb0EEEvNS_10AttendArgsE": 32,
+    "_ZN3lsh18attend_bf16_kernelILb1ELb0ELi8ELb0EEEvNS_10AttendArgsE": 32,
+    "_ZN3lsh18attend_bf16_kernelILb0ELb1ELi8ELb0EEEvNS_10AttendArgsE": 32,
+}
+# kernels of the benchmarked path and their waves per SIMD
+OCCUPANCY = {
+    "_ZN3lsh16hash_bf16_kernelEPKtS1_Piiiii": 4,
+    "_ZN3lsh18attend_bf16_kernelILb1ELb1ELi0ELb1EEEvNS_10AttendArgsE": 4,
+    "_ZN3lsh18attend_bf16_kernelILb1ELb1ELi8ELb1EEEvNS_10AttendArgsE": 4,
+}
+
+
+def _report(src):
+    cmd = [lib_build.hipcc(), *lib_build.HIPFLAGS, "-c", os.path.join(lib_build.CSRC, src),
+           "-o", os.devnull, "--offload-device-only", "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = r.stderr
+    marks = list(re.finditer(r"Function Name: (\S+)", out))
+    kernels = {}
+    for i, m in enumerate(marks):
+        blk = out[m.start(): marks[i + 1].start() if i + 1 < len(marks) else len(out)]
+        kernels[m.group(1)] = {
+            "scratch": int(re.search(r"ScratchSize \[bytes/lane\]: (\d+)", blk).group(1)),
+            "occupancy": int(re.search(r"Occupancy \[waves/SIMD\]: (\d+)", blk).group(1)),
+        }
+    return kernels
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    if not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")):
+        pytest.skip("hipcc not available")
+    out = {}
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        for rep in ex.map(_report, lib_build.SOURCES):
+            out.update(rep)
+    return out
+
+
+def test_no_kernel_uses_scratch(kernels):
+    assert len(kernels) > 50
+    bad = {k: v["scratch"] for k, v in kernels.items()
+           if v["scratch"] > SCRATCH_ALLOWED.get(k, 0)}
+    assert not bad, f"kernels using scratch memory (bytes per lane): {bad}"
+
+
+def test_benchmarked_kernels_keep_four_waves_per_simd(kernels):
+    for name, waves in OCCUPANCY.items():
+        assert name in kernels, name
+        assert kernels[name]["occupancy"] >= waves, (name, kernels[name])
