@@ -30,6 +30,17 @@ __device__ __forceinline__ float4 load_v4<float>(const float* row, int c4) {
   return *reinterpret_cast<const float4*>(row + c4);
 }
 
+// Every per-round row is read once and every y row written once, so neither
+// gains from staying in a cache: both go through non-temporal accesses
+// (measured: the combine at 8 x 65,536 tokens, 8 rounds, 148 -> 137 us).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store_y_nt(float* p, float4 v) {
+  const f32x4v w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4v*>(p));
+}
+
 // Per-round rows: fp32, or fp16 in the compact format (O16).
 template <bool O16>
 struct ORows;
@@ -37,14 +48,16 @@ template <>
 struct ORows<false> {
   typedef float elem;
   __device__ static float4 load4(const float* row, int c4) {
-    return *reinterpret_cast<const float4*>(row + c4);
+    const f32x4v w = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(row + c4));
+    return make_float4(w.x, w.y, w.z, w.w);
   }
 };
 template <>
 struct ORows<true> {
   typedef uint16_t elem;
   __device__ static float4 load4(const uint16_t* row, int c4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(row + c4);
+    const u32x2v w = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(row + c4));
+    const uint2 u = make_uint2(w.x, w.y);
     const half2v lo = __builtin_bit_cast(half2v, u.x), hi = __builtin_bit_cast(half2v, u.y);
     return make_float4((float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y);
   }
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float inv = (1.0f / ws) * unscale;   // times a power of two: exact
     out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
-  *reinterpret_cast<float4*>(y + tok * kHeadDim + c4) = out;
+  store_y_nt(y + tok * kHeadDim + c4, out);
 }
 
 // Any number of rounds: a running softmax over the rounds, one round at a time.
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(256) void combine_many_kernel(
     const float inv = (1.0f / ws) * unscale;
     out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
-  *reinterpret_cast<float4*>(y + tok * kHeadDim + c4) = out;
+  store_y_nt(y + tok * kHeadDim + c4, out);
 }
 
 template <typename T, bool O16>
