@@ -107,6 +107,26 @@ typedef struct {
 lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* rot,
                     int32_t* buckets, uint32_t* fallback_rows, void* stream);
 
+/*
+ * lsh_rot_from_columns -- rotations stored as d x B/2 matrices, rewritten as
+ * the direction rows lsh_hash reads.
+ * Follows: Reformer study note, section "LSH Attention" (the random-rotation
+ * hash; R_{h,r} is a d x B/2 matrix applied to x).
+ *
+ *   rot_cols  [H][R][d][B/2]   dtype  input:  rot_cols[h][r][k][j] = R_{h,r}[k][j]
+ *   rot_rows  [H][R][B/2][d]   dtype  output: rot_rows[h][r][j][k] = R_{h,r}[k][j]
+ *
+ * A transposition of every (head, round) matrix, bits unchanged, enqueued on
+ * `stream`.  Uses cfg's heads, n_rounds, n_buckets, head_dim and dtype (the
+ * other fields must still form a valid configuration; batch and seq_len may be
+ * 0).  Both buffers are device memory owned by the caller, 16-byte aligned,
+ * and must not overlap (LSH_ERR_INVALID_ARGUMENT).  Nothing to do (LSH_OK,
+ * pointers unused) when heads == 0 or n_buckets == 1.  Rotations are
+ * parameters: convert them once and pass rot_rows to every lsh_hash call.
+ */
+lsh_status lsh_rot_from_columns(const lsh_config* cfg, const void* rot_cols, void* rot_rows,
+                                void* stream);
+
 /* Bytes of device workspace lsh_sort needs for cfg (0 for an empty problem). */
 size_t lsh_sort_workspace_bytes(const lsh_config* cfg);
 

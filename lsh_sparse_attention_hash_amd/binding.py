@@ -29,7 +29,7 @@ LSH_BF16 = 1
 LSH_O_F32 = 0
 LSH_O_F16_SCALED = 1
 
-EXPORTS = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_sort_static_scratch",
+EXPORTS = ("lsh_hash", "lsh_rot_from_columns", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_sort_static_scratch",
            "lsh_o_rounds_bytes", "lsh_chunk_attend",
            "lsh_unsort_combine", "lsh_union_workspace_bytes", "lsh_chunk_attend_union",
            "lsh_local_attend", "lsh_project_qkv", "lsh_project_out", "lsh_ffn_workspace_bytes",
@@ -68,6 +68,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     cfgp = ctypes.POINTER(LshConfig)
     lib.lsh_hash.argtypes = [cfgp, P, P, P, P, P]
+    lib.lsh_rot_from_columns.argtypes = [cfgp, P, P, P]
     lib.lsh_sort_workspace_bytes.argtypes = [cfgp]
     lib.lsh_sort_workspace_bytes.restype = SZ
     lib.lsh_sort.argtypes = [cfgp, P, P, P, P, SZ, P]
@@ -91,7 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsh_layer_workspace_bytes.restype = SZ
     lib.lsh_reversible_forward.argtypes = [lcp, lwp, P, P, P, P, P, SZ, P]
     lib.lsh_reversible_inverse.argtypes = [lcp, lwp, P, P, P, P, P, SZ, P]
-    for f in ("lsh_hash", "lsh_sort", "lsh_sort_static_scratch", "lsh_chunk_attend", "lsh_unsort_combine",
+    for f in ("lsh_hash", "lsh_rot_from_columns", "lsh_sort", "lsh_sort_static_scratch", "lsh_chunk_attend", "lsh_unsort_combine",
               "lsh_local_attend", "lsh_chunk_attend_union", "lsh_project_qkv", "lsh_project_out",
               "lsh_ffn", "lsh_reversible_forward", "lsh_reversible_inverse"):
         getattr(lib, f).restype = I32
@@ -168,6 +169,19 @@ def lsh_hash(cfg: LshConfig, qk, rot, buckets, fallback_rows=None, stream=None):
         _expect(fallback_rows, (1,), torch.int32, "fallback_rows")
     _check("lsh_hash", _lib.lsh_hash(ctypes.byref(cfg), _ptr(qk), _ptr(rot) if B > 1 else None,
                                      _ptr(buckets), _ptr(fallback_rows), _stream(stream)))
+
+
+def lsh_rot_from_columns(cfg: LshConfig, rot_cols, rot_rows, stream=None):
+    """rot_cols [H][R][d][B/2] (each rotation as a d x B/2 matrix) -> rot_rows
+    [H][R][B/2][d], the layout lsh_hash reads."""
+    H, R, d, B = cfg.heads, cfg.n_rounds, cfg.head_dim, cfg.n_buckets
+    dt = _dtype_of(cfg)
+    if B > 1 and H > 0:
+        _expect(rot_cols, (H, R, d, B // 2), dt, "rot_cols")
+        _expect(rot_rows, (H, R, B // 2, d), dt, "rot_rows")
+    _check("lsh_rot_from_columns",
+           _lib.lsh_rot_from_columns(ctypes.byref(cfg), _ptr(rot_cols), _ptr(rot_rows),
+                                     _stream(stream)))
 
 
 def lsh_sort_workspace_bytes(cfg: LshConfig) -> int:

@@ -37,7 +37,11 @@ HEADERS = ["lsh_device.h", "lsh_launch.h"]
 def source_digest() -> str:
     """Digest of everything the library is built from: the kernel and host
     sources, the internal headers, include/lsh.h and the compiler flags."""
-    h = hashlib.sha256(" ".join(HIPFLAGS).encode())
+    # include directories as paths relative to the repository, so that a copy
+    # of the tree elsewhere (another machine) computes the same digest
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    flags = [os.path.relpath(f, root) if f in (INCLUDE, CSRC) else f for f in HIPFLAGS]
+    h = hashlib.sha256(" ".join(flags).encode())
     paths = [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(INCLUDE, "lsh.h")]
     for path in paths:
         h.update(os.path.basename(path).encode())

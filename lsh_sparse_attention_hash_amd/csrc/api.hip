@@ -155,6 +155,23 @@ lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* rot, int3
                   "lsh_hash");
 }
 
+lsh_status lsh_rot_from_columns(const lsh_config* cfg, const void* rot_cols, void* rot_rows,
+                                void* stream) {
+  lsh::Shape s;
+  bool empty = false;
+  LSH_TRY(check_config(cfg, &s, &empty));
+  if (s.heads == 0 || s.buckets == 1) return ok();   // no rotation to convert
+  LSH_TRY(check_ptr(rot_cols, "rot_cols"));
+  LSH_TRY(check_ptr(rot_rows, "rot_rows"));
+  const size_t bytes = (size_t)s.heads * s.rounds * (s.buckets / 2) * lsh::kHeadDim *
+                       (s.bf16 ? sizeof(uint16_t) : sizeof(float));
+  const uintptr_t a = reinterpret_cast<uintptr_t>(rot_cols), b = reinterpret_cast<uintptr_t>(rot_rows);
+  if (a < b + bytes && b < a + bytes)
+    return fail(LSH_ERR_INVALID_ARGUMENT, "rot_cols and rot_rows overlap");
+  return launched(lsh::launch_rot_rows(s, rot_cols, rot_rows, static_cast<hipStream_t>(stream)),
+                  "lsh_rot_from_columns");
+}
+
 size_t lsh_sort_workspace_bytes(const lsh_config* cfg) {
   lsh::Shape s;
   bool empty = false;

@@ -638,4 +638,50 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Rotations given as d x B/2 matrices ([H][R][d][B/2], rot_cols[h][r][k][j] =
+// R_{h,r}[k][j]) rewritten as the direction rows the kernels above read
+// ([H][R][B/2][d]).  One workgroup per (matrix, block of 64 directions): the
+// 64 x 64 block goes through LDS, read along directions and written along k,
+// so both sides are coalesced.  Bits are copied unchanged.
+template <typename T>
+__global__ __launch_bounds__(256) void rot_rows_kernel(const T* __restrict__ cols,
+                                                       T* __restrict__ rows, int half,
+                                                       int blocks_per_matrix, int64_t blk0) {
+  __shared__ T tile[kHeadDim][kHeadDim + 1];   // [direction][k], padded
+  const int64_t blk = blk0 + blockIdx.x;
+  const int64_t mat = blk / blocks_per_matrix;
+  const int j0 = (int)(blk % blocks_per_matrix) * kHeadDim;
+  const T* src = cols + mat * kHeadDim * (int64_t)half;
+  T* dst = rows + mat * (int64_t)half * kHeadDim;
+  for (int idx = threadIdx.x; idx < kHeadDim * kHeadDim; idx += 256) {
+    const int k = idx / kHeadDim, j = idx % kHeadDim;
+    if (j0 + j < half) tile[j][k] = src[(int64_t)k * half + j0 + j];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kHeadDim * kHeadDim; idx += 256) {
+    const int j = idx / kHeadDim, k = idx % kHeadDim;
+    if (j0 + j < half) dst[(int64_t)(j0 + j) * kHeadDim + k] = tile[j][k];
+  }
+}
+
+hipError_t launch_rot_rows(const Shape& s, const void* rot_cols, void* rot_rows,
+                           hipStream_t stream) {
+  const int half = s.buckets / 2;
+  const int per = (half + kHeadDim - 1) / kHeadDim;
+  const int64_t nblk = (int64_t)s.heads * s.rounds * per;
+  for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks) {
+    const dim3 grid((unsigned)std::min(kMaxBlocks, nblk - b0));
+    if (s.bf16)
+      hipLaunchKernelGGL(rot_rows_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(rot_cols), static_cast<uint16_t*>(rot_rows),
+                         half, per, b0);
+    else
+      hipLaunchKernelGGL(rot_rows_kernel<float>, grid, dim3(256), 0, stream,
+                         static_cast<const float*>(rot_cols), static_cast<float*>(rot_rows), half,
+                         per, b0);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace lsh

@@ -18,6 +18,9 @@ struct Shape {
 
 hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t* buckets,
                        uint32_t* fallback_rows, hipStream_t stream);
+// Rotations [H][R][d][B/2] -> [H][R][B/2][d] (the rows launch_hash reads).
+hipError_t launch_rot_rows(const Shape& s, const void* rot_cols, void* rot_rows,
+                           hipStream_t stream);
 
 // Sort tiling: each segment is cut into tiles of sort_tile(s) tokens.
 int sort_tile(const Shape& s);
@@ -30,10 +33,10 @@ size_t static_sort_scratch_bytes();
 hipError_t static_sort_scratch(int device, void** ptr);
 
 // Per-round outputs.  fp32 rows [S][L][64] (any input dtype), or with o16: a
-// header of kVParts partial maxima of |v| per (batch, head) (fp32, padded to
-// 256 bytes), then fp16 rows [S][L][64] holding o * 2^-k, with k the
-// (batch, head)'s scale exponent (o_scale_exponent of the header's maximum;
-// kVParts and the rule are in lsh_device.h).
+// header of kVParts partial maxima of |v| per (batch, head) (fp32) followed by
+// the int32 scale exponent k of each (batch, head), padded to 256 bytes, then
+// fp16 rows [S][L][64] holding o * 2^-k (o_scale_exponent of the head's
+// maximum; kVParts and the rule are in lsh_device.h).
 size_t o_header_bytes(const Shape& s);
 size_t o_rounds_bytes(const Shape& s);
 

@@ -322,3 +322,23 @@ def test_static_scratch_sort_validates_before_any_launch():
     assert b"static scratch" in lib.lsh_last_error()
     empty = cfg(seq_len=0)
     assert lib.lsh_sort_static_scratch(ctypes.byref(empty), None, None, None, None) == B.LSH_OK
+
+
+def test_rotation_conversion_validates_before_any_launch():
+    lib = B.library()
+    conv = lambda c, src, dst: lib.lsh_rot_from_columns(ctypes.byref(c), src, dst, None)
+    c = cfg()
+    assert conv(c, None, FAKE) == B.LSH_ERR_INVALID_ARGUMENT
+    assert b"rot_cols" in lib.lsh_last_error()
+    assert conv(c, FAKE, None) == B.LSH_ERR_INVALID_ARGUMENT
+    assert conv(c, FAKE, ctypes.c_void_p(0x20008)) == B.LSH_ERR_INVALID_ARGUMENT   # misaligned
+    # 2 heads x 2 rounds x 4 directions x 64 bf16 = 2,048 bytes: overlapping buffers rejected
+    assert conv(c, ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10000 + 1024)) == \
+        B.LSH_ERR_INVALID_ARGUMENT
+    assert b"overlap" in lib.lsh_last_error()
+    assert conv(cfg(dtype=7), FAKE, FAKE) == B.LSH_ERR_INVALID_ARGUMENT
+    assert conv(cfg(head_dim=32), FAKE, FAKE) == B.LSH_ERR_UNSUPPORTED
+    # nothing to convert: no heads, or no hashing
+    assert conv(cfg(heads=0), None, None) == B.LSH_OK
+    assert conv(cfg(n_buckets=1), None, None) == B.LSH_OK
+    assert lib.lsh_rot_from_columns(None, FAKE, FAKE, None) == B.LSH_ERR_INVALID_ARGUMENT

@@ -406,3 +406,34 @@ def test_fp32_hash_beyond_one_dispatch(B):
     ref = oracle.hash_rows(qk.astype(np.float64), rot.astype(np.float64), 2, R, idx)
     assert np.array_equal(got[idx], ref)
     assert set(np.unique(got)) <= {0, 1}
+
+
+@pytest.mark.parametrize("dtype,n_buckets", [("bf16", 1024), ("bf16", 38), ("f32", 200)])
+def test_rotations_given_as_columns(B, dtype, n_buckets):
+    """lsh_rot_from_columns: rotations stored as d x B/2 matrices come out as
+    the direction rows lsh_hash reads, bit for bit (against a NumPy
+    transpose), and hashing with them equals the oracle's hash of the same
+    matrices."""
+    H, R, L = 3, 2, 1024
+    half = n_buckets // 2
+    w = synth.Workload(f"rotcols_{dtype}_{n_buckets}", 1, H, L, 64, n_buckets, R, 64, True, True,
+                       dtype, 61)
+    g = np.random.default_rng(62)
+    cols = g.standard_normal((H, R, 64, half)).astype(np.float32)   # R_{h,r}[k][j]
+    qk = g.standard_normal((1, H, L, 64)).astype(np.float32)
+    to_dev = lambda a: B.to_device(synth.bf16_bits(a) if dtype == "bf16" else a, dtype)
+    cfg = B.config_for(w)
+    cols_d = to_dev(cols)
+    rows_d = torch.empty((H, R, half, 64), dtype=cols_d.dtype, device="cuda")
+    B.lsh_rot_from_columns(cfg, cols_d, rows_d)
+    torch.cuda.synchronize()
+    bits = lambda t: host(t.view(torch.int16) if t.dtype == torch.bfloat16 else t)
+    want = np.ascontiguousarray(np.swapaxes(bits(cols_d), 2, 3))
+    assert np.array_equal(bits(rows_d), want)
+    bk = torch.empty((1, H, R, L), dtype=torch.int32, device="cuda")
+    qk_d = to_dev(qk)
+    B.lsh_hash(cfg, qk_d, rows_d, bk)
+    torch.cuda.synchronize()
+    rows64 = np.swapaxes(synth.to_f64(synth.bf16_bits(cols) if dtype == "bf16" else cols, dtype), 2, 3)
+    qk64 = synth.to_f64(synth.bf16_bits(qk) if dtype == "bf16" else qk, dtype)
+    assert np.array_equal(host(bk), oracle.hash(qk64, np.ascontiguousarray(rows64), n_buckets, R))
