@@ -384,7 +384,7 @@ def bench_local(args, w, inputs, binding, torch):
     loc = binding.Local(binding.config_for(w), w.look_before, w.look_after)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        loc.run(qk, v)
+        loc.run(qk, v, stream)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -394,7 +394,7 @@ def bench_local(args, w, inputs, binding, torch):
     start.record(stream)
     for k in range(args.steps):
         ev[k][0].record(stream)
-        loc.run(qk, v)
+        loc.run(qk, v, stream)
         ev[k][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
