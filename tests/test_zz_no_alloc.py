@@ -60,3 +60,29 @@ def test_static_scratch_sort_equals_workspace_sort(B):
         p, i = oracle.sort(bk.cpu().numpy())
         assert np.array_equal(perm.cpu().numpy(), p) and np.array_equal(inv.cpu().numpy(), i)
         say(f"[no-alloc] {name}: perm and inv_perm equal the workspace sort and the oracle")
+
+
+def test_static_scratch_sort_more_than_2048_buckets(B):
+    """The same for the four-launch sort of more than 2,048 buckets, whose
+    static array also holds the bucket bases: 8,192 buckets, then 4,096."""
+    lib = B.library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for w in (synth.Workload("nb8192", 1, 2, 131072, 64, 8192, 2, 64, True, True, "bf16", 71),
+              synth.Workload("nb4096", 1, 1, 65536, 64, 4096, 2, 64, True, True, "bf16", 72)):
+        say(f"[no-alloc] {w}")
+        cfg, bk = _buckets(B, w)
+        ref_perm, ref_inv = torch.empty_like(bk), torch.empty_like(bk)
+        ws = torch.empty(max(16, B.lsh_sort_workspace_bytes(cfg)), dtype=torch.uint8,
+                         device="cuda")
+        B.lsh_sort(cfg, bk, ref_perm, ref_inv, ws)
+        perm = torch.full_like(bk, -1)
+        inv = torch.full_like(bk, -1)
+        st = lib.lsh_sort_static_scratch(ctypes.byref(cfg), ctypes.c_void_p(bk.data_ptr()),
+                                         ctypes.c_void_p(perm.data_ptr()),
+                                         ctypes.c_void_p(inv.data_ptr()), stream)
+        assert st == B.LSH_OK, lib.lsh_last_error()
+        torch.cuda.synchronize()
+        assert torch.equal(perm, ref_perm) and torch.equal(inv, ref_inv)
+        p, i = oracle.sort(bk.cpu().numpy())
+        assert np.array_equal(perm.cpu().numpy(), p) and np.array_equal(inv.cpu().numpy(), i)
+        say(f"[no-alloc] {w.name}: perm and inv_perm equal the workspace sort and the oracle")
