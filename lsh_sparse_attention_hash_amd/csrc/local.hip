@@ -213,10 +213,11 @@ __global__ __launch_bounds__(256) void local_bf16_kernel(LocalArgs a) {
       __syncthreads();
     }
   } else {
+    // unconditional (chunks past the window repeat the last one, unused), so
+    // that the first chunk is committed as soon as its own rows are in
     KeyRegs kr[NPRE];
 #pragma unroll
-    for (int i = 0; i < NPRE; ++i)
-      if (k0 + i <= k1) gather_keys(kr[i], xb, vb, k0 + i);
+    for (int i = 0; i < NPRE; ++i) gather_keys(kr[i], xb, vb, min(k0 + i, k1));
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) {
       if (k0 + i > k1) break;
