@@ -670,6 +670,13 @@ def main():
                 "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     roof["traffic"] = measured_traffic(dom, w.name + ("_union" if args.union else ""))
+    # what the HIP events around the call time (one ABI call can launch two
+    # kernels; the traffic is that of the same kernels)
+    roof["timed"] = {"hash": "lsh_hash: hash_bf16_kernel + hash_settle_kernel",
+                     "attend": ("lsh_chunk_attend_union: union_keys_kernel + vmax_kernel + "
+                                "attend_bf16_kernel" if args.union else
+                                "lsh_chunk_attend: vmax_kernel + attend_bf16_kernel"),
+                     "combine": "lsh_unsort_combine: combine_kernel"}[dom]
 
     result = {
         "metric": METRIC if not args.union else
