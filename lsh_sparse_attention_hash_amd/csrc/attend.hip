@@ -60,6 +60,10 @@ struct AttendArgs {
 };
 
 constexpr int kMaxUnionRounds = 16;
+// Set union: the query-side stand-in for rounds a test skips.  (kUnionNoKey -
+// w) is 0 or 1 only for w = -4 or -5, and table entries are keys (>= 0) or
+// padding (-2).
+constexpr int32_t kUnionNoKey = -4;
 
 // ------------------------------------------------------------------- bf16
 // V^T rows hold the 128 window keys as 64 dwords (two bf16 keys each) plus 4
@@ -284,9 +288,11 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
       // each key of the union is attended in the first round that finds it:
       // it is left out here if an earlier round has it as a candidate of this
       // query (same bucket, and its sorted slot in the query's chunk or the
-      // one before: round-key difference 0 or 1).  Query round keys of rounds
-      // from rnd on are replaced by 2^30, which never matches (keys >= -2).
-      // (any difference <= 1 iff the smallest, as unsigned, is)
+      // one before: round-key difference 0 or 1).  The query's entries for
+      // rounds from rnd on are replaced by -4, which lies within 1 of no table
+      // entry: keys are >= 0 and padding is -2, while later rounds' keys can be
+      // any value below 2^31.  (Any difference is 0 or 1 iff the smallest, as
+      // unsigned, is at most 1.)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t dmin = ~0u;
@@ -294,9 +300,9 @@ __device__ __forceinline__ void attend_chunk_bf16(AttendLds& sm, const AttendArg
         for (int q4 = 0; q4 < UR; q4 += 4) {
           if (q4 < rnd) {
             int4 kq = *reinterpret_cast<const int4*>(ukey_block<UR>(sm, kkey, qrow, q4 / 4));
-            if (q4 + 1 >= rnd) kq.y = 1 << 30;
-            if (q4 + 2 >= rnd) kq.z = 1 << 30;
-            if (q4 + 3 >= rnd) kq.w = 1 << 30;
+            if (q4 + 1 >= rnd) kq.y = kUnionNoKey;
+            if (q4 + 2 >= rnd) kq.z = kUnionNoKey;
+            if (q4 + 3 >= rnd) kq.w = kUnionNoKey;
             const int4 w = *reinterpret_cast<const int4*>(ukey_block<UR>(sm, kkey, row4 + i, q4 / 4));
             dmin = min(min(dmin, (uint32_t)(kq.x - w.x)),
                        min(min((uint32_t)(kq.y - w.y), (uint32_t)(kq.z - w.z)),
@@ -628,8 +634,8 @@ __global__ __launch_bounds__(256) void union_keys_kernel(const int32_t* __restri
   const int pos = (int)(g % L);
   const int span = L / kChunk + 1;
   // every round's bucket and slot requested at once (rounds past the last
-  // repeat its addresses); padding keys are -2, and the query side pads with
-  // 2^30, so a padded round never matches
+  // repeat its addresses); padding keys are -2 (the attention masks the
+  // rounds a test must skip with kUnionNoKey, -4: no entry lies within 1 of it)
   int32_t bk[RMAX], ip[RMAX];
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {

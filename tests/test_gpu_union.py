@@ -163,3 +163,42 @@ def test_union_attention_of_any_permutation(B, name):
                                              w.causal, w.self_mask)
         close(host(f.lse), lse_ref, tol, f"lse ({kind})")
         close(read_o_rounds(host(f.o_rounds), w), o_ref, tol, f"o_rounds ({kind})")
+
+
+def test_union_round_keys_near_2_pow_30(B):
+    """Round keys bucket * (C + 1) + chunk reach 2^30 once B * (C + 1) does
+    (here B = 16,384 and C + 1 = 65,537 at 4,194,304 tokens).  Buckets are
+    given directly: random in round 0, all 16,383 in round 1, so the round-1
+    keys of chunks 49,152 and 49,153 are 2^30 - 1 and 2^30.  The stand-in the
+    kernel gives the rounds a test skips must not match them: every row of
+    those windows in round 1 (and random rows of both rounds) against the
+    oracle."""
+    L, nb, R = 4194304, 16384, 2
+    w = synth.Workload("u_big_keys", 1, 1, L, 64, nb, R, 64, True, True, "bf16", 63,
+                       o_format="f32")
+    g = np.random.default_rng(64)
+    bk = np.empty((1, 1, R, L), np.int32)
+    bk[0, 0, 0] = g.integers(0, nb, L, dtype=np.int32)
+    bk[0, 0, 1] = nb - 1
+    assert (nb - 1) * (L // 64 + 1) + 49153 == 1 << 30
+    perm, inv = oracle.sort(bk)
+    qk = synth.bf16_bits(g.standard_normal((1, 1, L, 64)).astype(np.float32))
+    v = synth.bf16_bits(g.standard_normal((1, 1, L, 64)).astype(np.float32))
+    f = B.Forward(B.config_for(w))
+    f.buckets.copy_(torch.from_numpy(bk))
+    f.perm.copy_(torch.from_numpy(perm))
+    f.inv_perm.copy_(torch.from_numpy(inv))
+    f.attend_union(B.to_device(qk, "bf16"), B.to_device(v, "bf16"))
+    torch.cuda.synchronize()
+    crit = L + np.arange(49151 * 64, 49156 * 64)          # round 1, chunks 49,151 .. 49,155
+    rows = np.concatenate([crit, g.integers(0, R * L, 1000)])
+    o_ref, lse_ref = oracle.attend_union_rows(synth.to_f64(qk, "bf16"), synth.to_f64(v, "bf16"),
+                                              bk, perm, inv, nb, 64, True, True, rows)
+    idx = torch.from_numpy(rows).cuda()
+    o_gpu = host(f.o_rounds[:R * L * 64 * 4].view(torch.float32).view(R * L, 64)[idx])
+    lse_gpu = host(f.lse.view(-1)[idx])
+    close(lse_gpu, lse_ref, 2e-2, "lse")
+    close(o_gpu, o_ref, 2e-2, "o_rounds")
+    # the round-1 windows of those chunks keep their keys
+    assert np.isfinite(lse_gpu[64:len(crit)]).all()
+    say("[union] round keys at 2^30: 1,320 rows of o_rounds / lse within tolerance")
