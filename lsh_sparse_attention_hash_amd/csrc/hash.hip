@@ -3,13 +3,13 @@
 // bucket = first argmax of [x R ; -x R]) for every token and round.
 //
 // bf16 inputs: x R is contracted on the matrix cores (v_mfma_f32_32x32x16_bf16,
-// exact bf16 products, fp32 accumulation).  The epilogue keeps, per token, the
-// two largest |x R_j| as packed keys (magnitude bits with the direction's
-// offset in its tile in the low mantissa bits) and the tile of the largest.
-// A row is accepted only when the gap between the two best candidates exceeds
-// twice a bound on the fp32 accumulation error (plus the fp64 rounding of the
+// exact bf16 products, fp32 accumulation).  Per token the epilogue tracks the
+// largest |x R_j|, its direction, and a bound on every other score, in one of
+// two forms (below, chosen by the number of directions).  A row is accepted
+// only when the gap between its best score and every other exceeds twice a
+// bound on the fp32 accumulation error (plus the fp64 rounding of the
 // defining sum), so that its bucket is provably the one of the fp64
-// definition; the winner's sign then comes from an exact-sign dot product.
+// definition; the winner's sign comes from a recomputed dot product.
 // Other rows are marked (with a lower bound on their best score) and settled
 // by a second kernel, which scores them again with per-direction error bounds
 // and recomputes the few directions that can reach the maximum in fp64, in
@@ -31,6 +31,7 @@ constexpr int kHashTokWave = 64;                       // two 32-token MFMA colu
 constexpr int kHashTokWG = kHashWaves * kHashTokWave;  // 256 tokens per workgroup
 constexpr int kStageRows = 128;                        // rotation rows staged per LDS pass
 constexpr int kRowStride = 72;                         // bf16 per staged row (144 B, padded)
+
 
 // ---------------------------------------------------------------------------
 // Exact bucket of one token, computed by one wave in the defining arithmetic:
@@ -75,12 +76,191 @@ __device__ int exact_bucket(const double* x, const T* rot_hr, int half) {
 }
 
 // ---------------------------------------------------------------------------
-// Keys: the fp32 score with its 5 low mantissa bits replaced by the direction's
-// offset inside its 32-direction tile (the lane-half bit 4 of that offset is
-// added after the halves merge).  Magnitude keys |key| order like |score| up to
-// that truncation; the tile of the running maximum is tracked per lane.
+// Epilogues.  Register i of a lane holds the score of direction
+// 32 t + 8 (i / 4) + 4 (lane / 32) + i % 4 of tile t for token lane % 32; the
+// two lanes l and l ^ 32 of a token see disjoint halves of every tile and
+// merge after the round.  finish() returns, the same in both lanes of the
+// token unless their halves tie (then w1 <= upper2 and the row is not
+// certified): the winning direction, a lower bound w1 on its matrix-core
+// |score|, an upper bound on the matrix-core |score| of every other direction
+// (or, for recomputed ones, on their recomputed value), and the winner's
+// recomputed signed value.  A recomputed score (the two lanes of the token
+// each dot their 32 k-values with the direction row: exact bf16 products,
+// fp32 sums) lies within E of the defining sum, like any fp32 sum of these
+// 64 products.
+struct Cand {
+  uint32_t j;
+  float w1, upper2, value;
+};
+
+// The recomputed signed scores of n consecutive directions j0 .. j0 + n - 1
+// for the token of this lane pair.  Every 16-byte piece of a pair of rows is
+// requested before any of them is used.  The descriptor covers the rotation's half
+// directions, so rows past half read as zero and score 0, as in the padded
+// tile.
+template <int N>
+__device__ __forceinline__ void recompute(float (&v)[N], __amdgpu_buffer_rsrc_t rrs, uint32_t j0,
+                                          const bf16x8 (&x)[4]) {
+  const uint32_t lane_off = 16u * (lane_id() >> 5);
+#pragma unroll
+  for (int e0 = 0; e0 < N; e0 += 2) {
+    constexpr int kPair = N < 2 ? N : 2;
+    uint4 rv[kPair][4];
+#pragma unroll
+    for (int e = 0; e < kPair; ++e)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        rv[e][ks] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rrs, (j0 + e0 + e) * (uint32_t)(kHeadDim * 2) + lane_off + 32u * ks, 0, 0));
+    // (two rows: keep the scheduler from splitting the requests again)
+    if constexpr (N > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < kPair; ++e) {
+      float part = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 xv = __builtin_bit_cast(uint4, x[ks]);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.x), __builtin_bit_cast(bf16x2, rv[e][ks].x), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.y), __builtin_bit_cast(bf16x2, rv[e][ks].y), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.z), __builtin_bit_cast(bf16x2, rv[e][ks].z), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.w), __builtin_bit_cast(bf16x2, rv[e][ks].w), part, false);
+      }
+      v[e0 + e] = part + other_half(part);
+    }
+  }
+}
+
+// Keys (fewer directions): every score becomes a key, the fp32 score with its
+// 5 low mantissa bits replaced by the direction's offset in the lane's half
+// of the tile; the two largest keys are kept (a max3 and a med3 per two
+// scores) with the tile of the first.  Magnitude keys order like |score| up
+// to that truncation, which the bounds widen by 32 units in the last place.
+// Only the winner is recomputed, for its sign.
 constexpr uint32_t kKeyMask = ~31u;
 
+struct KeyEpilogue {
+  float m1, m2;
+  int wt;
+  __device__ __forceinline__ void reset() {
+    m1 = m2 = 0.f;
+    wt = 0;
+  }
+  __device__ __forceinline__ void tile(const f32x16& acc, int t) {
+    const float before = m1;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const uint32_t off = 8 * (i >> 2) + (i & 3);
+      const uint32_t ka = (__float_as_uint(acc[i]) & kKeyMask) | off;
+      const uint32_t kb = (__float_as_uint(acc[i + 1]) & kKeyMask) | (off + 1);
+      const float aa = fabsf(__uint_as_float(ka)), ab = fabsf(__uint_as_float(kb));
+      const float n1 = fmaxf(m1, fmaxf(aa, ab));
+      m2 = fmaxf(m2, __builtin_amdgcn_fmed3f(m1, aa, ab));
+      m1 = n1;
+    }
+    wt = (__float_as_uint(m1) != __float_as_uint(before)) ? t : wt;
+  }
+  __device__ __forceinline__ Cand finish(__amdgpu_buffer_rsrc_t rrs, const bf16x8 (&x)[4]) const {
+    const uint32_t own_j = 32u * wt + (__float_as_uint(m1) & 31u) + 4u * (lane_id() >> 5);
+    const float pm1 = other_half(m1);
+    const float pm2 = other_half(m2);
+    const uint32_t other_j = other_half(own_j);
+    const bool other = pm1 > m1;
+    const float w1 = other ? pm1 : m1;
+    const float w2 = fmaxf(fminf(m1, pm1), fmaxf(m2, pm2));
+    Cand c;
+    c.j = other ? other_j : own_j;
+    float v[1];
+    recompute<1>(v, rrs, c.j, x);
+    c.value = v[0];
+    c.w1 = __uint_as_float(__float_as_uint(w1) & kKeyMask);
+    c.upper2 = __uint_as_float((__float_as_uint(w2) & kKeyMask) + 32u);
+    return c;
+  }
+};
+
+// Quads (many directions): registers 4q .. 4q + 3 form quad q (four
+// neighbouring directions).  Per round the epilogue keeps each quad's largest
+// |score| over the tiles and the two largest tile maxima with the tile of the
+// first: two 3-input maxima per quad and tile, about half the operations of
+// the keys per score.  The largest score of the lane lies in the winning quad
+// of the winning tile; every other score is bounded by the second tile
+// maximum, by the other quads' maxima, or lies in the winning quad, whose
+// four scores are recomputed after the round (512 bytes of rows per token and
+// round, repaid only when a round has many tiles).
+struct QuadEpilogue {
+  float pm[4], t1, t2;
+  int wt;
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pm[q] = 0.f;
+    t1 = t2 = 0.f;
+    wt = 0;
+  }
+  // IEEE-754 maximum (v_maximum3_f32): the scores are finite, and unlike
+  // fmaxf it takes the raw matrix-core results without first quieting each
+  // one (an extra instruction per score)
+  static __device__ __forceinline__ float vmax(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+  }
+  __device__ __forceinline__ void tile(const f32x16& acc, int t) {
+    float qm[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      qm[q] = vmax(vmax(fabsf(acc[4 * q]), vmax(fabsf(acc[4 * q + 1]), fabsf(acc[4 * q + 2]))),
+                   fabsf(acc[4 * q + 3]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pm[q] = vmax(pm[q], qm[q]);
+    const float tm = vmax(vmax(qm[0], vmax(qm[1], qm[2])), qm[3]);
+    // t1 >= t2 throughout; the first tile reaching the maximum keeps it
+    wt = tm > t1 ? t : wt;
+    t2 = __builtin_amdgcn_fmed3f(t1, t2, tm);
+    t1 = vmax(t1, tm);
+  }
+  __device__ __forceinline__ Cand finish(__amdgpu_buffer_rsrc_t rrs, const bf16x8 (&x)[4]) const {
+    // the quad holding the lane's largest score (first quad on equal values),
+    // and the largest of the other quads; s1 == t1
+    float s1 = pm[0], s2 = 0.f;
+    int qs = 0;
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      qs = pm[q] > s1 ? q : qs;
+      s2 = __builtin_amdgcn_fmed3f(s1, s2, pm[q]);
+      s1 = fmaxf(s1, pm[q]);
+    }
+    // u2 bounds every other score of the lane outside the winning quad
+    const float u2 = fmaxf(t2, s2);
+    const uint32_t own_j = 32u * wt + 8u * qs + 4u * (lane_id() >> 5);
+    const float pm1 = other_half(t1);
+    const float pu2 = other_half(u2);
+    const uint32_t other_j = other_half(own_j);
+    const bool other = pm1 > t1;
+    const uint32_t j0 = other ? other_j : own_j;
+    float v[4];
+    recompute<4>(v, rrs, j0, x);
+    // The direction with the largest |value| is taken (the first on equal
+    // values).  Had the matrix-core maximum been another one of the quad,
+    // that one's |value| would be at least w1 - 2E and the row is not
+    // certified.
+    float vpart = 0.f;
+    Cand c;
+    c.j = j0;
+    c.value = v[0];
+#pragma unroll
+    for (int e = 1; e < 4; ++e) {
+      const bool gt = fabsf(v[e]) > fabsf(c.value);
+      vpart = fmaxf(vpart, gt ? fabsf(c.value) : fabsf(v[e]));
+      c.j = gt ? j0 + e : c.j;
+      c.value = gt ? v[e] : c.value;
+    }
+    c.w1 = other ? pm1 : t1;
+    // the losing half's scores are at most its maximum
+    c.upper2 = fmaxf(fmaxf(fminf(t1, pm1), fmaxf(u2, pu2)), vpart);
+    return c;
+  }
+};
+// quads for more than this many directions (32 tiles per round)
+constexpr int kQuadMinHalf = 1024;
 
 // Stage st of a round: rows [128 st, 128 st + 128) of the rotation, 1024
 // pieces of 16 B, 4 per thread.  The descriptor covers only the stage's rows
@@ -109,14 +289,18 @@ __device__ __forceinline__ void stage_store(uint16_t* dst, const uint4 (&buf)[4]
 
 // At most 128 VGPRs (the second bound): four waves per SIMD hide more of the
 // matrix-core and LDS latency than three with more registers each.
+template <typename Epilogue>
 __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
     const uint16_t* __restrict__ qk, const uint16_t* __restrict__ rot,
     int32_t* __restrict__ buckets, int heads, int L, int half, int rounds) {
   __shared__ __attribute__((aligned(16))) uint16_t rs[2][kStageRows * kRowStride];
   __shared__ float gram_part[kHashWaves];
+  // |x| of every token of the workgroup, read once per round for the error
+  // bound (held in registers it would push the quad epilogue past 128)
+  __shared__ float xnorm_s[2][kHashTokWG];
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
   // each XCD takes a contiguous range of (batch, head, token block): its L2
   // then holds the rotations of one or two heads instead of all of them
   const int nblk = (L + kHashTokWG - 1) / kHashTokWG;
@@ -131,7 +315,6 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
   // All eight pieces are requested before any is used.  The descriptor covers
   // the wave's tokens below L, so the rows of tokens past L read as zero.
   bf16x8 xf[2][4];
-  float xnorm[2];
   {
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(xbase + (size_t)min(tok_wave, L) * kHeadDim), (short)0,
@@ -158,8 +341,8 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
         ss += a * a + b * b;
       }
     }
-    ss += __shfl_xor(ss, 32);
-    xnorm[nb] = sqrtf(ss);
+    ss += other_half(ss);
+    xnorm_s[nb][threadIdx.x] = sqrtf(ss);   // lanes l and l ^ 32 hold the same value
   }
 
   const int nstages = (half + kStageRows - 1) / kStageRows;
@@ -167,8 +350,9 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
 
   for (int r = 0; r < rounds; ++r) {
     const uint16_t* rhr = rot + ((size_t)h * rounds + r) * (size_t)half * kHeadDim;
-    float m1[2] = {0.f, 0.f}, m2[2] = {0.f, 0.f};
-    int wt[2] = {0, 0};
+    Epilogue ep[2];
+    ep[0].reset();
+    ep[1].reset();
     float gmax = 0.f;
 
     uint4 buf[4];
@@ -217,20 +401,7 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], xf[nb][ks], acc, 0, 0, 0);
-          // Output layout: register i of lane l is direction 32*tile + 8*(i/4) + 4*(l/32) + i%4
-          // of token l%32.
-          const float before = m1[nb];
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            const uint32_t off = 8 * (i >> 2) + (i & 3);
-            const uint32_t ka = (__float_as_uint(acc[i]) & kKeyMask) | off;
-            const uint32_t kb = (__float_as_uint(acc[i + 1]) & kKeyMask) | (off + 1);
-            const float aa = fabsf(__uint_as_float(ka)), ab = fabsf(__uint_as_float(kb));
-            const float n1 = fmaxf(m1[nb], fmaxf(aa, ab));
-            m2[nb] = fmaxf(m2[nb], __builtin_amdgcn_fmed3f(m1[nb], aa, ab));
-            m1[nb] = n1;
-          }
-          wt[nb] = (__float_as_uint(m1[nb]) != __float_as_uint(before)) ? tile : wt[nb];
+          ep[nb].tile(acc, tile);
         }
       }
       if (more) {
@@ -240,8 +411,7 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
     }
 
     // Largest direction norm of this rotation (all waves' Gram tiles).
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off));
+    gmax = wave_max(gmax);
     if (lane == 0) gram_part[wave] = gmax;
     __syncthreads();
     float g2 = gram_part[0];
@@ -250,36 +420,12 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
     const float rcol = sqrtf(g2 * (1.0f + 0x1p-10f));
 
     int32_t* bout = buckets + (bh * rounds + r) * (size_t)L;
+    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(uniform_ptr(rhr)), (short)0, half * kHeadDim * (int)sizeof(uint16_t),
+        kBufferWord3);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const uint32_t own_j = 32u * wt[nb] + (__float_as_uint(m1[nb]) & 31u) + 4u * (lane >> 5);
-      const float pm1 = __shfl_xor(m1[nb], 32);
-      const float pm2 = __shfl_xor(m2[nb], 32);
-      const uint32_t other_j = __shfl_xor(own_j, 32);
-      const bool other = pm1 > m1[nb];
-      const float w1 = other ? pm1 : m1[nb];
-      const float w2 = fmaxf(fminf(m1[nb], pm1), fmaxf(m2[nb], pm2));
-      const uint32_t jstar = other ? other_j : own_j;   // the same in lanes l and l^32
-      // Sign of the winning score x.R_j*: the two lanes of the token each dot
-      // their 32 k-values with the winner's direction row (exact bf16 products,
-      // fp32 sums).  On a certified row |x.R_j*| > 2E exceeds the error of any
-      // fp32 sum of these 64 products, so the computed sign is exact.
-      float part = 0.f;
-      {
-        const uint16_t* jrow = rhr + (size_t)min(jstar, (uint32_t)(half - 1)) * kHeadDim + 8 * (lane >> 5);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const uint4 rv = load16(jrow + 16 * ks);
-          const uint4 xv = __builtin_bit_cast(uint4, xf[nb][ks]);
-          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.x), __builtin_bit_cast(bf16x2, rv.x), part, false);
-          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.y), __builtin_bit_cast(bf16x2, rv.y), part, false);
-          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.z), __builtin_bit_cast(bf16x2, rv.z), part, false);
-          part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xv.w), __builtin_bit_cast(bf16x2, rv.w), part, false);
-        }
-      }
-      const bool pos = part + __shfl_xor(part, 32) > 0.f;
-      const float lower1 = __uint_as_float(__float_as_uint(w1) & kKeyMask);
-      const float upper2 = __uint_as_float((__float_as_uint(w2) & kKeyMask) + 32u);
+      const Cand c = ep[nb].finish(rrs, xf[nb]);
       // |fp32 MFMA score - exact| <= 64 * 2^-23 * sum_k |x_k R_kj| <= 64 * 2^-23 |x| |R_j|
       // when each of the 64 additions rounds once, by at most one ulp.  The
       // bound is doubled: the matrix core's internal datapath is not
@@ -287,18 +433,21 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(
       // exponent and truncates can exceed 64 ulps by a few percent.  The 1%
       // covers the fp64 rounding of the definition; the last terms are
       // flush-to-zero slack.
-      const float E = xnorm[nb] * rcol * (64.0f * 0x1p-22f * 1.01f) +
-                      (xnorm[nb] + rcol) * 0x1p-120f + 0x1p-118f;
-      const bool cert = (lower1 - upper2 > 2.0f * E + lower1 * 0x1p-20f) && (jstar < (uint32_t)half);
-      const int bucket = pos ? (int)jstar : (int)jstar + half;
+      const float xnorm = xnorm_s[nb][threadIdx.x];
+      const float E = xnorm * rcol * (64.0f * 0x1p-22f * 1.01f) +
+                      (xnorm + rcol) * 0x1p-120f + 0x1p-118f;
+      const bool cert = (c.w1 - c.upper2 > 2.0f * E + c.w1 * 0x1p-20f) && (c.j < (uint32_t)half);
+      // On a certified row |x.R_j*| > 2E exceeds the error of the recomputed
+      // sum, so its sign is exact.
+      const int bucket = c.value > 0.f ? (int)c.j : (int)c.j + half;
 
       const int tok = tok_wave + nb * 32 + (lane & 31);
       // Rows the fp32 margin cannot certify are settled by hash_settle_kernel,
       // so no wave waits on them.  Such a row's entry holds the bitwise
       // complement of a lower bound on its best |x.R_j| (negative: the bound
-      // is >= 0): lower1 <= |t_j*| <= |s_j*| + E for the defining sum s_j*,
-      // less 2^-20 of lower1 for the rounding of this subtraction.
-      const float lower = fmaxf(lower1 - E - lower1 * 0x1p-20f, 0.0f);
+      // is >= 0): w1 <= |t_j*| <= |s_j*| + E for the defining sum s_j*, less
+      // 2^-20 of w1 for the rounding of this subtraction.
+      const float lower = fmaxf(c.w1 - E - c.w1 * 0x1p-20f, 0.0f);
       if (lane < 32 && tok < L) bout[tok] = cert ? bucket : (int)~__float_as_uint(lower);
     }
   }
@@ -625,9 +774,14 @@ hipError_t launch_hash(const Shape& s, const void* qk, const void* rot, int32_t*
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((int64_t)(s.len + kHashTokWG - 1) / kHashTokWG * s.heads * s.batch));
-  hipLaunchKernelGGL(hash_bf16_kernel, grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
-                     s.heads, s.len, half, s.rounds);
+  if (half > kQuadMinHalf)
+    hipLaunchKernelGGL(hash_bf16_kernel<QuadEpilogue>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
+                       s.heads, s.len, half, s.rounds);
+  else
+    hipLaunchKernelGGL(hash_bf16_kernel<KeyEpilogue>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(qk), static_cast<const uint16_t*>(rot), buckets,
+                       s.heads, s.len, half, s.rounds);
   const int nranges = (s.len + kSettleRange - 1) / kSettleRange;
   const int64_t nblk = s.segments() * nranges;
   for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks)

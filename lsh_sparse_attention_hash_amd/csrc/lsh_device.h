@@ -54,6 +54,44 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// A pointer that is the same in every lane, marked as such (read from the
+// first active lane), so that a buffer descriptor built from it stays in
+// scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// The value of lane l ^ 32 (the other half of the wave), with one
+// v_permlane32_swap (a VALU exchange of the two 32-lane halves) instead of an
+// LDS permute.  Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t other_half(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  // r[0]: lanes 0-31 keep x, lanes 32-63 receive x of lanes 0-31;
+  // r[1]: lanes 0-31 receive x of lanes 32-63, lanes 32-63 keep x
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float other_half(float x) {
+  return __uint_as_float(other_half(__float_as_uint(x)));
+}
+
+// Maximum over the 64 lanes of a wave (every lane active), with no LDS
+// address registers: DPP exchanges inside each row of 16 lanes (quad
+// permutes for lane ^ 1 and lane ^ 2, then the half-row and row mirrors,
+// which pair groups of 4 and of 8), ds_swizzle for lane ^ 16, and the
+// 32-lane swap.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  return fmaxf(v, other_half(v));
+}
+
 // Index read from caller memory, forced into [0, n) so that no input can make
 // a kernel access memory outside its buffers.
 __device__ __forceinline__ int clamp_index(int i, int n) { return min(max(i, 0), n - 1); }

@@ -280,17 +280,19 @@ def test_scaled_inputs_parity(B, log2_scale):
     say(f"[scaled 2^{log2_scale}] fallback rows {int(host(f.fallback_rows)[0])}")
 
 
-def test_hash_matches_exactly_on_skewed_and_tied_inputs(B):
+@pytest.mark.parametrize("n_buckets", [64, 4096])   # key and quad epilogues
+def test_hash_matches_exactly_on_skewed_and_tied_inputs(B, n_buckets):
     """Integer-valued bf16 inputs produce exact ties; zero rows tie everywhere."""
-    w = synth.Workload("ties", 1, 2, 1024, 64, 64, 2, 64, True, True, "bf16", 20)
+    w = synth.Workload("ties", 1, 2, 1024, 64, n_buckets, 2, 64, True, True, "bf16", 20)
     g = np.random.default_rng(21)
     qk = g.integers(-2, 3, size=(1, 2, 1024, 64)).astype(np.float32)
     qk[0, 0, :10] = 0.0
-    rot = g.integers(-1, 2, size=(2, 2, 32, 64)).astype(np.float32)
+    rot = g.integers(-1, 2, size=(2, 2, n_buckets // 2, 64)).astype(np.float32)
     inp = {"qk": synth.bf16_bits(qk), "v": synth.bf16_bits(g.standard_normal(qk.shape)),
            "rot": synth.bf16_bits(rot)}
     f = run_gpu(B, w, inp)
-    ref = oracle.hash(synth.to_f64(inp["qk"], "bf16"), synth.to_f64(inp["rot"], "bf16"), 64, 2)
+    ref = oracle.hash(synth.to_f64(inp["qk"], "bf16"), synth.to_f64(inp["rot"], "bf16"),
+                      n_buckets, 2)
     assert np.array_equal(host(f.buckets), ref)
     assert int(host(f.fallback_rows)[0]) > 0   # ties can only be settled by the fp64 path
 

@@ -28,7 +28,8 @@ SCRATCH_ALLOWED = {
 }
 # kernels of the benchmarked path and their waves per SIMD
 OCCUPANCY = {
-    "_ZN3lsh16hash_bf16_kernelEPKtS1_Piiiii": 4,
+    "_ZN3lsh16hash_bf16_kernelINS_11KeyEpilogueEEEvPKtS3_Piiiii": 4,
+    "_ZN3lsh16hash_bf16_kernelINS_12QuadEpilogueEEEvPKtS3_Piiiii": 4,
     "_ZN3lsh18attend_bf16_kernelILb1ELb1ELi0ELb1EEEvNS_10AttendArgsE": 4,
     "_ZN3lsh18attend_bf16_kernelILb1ELb1ELi8ELb1EEEvNS_10AttendArgsE": 4,
 }
