@@ -370,7 +370,8 @@ lsh_status lsh_ffn(const lsh_layer_config* cfg, const float* x, const void* w_1,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace the reversible layer needs (qk, v, the LSH
- * attention's intermediates, the per-head outputs and one FFN chunk). */
+ * attention's intermediates, the per-head outputs -- kept as bf16, the
+ * precision the output map reads them in -- and one FFN chunk). */
 size_t lsh_layer_workspace_bytes(const lsh_layer_config* cfg);
 
 /*

@@ -40,6 +40,14 @@ __device__ __forceinline__ void store_y_nt(float* p, float4 v) {
   const f32x4v w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<f32x4v*>(p));
 }
+// bf16 outputs (the reversible layer's attention output, which its output
+// map reads as bf16 anyway): rounded to nearest even, like that map's own
+// rounding of fp32 inputs, so the layer's results do not change
+__device__ __forceinline__ void store_y_nt(uint16_t* p, float4 v) {
+  const bf16x2 lo = {(__bf16)v.x, (__bf16)v.y}, hi = {(__bf16)v.z, (__bf16)v.w};
+  const u32x2v w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2v*>(p));
+}
 
 // Per-round rows: fp32, or fp16 in the compact format (O16).
 template <bool O16>
@@ -72,11 +80,11 @@ __device__ __forceinline__ float o_unscale(const int32_t* hexp, int64_t bh) {
 
 // RMAX >= rounds: every round's slot, lse and output row are requested before
 // any is used, so a token's R row gathers are in flight together.
-template <typename T, bool O16, int RMAX>
+template <typename T, bool O16, int RMAX, typename Y>
 __global__ __launch_bounds__(256) void combine_kernel(
     const typename ORows<O16>::elem* __restrict__ o_rounds, const int32_t* __restrict__ hexp,
     const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
-    float* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
+    Y* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
   // Last tokens first: the per-round rows written last by the attention step
   // are the likeliest to still sit in the memory-side cache.
   const int64_t tok0 = (blk0 + gridDim.x - 1 - blockIdx.x) * 16;   // < total
@@ -132,11 +140,11 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }
 
 // Any number of rounds: a running softmax over the rounds, one round at a time.
-template <typename T, bool O16>
+template <typename T, bool O16, typename Y>
 __global__ __launch_bounds__(256) void combine_many_kernel(
     const typename ORows<O16>::elem* __restrict__ o_rounds, const int32_t* __restrict__ hexp,
     const float* __restrict__ lse, const int32_t* __restrict__ inv_perm, const T* __restrict__ v,
-    float* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
+    Y* __restrict__ y, int rounds, int L, int64_t total, int64_t blk0) {
   const int64_t tok0 = (blk0 + gridDim.x - 1 - blockIdx.x) * 16;
   const float unscale = o_unscale<O16>(hexp, tok0 / L);
   const int64_t tok = tok0 + (threadIdx.x >> 4);
@@ -173,9 +181,9 @@ __global__ __launch_bounds__(256) void combine_many_kernel(
   store_y_nt(y + tok * kHeadDim + c4, out);
 }
 
-template <typename T, bool O16>
+template <typename T, bool O16, typename Y>
 static void launch_combine_t(const Shape& s, const void* o_buf, const float* lse,
-                             const int32_t* inv_perm, const T* v, float* y, hipStream_t stream) {
+                             const int32_t* inv_perm, const T* v, Y* y, hipStream_t stream) {
   const int32_t* hexp = reinterpret_cast<const int32_t*>(static_cast<const float*>(o_buf) +
                                                          (int64_t)s.batch * s.heads * kVParts);
   const auto* o_rounds = reinterpret_cast<const typename ORows<O16>::elem*>(
@@ -190,23 +198,25 @@ static void launch_combine_t(const Shape& s, const void* o_buf, const float* lse
   hipLaunchKernelGGL(K, grid, block, 0, stream, o_rounds, hexp, lse, inv_perm, v, y, s.rounds, \
                      s.len, total, b0)
   if (s.rounds <= 1)
-    LSH_COMBINE((combine_kernel<T, O16, 1>));
+    LSH_COMBINE((combine_kernel<T, O16, 1, Y>));
   else if (s.rounds <= 2)
-    LSH_COMBINE((combine_kernel<T, O16, 2>));
+    LSH_COMBINE((combine_kernel<T, O16, 2, Y>));
   else if (s.rounds <= 4)
-    LSH_COMBINE((combine_kernel<T, O16, 4>));
+    LSH_COMBINE((combine_kernel<T, O16, 4, Y>));
   else if (s.rounds <= 8)
-    LSH_COMBINE((combine_kernel<T, O16, 8>));
+    LSH_COMBINE((combine_kernel<T, O16, 8, Y>));
   else if (s.rounds <= 16)
-    LSH_COMBINE((combine_kernel<T, O16, 16>));
+    LSH_COMBINE((combine_kernel<T, O16, 16, Y>));
   else
-    LSH_COMBINE((combine_many_kernel<T, O16>));
+    LSH_COMBINE((combine_many_kernel<T, O16, Y>));
 #undef LSH_COMBINE
   }
 }
 
-hipError_t launch_combine(const Shape& s, const void* o_rounds, const float* lse,
-                          const int32_t* inv_perm, const void* v, float* y, hipStream_t stream) {
+template <typename Y>
+static hipError_t launch_combine_y(const Shape& s, const void* o_rounds, const float* lse,
+                                   const int32_t* inv_perm, const void* v, Y* y,
+                                   hipStream_t stream) {
   if (s.o16)
     launch_combine_t<uint16_t, true>(s, o_rounds, lse, inv_perm, static_cast<const uint16_t*>(v),
                                      y, stream);
@@ -217,6 +227,17 @@ hipError_t launch_combine(const Shape& s, const void* o_rounds, const float* lse
     launch_combine_t<float, false>(s, o_rounds, lse, inv_perm, static_cast<const float*>(v), y,
                                    stream);
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const Shape& s, const void* o_rounds, const float* lse,
+                          const int32_t* inv_perm, const void* v, float* y, hipStream_t stream) {
+  return launch_combine_y(s, o_rounds, lse, inv_perm, v, y, stream);
+}
+
+hipError_t launch_combine_bf16(const Shape& s, const void* o_rounds, const float* lse,
+                               const int32_t* inv_perm, const void* v, uint16_t* y,
+                               hipStream_t stream) {
+  return launch_combine_y(s, o_rounds, lse, inv_perm, v, y, stream);
 }
 
 }  // namespace lsh

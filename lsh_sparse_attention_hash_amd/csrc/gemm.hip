@@ -6,7 +6,7 @@
 //
 // A is bf16 or fp32 (rounded to bf16, nearest-even, as it is staged), in rows
 // [M][lda] or, for the attention output, as heads [b][H][L][64] read as the
-// concatenation [b*L][H*64].  W is bf16, one row per output feature ([N][K]),
+// concatenation [b*L][H*64] (fp32, or bf16 inside the reversible layer).  W is bf16, one row per output feature ([N][K]),
 // so both operands are K-contiguous: every MFMA fragment is one 16-byte load.
 //
 // Tiles: 128 x 128 outputs per workgroup (4 waves, 64 x 64 each as 2 x 2
@@ -25,7 +25,9 @@ namespace lsh {
 constexpr int kBM = 128, kBN = 128, kBK = 32;
 constexpr int kTS = 40;   // bf16 per staged row (32 + 8 pad: 80 B)
 
-enum ALayout { kAF32Rows = 0, kABf16Rows = 1, kAF32Heads = 2 };
+enum ALayout { kAF32Rows = 0, kABf16Rows = 1, kAF32Heads = 2, kABf16Heads = 3 };
+constexpr bool a_bf16(int al) { return al == kABf16Rows || al == kABf16Heads; }
+constexpr bool a_heads(int al) { return al == kAF32Heads || al == kABf16Heads; }
 enum Epilogue { kEpiQkv = 0, kEpiResidual = 1, kEpiReluBf16 = 2 };
 
 struct GemmArgs {
@@ -51,7 +53,7 @@ __device__ __forceinline__ uint32_t gemm_pack2(float a, float b) {
 // One K-tile of A (128 rows x 32 k) in registers.
 template <int AL>
 struct GemmATile {
-  uint4 r[AL == kABf16Rows ? 2 : 4];
+  uint4 r[a_bf16(AL) ? 2 : 4];
 };
 
 // Element offset of (row m, k = 0) of A for the rows this thread stages, or
@@ -60,18 +62,18 @@ struct GemmATile {
 // h * L * 64 + j.
 template <int AL>
 struct GemmARows {
-  int64_t off[AL == kABf16Rows ? 2 : 4];
+  int64_t off[a_bf16(AL) ? 2 : 4];
 };
 
 template <int AL>
 __device__ __forceinline__ void gemm_a_rows(GemmARows<AL>& ar, const GemmArgs& g, int m0) {
 #pragma unroll
-  for (int q = 0; q < (AL == kABf16Rows ? 2 : 4); ++q) {
+  for (int q = 0; q < (a_bf16(AL) ? 2 : 4); ++q) {
     const int idx = threadIdx.x + 256 * q;
-    const int m = m0 + (AL == kABf16Rows ? idx >> 2 : idx >> 3);
+    const int m = m0 + (a_bf16(AL) ? idx >> 2 : idx >> 3);
     int64_t o = -1;
     if (m < g.M) {
-      if (AL == kAF32Heads) {
+      if (a_heads(AL)) {
         const int bi = m / g.L, l = m - bi * g.L;
         o = ((int64_t)bi * g.heads * g.L + l) * kHeadDim;
       } else {
@@ -87,12 +89,16 @@ __device__ __forceinline__ void gemm_a_rows(GemmARows<AL>& ar, const GemmArgs& g
 template <int AL, bool FULL>
 __device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g,
                                             const GemmARows<AL>& ar, int k0) {
-  if (AL == kABf16Rows) {
+  if (a_bf16(AL)) {
     const uint16_t* a = static_cast<const uint16_t*>(g.a);
+    // heads: the K-tile at k0 lies in head k0 / 64
+    const int64_t kofs = AL == kABf16Heads
+                             ? (int64_t)(k0 / kHeadDim) * g.L * kHeadDim + k0 % kHeadDim
+                             : k0;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int c8 = ((threadIdx.x + 256 * q) & 3) * 8;
-      t.r[q] = (FULL || ar.off[q] >= 0) ? load16(a + ar.off[q] + k0 + c8)
+      t.r[q] = (FULL || ar.off[q] >= 0) ? load16(a + ar.off[q] + kofs + c8)
                                          : make_uint4(0, 0, 0, 0);
     }
   } else {
@@ -112,7 +118,7 @@ __device__ __forceinline__ void gemm_load_a(GemmATile<AL>& t, const GemmArgs& g,
 
 template <int AL>
 __device__ __forceinline__ void gemm_store_a(uint16_t* as, const GemmATile<AL>& t) {
-  if (AL == kABf16Rows) {
+  if (a_bf16(AL)) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int idx = threadIdx.x + 256 * q;
@@ -395,6 +401,20 @@ hipError_t launch_project_out(const LayerShape& s, const float* y_att, const uin
   g.resid = resid;
   g.sign = sign;
   return gemm_launch<kAF32Heads, kEpiResidual>(g, stream);
+}
+
+hipError_t launch_project_out_bf16(const LayerShape& s, const uint16_t* y_att,
+                                   const uint16_t* w_o, const float* resid, float sign,
+                                   float* out, hipStream_t stream) {
+  GemmArgs g = gemm_args(s.batch * s.len, s.d_model, s.d_model);
+  g.a = y_att;
+  g.heads = s.d_model / kHeadDim;
+  g.L = s.len;
+  g.w0 = g.w1 = w_o;
+  g.out0 = out;
+  g.resid = resid;
+  g.sign = sign;
+  return gemm_launch<kABf16Heads, kEpiResidual>(g, stream);
 }
 
 hipError_t launch_ffn(const LayerShape& s, const float* x, const uint16_t* w_1, const float* b_1,

@@ -28,7 +28,8 @@ struct LayerScratch {
   uint16_t *qk, *v, *hidden;
   int32_t *buckets, *perm, *inv_perm;
   void *sort_ws, *o_rounds;
-  float *lse, *y_att;
+  float* lse;
+  uint16_t* y_att;   // bf16: the output map rounds its input to bf16 anyway
   size_t bytes;
 };
 
@@ -44,7 +45,7 @@ LayerScratch carve(const LayerShape& ls, const Shape& as, void* base) {
   w.sort_ws = c.take<char>(sort_workspace_bytes(as));
   w.o_rounds = c.take<char>(o_rounds_bytes(as));
   w.lse = c.take<float>(N * 4);
-  w.y_att = c.take<float>(T * kHeadDim * 4);
+  w.y_att = c.take<uint16_t>(T * kHeadDim * 2);
   w.hidden = c.take<uint16_t>(ffn_workspace_bytes(ls));
   w.bytes = c.at;
   return w;
@@ -60,9 +61,10 @@ hipError_t attention_block(const LayerShape& ls, const Shape& as, const LayerWei
   if ((e = launch_sort(as, w.buckets, w.perm, w.inv_perm, w.sort_ws, stream)) != hipSuccess) return e;
   if ((e = launch_attend(as, w.qk, w.v, w.buckets, w.perm, w.o_rounds, w.lse, stream)) != hipSuccess)
     return e;
-  if ((e = launch_combine(as, w.o_rounds, w.lse, w.inv_perm, w.v, w.y_att, stream)) != hipSuccess)
+  if ((e = launch_combine_bf16(as, w.o_rounds, w.lse, w.inv_perm, w.v, w.y_att, stream)) !=
+      hipSuccess)
     return e;
-  return launch_project_out(ls, w.y_att, wt.w_o, resid, sign, out, stream);
+  return launch_project_out_bf16(ls, w.y_att, wt.w_o, resid, sign, out, stream);
 }
 
 }  // namespace

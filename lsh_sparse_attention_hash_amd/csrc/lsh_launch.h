@@ -53,6 +53,10 @@ hipError_t launch_attend_union(const Shape& s, const void* qk, const void* v,
 
 hipError_t launch_combine(const Shape& s, const void* o_rounds, const float* lse,
                           const int32_t* inv_perm, const void* v, float* y, hipStream_t stream);
+// the same with y rounded to bf16 (nearest even), for the reversible layer
+hipError_t launch_combine_bf16(const Shape& s, const void* o_rounds, const float* lse,
+                               const int32_t* inv_perm, const void* v, uint16_t* y,
+                               hipStream_t stream);
 
 hipError_t launch_local(const Shape& s, int before, int after, const void* qk, const void* v,
                         float* y, float* lse, hipStream_t stream);
@@ -75,6 +79,10 @@ hipError_t launch_project_qkv(const LayerShape& s, const float* x, const uint16_
 // out = resid + sign * (concat_heads(bf16(y_att)) W_o^T); out may equal resid
 hipError_t launch_project_out(const LayerShape& s, const float* y_att, const uint16_t* w_o,
                               const float* resid, float sign, float* out, hipStream_t stream);
+// the same with y_att already bf16 ([b][H][L][64])
+hipError_t launch_project_out_bf16(const LayerShape& s, const uint16_t* y_att,
+                                   const uint16_t* w_o, const float* resid, float sign,
+                                   float* out, hipStream_t stream);
 // out = resid + sign * (bf16(ReLU(bf16(x) W1^T + b1)) W2^T + b2), chunk by chunk of rows;
 // hidden: chunk_rows() x d_ff bf16 scratch
 hipError_t launch_ffn(const LayerShape& s, const float* x, const uint16_t* w_1, const float* b_1,
