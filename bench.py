@@ -661,7 +661,9 @@ def main():
     t = per[dom] * 1e-3
     if dom == "hash":
         ach = work["hash"]["flops"] / t / 1e12
-        roof = {"kernel": "hash_bf16_kernel", "bound": "mfma", "achieved": round(ach, 2),
+        # the epilogue the library picks: keys up to 1,024 directions, else quads
+        epi = "KeyEpilogue" if w.n_buckets // 2 <= 1024 else "QuadEpilogue"
+        roof = {"kernel": f"hash_bf16_kernel<{epi}>", "bound": "mfma", "achieved": round(ach, 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
     else:
@@ -672,7 +674,7 @@ def main():
     roof["traffic"] = measured_traffic(dom, w.name + ("_union" if args.union else ""))
     # what the HIP events around the call time (one ABI call can launch two
     # kernels; the traffic is that of the same kernels)
-    roof["timed"] = {"hash": "lsh_hash: hash_bf16_kernel + hash_settle_kernel",
+    roof["timed"] = {"hash": "lsh_hash: hash_bf16_kernel<...Epilogue> + hash_settle_kernel",
                      "attend": ("lsh_chunk_attend_union: union_keys_kernel + vmax_kernel + "
                                 "attend_bf16_kernel" if args.union else
                                 "lsh_chunk_attend: vmax_kernel + attend_bf16_kernel"),
