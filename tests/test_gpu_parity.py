@@ -123,6 +123,10 @@ EDGE = {
     "mask_match_limit": synth.Workload("b2048", 1, 2, 4096, 64, 2048, 2, 64, True, True, "bf16",
                                        23),
     "ballot_match": synth.Workload("b4096", 1, 1, 4096, 64, 4096, 1, 64, False, True, "bf16", 24),
+    # the first bucket count that takes the hash's quad epilogue: 1,025 directions,
+    # the last of 33 direction tiles holding one (its quads past half read as zero)
+    "quad_ragged_tile": synth.Workload("b2050", 1, 2, 64 * 5, 64, 2050, 2, 64, True, True, "bf16",
+                                       28),
     # round counts that leave padded slots in the combine's unrolled loads
     "rounds5": synth.Workload("r5", 1, 2, 64 * 11, 64, 16, 5, 64, True, True, "bf16", 25),
     "rounds12": synth.Workload("r12", 1, 1, 64 * 6, 64, 8, 12, 64, False, False, "bf16", 26),
