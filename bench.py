@@ -74,7 +74,7 @@ def algorithmic(w, union=False):
     return out
 
 
-def survey_bytes(w):
+def fixed_count_bytes(w):
     """The fixed per-step byte counts every build is compared on (bf16 or fp32
     inputs, fp32 per-round rows, predecessor chunk reused): hash T*2d + 4N
     (bf16), sort 16 N, attention 524 N (780 N for fp32 inputs), combine
@@ -87,13 +87,13 @@ def survey_bytes(w):
             "combine": N * (4 * w.head_dim + 8) + T * 4 * w.head_dim}
 
 
-def north_star(w, per, union=False):
+def path_targets(w, per, union=False):
     """The two target branches at this shape: the chunk attention's flops
     against the dense bf16 matrix-core peak (target 0.40), and the bytes of
     sort + attention + combine against HBM peak (target 0.60), the bytes
     counted as this layout moves them and as the fixed counts above."""
     work = algorithmic(w, union)
-    fixed = survey_bytes(w)
+    fixed = fixed_count_bytes(w)
     t_att = per["attend"] * 1e-3
     t_path = sum(per[n] for n in ("sort", "attend", "combine")) * 1e-3
     mine = sum(work[n]["bytes"] for n in ("sort", "attend", "combine"))
@@ -642,7 +642,7 @@ def main():
         copy_calibration(torch)
 
     work = algorithmic(w, args.union)
-    fixed = survey_bytes(w)
+    fixed = fixed_count_bytes(w)
     kernels = {}
     for n in names:
         t = per[n] * 1e-3
@@ -704,7 +704,7 @@ def main():
         "step_ms": tm["step_pct"],
         **forward_summary(w, tm, args.union),
         "roofline": roof,
-        "north_star": north_star(w, per, args.union),
+        "targets": path_targets(w, per, args.union),
         "kernels": kernels,
         "hash_fallback_rows_per_step": tm["fallback_rows"],
         "cpu_baseline": None,
@@ -719,7 +719,7 @@ def main():
                 "ms_per_step": round(ta["ms"], 5), "step_ms": ta["step_pct"],
                 "value": round(w.batch * w.seq_len / (ta["ms"] * 1e-3), 1),
                 "kernels_ms": {n: round(x, 5) for n, x in ta["per"].items()},
-                "north_star": north_star(wa, ta["per"])}
+                "targets": path_targets(wa, ta["per"])}
         result["other_configs"] = other_configs(args, w, binding, torch, synth)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

@@ -41,23 +41,23 @@ def test_algorithmic_work_of_the_headline_shape():
     assert f["combine"]["bytes"] == 264 * Nt + 256 * Tt
     # x read once, every rotation read, bucket ids written
     assert a["hash"]["bytes"] == T * 128 + 8 * 8 * 512 * 64 * 2 + 4 * N
-    # fp32 per-round rows for bf16 inputs: the fixed counts of the survey
+    # fp32 per-round rows for bf16 inputs: the fixed per-token byte counts
     # (524 B per token-round for the attention, 264 + 256 per token-head for
     # the combine), no scale pass
     g = bench.algorithmic(w.replace(o_format="f32"))
     assert g["attend"]["bytes"] == 524 * N
     assert g["combine"]["bytes"] == 264 * N + 256 * T
-    assert bench.survey_bytes(w) == {"hash": 128 * T + 4 * N, "sort": 16 * N,
+    assert bench.fixed_count_bytes(w) == {"hash": 128 * T + 4 * N, "sort": 16 * N,
                                      "attend": 524 * N, "combine": 264 * N + 256 * T}
 
 
-def test_north_star_fractions():
+def test_path_target_fractions():
     """Both target branches from per-call times: the attention's flops over
     the bf16 peak, the path's bytes over HBM peak (own and fixed counts)."""
     w = synth.WORKLOADS["long"]
     N, T = w.token_rounds, w.batch * w.heads * w.seq_len
     per = {"hash": 0.4, "sort": 0.025, "attend": 0.35, "combine": 0.145}   # ms
-    ns = bench.north_star(w, per)
+    ns = bench.path_targets(w, per)
     assert ns["attend_mfma_frac"] == pytest.approx(32_768 * N / 0.35e-3 / 2.5e15, abs=1e-4)
     own = 16 * N + 396 * N + 128 * T + 136 * N + 256 * T
     assert ns["path_bytes"] == own
