@@ -608,7 +608,7 @@ def main():
                          "(reference for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads would shard across GPUs with no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
