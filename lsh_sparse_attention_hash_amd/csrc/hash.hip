@@ -32,7 +32,6 @@ constexpr int kHashTokWG = kHashWaves * kHashTokWave;  // 256 tokens per workgro
 constexpr int kStageRows = 128;                        // rotation rows staged per LDS pass
 constexpr int kRowStride = 72;                         // bf16 per staged row (144 B, padded)
 
-
 // ---------------------------------------------------------------------------
 // Exact bucket of one token, computed by one wave in the defining arithmetic:
 // s_j = sum_{k=0..63} x_k R[k][j] in fp64, k ascending from 0.0 (each product
@@ -93,11 +92,11 @@ struct Cand {
   float w1, upper2, value;
 };
 
-// The recomputed signed scores of n consecutive directions j0 .. j0 + n - 1
+// The recomputed signed scores of N consecutive directions j0 .. j0 + N - 1
 // for the token of this lane pair.  Every 16-byte piece of a pair of rows is
-// requested before any of them is used.  The descriptor covers the rotation's half
-// directions, so rows past half read as zero and score 0, as in the padded
-// tile.
+// requested before any of them is used.  The descriptor covers the rotation's
+// half directions, so rows past half read as zero and score 0, as in the
+// padded tile.
 template <int N>
 __device__ __forceinline__ void recompute(float (&v)[N], __amdgpu_buffer_rsrc_t rrs, uint32_t j0,
                                           const bf16x8 (&x)[4]) {
@@ -113,7 +112,8 @@ __device__ __forceinline__ void recompute(float (&v)[N], __amdgpu_buffer_rsrc_t 
         rv[e][ks] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
                        rrs, (j0 + e0 + e) * (uint32_t)(kHeadDim * 2) + lane_off + 32u * ks, 0, 0));
-    // (two rows: keep the scheduler from splitting the requests again)
+    // two rows: keep the scheduler from splitting the requests again (with
+    // one row it may move other work in between, which hides their latency)
     if constexpr (N > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < kPair; ++e) {
