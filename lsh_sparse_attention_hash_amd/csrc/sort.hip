@@ -20,9 +20,12 @@
 //   count    one workgroup per (segment, tile): LDS histogram of the tile
 //   scan_t   one thread per (segment, bucket): exclusive prefix over tiles
 //   scan_b   one workgroup per segment: exclusive prefix over bucket totals
-//   scatter  one wave per (segment, tile): walks the tile in order, 64 keys
-//            at a time; equal keys inside a batch are ranked by lane through
-//            ballots over the key bits, so the scatter is stable.
+//   scatter  one workgroup of eight waves per (segment, tile) for B <= 8,192
+//            (each wave an eighth of the tile, its offsets from per-wave LDS
+//            counts), else one wave per (segment, tile); each wave walks its
+//            keys in order, 64 at a time; equal keys inside a batch are
+//            ranked by lane through ballots over the key bits, so the
+//            scatter is stable.
 // Workspace: cnt[S][tiles][B] (B <= 2048); cnt[S][tiles][B] (counts, then
 // tile prefixes) and base[S][B] (B > 2048).
 #include <algorithm>
@@ -321,6 +324,131 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
   }
 }
 
+// The same with the tile split over eight waves (B <= 8,192), so that a
+// tile's keys are ranked by eight waves at once.  Each wave takes an eighth
+// of the tile in position order.  Pass 1 counts every wave's keys per bucket
+// (LDS atomics on 16-bit halves of 32-bit words: an eighth of a tile holds
+// at most 1,024 keys); the counts then become each wave's offset inside the
+// tile's run of every bucket (the counts of the waves before it); pass 2
+// ranks the keys 64 at a time like the one-wave form, each key's slot being
+// its bucket's first slot in the tile plus its wave's running offset plus
+// its rank among the equal keys of lower lanes.  The tables take all 160 KB
+// of the CU's LDS at B = 8,192 (one workgroup per CU); against one wave per
+// tile the scatter at 4 x 524,288 tokens and 8,192 buckets takes 83 instead
+// of 128 us (four waves: 102 us).
+constexpr int kSplitMaxBuckets = 8192;
+constexpr int kSplitWaves = 8;
+
+__global__ __launch_bounds__(kWave * kSplitWaves) void sort_scatter_split_kernel(
+    const int32_t* __restrict__ buckets, const int32_t* __restrict__ cnt,
+    const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int L, int nb, int nbits, int tile, int ntiles) {
+  __shared__ int32_t run[kSplitMaxBuckets];                       // the tile's first slot
+  __shared__ uint32_t hw[kSplitWaves * kSplitMaxBuckets / 2];     // 16-bit per (wave, bucket)
+  constexpr int kThreads = kWave * kSplitWaves;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid >> 6;
+  const int64_t blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t seg = blk / ntiles;
+  const int t = (int)(blk % ntiles);
+  const int32_t* pre = cnt + (seg * ntiles + t) * (int64_t)nb;
+  const int32_t* bs = base + seg * nb;
+  const int lo = t * tile;
+  const int hi = min(L, lo + tile);
+  const int sub = tile / kSplitWaves;   // a multiple of 64 (tiles here hold >= 4,096 keys)
+  const int wlo = min(hi, lo + w * sub);
+  const int whi = min(hi, wlo + sub);
+  const int32_t* bk = buckets + seg * L;
+  int32_t* pm = perm + seg * L;
+  int32_t* ip = inv_perm + seg * L;
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(hw) + w * nb;   // this wave's table
+
+  for (int i = tid; i < kSplitWaves * nb / 2; i += kThreads) hw[i] = 0u;
+  // the tile's first slot of every bucket, eight loads of each kind in flight
+  for (int i0 = 0; i0 < nb; i0 += kThreads * 8) {
+    int32_t bv[8], pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + kThreads * u + tid, nb - 1);
+      bv[u] = bs[i];
+      pv[u] = pre[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + kThreads * u + tid;
+      if (i < nb) run[i] = bv[u] + pv[u];
+    }
+  }
+  __syncthreads();
+
+  // pass 1: this wave's count of every bucket (nb is even, so the wave's
+  // table starts on a word: bucket k of wave w is half k % 2 of word
+  // (w * nb + k) / 2)
+  for (int c0 = wlo; c0 < whi; c0 += kWave * kScatterBatches) {
+    int key[kScatterBatches];
+#pragma unroll
+    for (int b = 0; b < kScatterBatches; ++b) key[b] = bk[min(c0 + b * kWave + lane, whi - 1)];
+#pragma unroll
+    for (int b = 0; b < kScatterBatches; ++b) {
+      if (c0 + b * kWave + lane < whi) {
+        const int k = clamp_bucket(key[b], nb);
+        atomicAdd(&hw[(w * nb + k) >> 1], 1u << (16 * (k & 1)));
+      }
+    }
+  }
+  __syncthreads();
+  // the counts become offsets: wave w's run of bucket b starts after the
+  // keys of b in the waves before it
+  for (int b = tid; b < nb; b += kThreads) {
+    const uint16_t* h0 = reinterpret_cast<const uint16_t*>(hw);
+    uint16_t* hm = reinterpret_cast<uint16_t*>(hw);
+    int acc = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kSplitWaves; ++w2) {
+      const int c = h0[w2 * nb + b];
+      hm[w2 * nb + b] = (uint16_t)acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+
+  // pass 2: ranks in position order and the scatter
+  for (int c0 = wlo; c0 < whi; c0 += kWave * kScatterBatches) {
+    int key[kScatterBatches];
+#pragma unroll
+    for (int b = 0; b < kScatterBatches; ++b) key[b] = bk[min(c0 + b * kWave + lane, whi - 1)];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int b = 0; b < kScatterBatches; ++b) {
+      const int i0 = c0 + b * kWave;
+      if (i0 >= whi) break;
+      const int i = i0 + lane;
+      const bool valid = i < whi;
+      const int k = valid ? clamp_bucket(key[b], nb) : 0;
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (k >> bit) & 1;
+        const uint64_t ones = __ballot(set);
+        peers &= set ? ones : ~ones;
+      }
+      const int off = valid ? (int)h16[k] : 0;
+      const int32_t start = valid ? run[k] : 0;
+      const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+      const int n = __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+      if (valid && rank == n - 1) h16[k] = (uint16_t)(off + n);
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        const int32_t slot = start + off + rank;
+        pm[slot] = i;
+        ip[i] = slot;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Wide tiles (B <= 2048).  One workgroup of W waves per (segment, tile of
 // W * 64 * nbat keys, nbat <= 32 batches of 64 per wave, at most 16,384 keys).
@@ -600,8 +728,13 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
                          dim3(256), 0, stream, cnt, base, nb, ntiles, nbins, b0);
     hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base, nb);
   }
-  hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)(S * ntiles)), dim3(64), lds, stream,
-                     buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
+  if (nb <= kSplitMaxBuckets && tile >= kSplitWaves * kWave)
+    hipLaunchKernelGGL(sort_scatter_split_kernel, dim3((unsigned)(S * ntiles)),
+                       dim3(kWave * kSplitWaves), 0, stream, buckets, cnt, base, perm, inv_perm,
+                       s.len, nb, nbits, tile, ntiles);
+  else
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3((unsigned)(S * ntiles)), dim3(64), lds, stream,
+                       buckets, cnt, base, perm, inv_perm, s.len, nb, nbits, tile, ntiles);
   return hipGetLastError();
 }
 
