@@ -339,9 +339,10 @@ __global__ __launch_bounds__(64) void sort_scatter_kernel(
 constexpr int kSplitMaxBuckets = 8192;
 constexpr int kSplitWaves = 8;
 
+// `totals`: every bucket's count in the segment ([S][B], from scan_t).
 __global__ __launch_bounds__(kWave * kSplitWaves) void sort_scatter_split_kernel(
     const int32_t* __restrict__ buckets, const int32_t* __restrict__ cnt,
-    const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    const int32_t* __restrict__ totals, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int L, int nb, int nbits, int tile, int ntiles) {
   __shared__ int32_t run[kSplitMaxBuckets];                       // the tile's first slot
   __shared__ uint32_t hw[kSplitWaves * kSplitMaxBuckets / 2];     // 16-bit per (wave, bucket)
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(kWave * kSplitWaves) void sort_scatter_split_kernel
   const int64_t seg = blk / ntiles;
   const int t = (int)(blk % ntiles);
   const int32_t* pre = cnt + (seg * ntiles + t) * (int64_t)nb;
-  const int32_t* bs = base + seg * nb;
+  const int32_t* bs = totals + seg * nb;
   const int lo = t * tile;
   const int hi = min(L, lo + tile);
   const int sub = tile / kSplitWaves;   // a multiple of 64 (tiles here hold >= 4,096 keys)
@@ -364,22 +365,45 @@ __global__ __launch_bounds__(kWave * kSplitWaves) void sort_scatter_split_kernel
   int32_t* ip = inv_perm + seg * L;
   uint16_t* h16 = reinterpret_cast<uint16_t*>(hw) + w * nb;   // this wave's table
 
-  for (int i = tid; i < kSplitWaves * nb / 2; i += kThreads) hw[i] = 0u;
-  // the tile's first slot of every bucket, eight loads of each kind in flight
-  for (int i0 = 0; i0 < nb; i0 += kThreads * 8) {
-    int32_t bv[8], pv[8];
+  // The tile's first slot of every bucket: the bucket's base in the segment
+  // (the exclusive prefix over buckets of the segment's totals, computed here
+  // by every workgroup of the segment) plus the counts of the segment's
+  // earlier tiles.  Thread tid takes buckets 16 tid .. 16 tid + 15; the
+  // waves' sums pass through the first words of hw, cleared afterwards.
+  {
+    constexpr int kPer = kSplitMaxBuckets / kThreads;   // 16
+    int32_t* wsum = reinterpret_cast<int32_t*>(hw);
+    int32_t tv[kPer], pv[kPer];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = min(i0 + kThreads * u + tid, nb - 1);
-      bv[u] = bs[i];
+    for (int u = 0; u < kPer; ++u) {
+      const int i = min(kPer * tid + u, nb - 1);
+      tv[u] = bs[i];
       pv[u] = pre[i];
     }
+    int32_t mine = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + kThreads * u + tid;
-      if (i < nb) run[i] = bv[u] + pv[u];
+    for (int u = 0; u < kPer; ++u) mine += kPer * tid + u < nb ? tv[u] : 0;
+    // exclusive prefix of the per-thread sums over the workgroup
+    int32_t inc = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    if (lane == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    int32_t acc = inc - mine;
+#pragma unroll
+    for (int w2 = 0; w2 < kSplitWaves; ++w2) acc += w2 < w ? wsum[w2] : 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = kPer * tid + u;
+      if (i < nb) run[i] = acc + pv[u];
+      acc += i < nb ? tv[u] : 0;
     }
   }
+  __syncthreads();   // the waves' sums are read
+  for (int i = tid; i < kSplitWaves * nb / 2; i += kThreads) hw[i] = 0u;
   __syncthreads();
 
   // pass 1: this wave's count of every bucket (nb is even, so the wave's
@@ -712,9 +736,11 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
   int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cnt_bytes);
   const size_t lds = (size_t)nb * sizeof(int32_t);
 
+  // the eight-wave scatter computes the bucket bases from the totals itself
+  const bool split = nb <= kSplitMaxBuckets && tile >= kSplitWaves * kWave;
   // one workgroup per segment pays off while a segment is short: a long one
   // is counted faster by a workgroup per tile
-  if ((int64_t)ntiles * nb <= kPrefixLdsInts && s.len <= kPrefixMaxLen) {
+  if (!split && (int64_t)ntiles * nb <= kPrefixLdsInts && s.len <= kPrefixMaxLen) {
     hipLaunchKernelGGL(sort_prefix_kernel, dim3((unsigned)S), dim3(kPrefixThreads), 0, stream,
                        buckets, cnt, base, s.len, nb, tile, ntiles);
   } else {
@@ -726,9 +752,11 @@ hipError_t launch_sort(const Shape& s, const int32_t* buckets, int32_t* perm, in
     for (int64_t b0 = 0; b0 < nblk; b0 += kMaxBlocks)
       hipLaunchKernelGGL(sort_scan_tiles_kernel, dim3((unsigned)std::min(kMaxBlocks, nblk - b0)),
                          dim3(256), 0, stream, cnt, base, nb, ntiles, nbins, b0);
-    hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base, nb);
+    if (!split)
+      hipLaunchKernelGGL(sort_scan_bins_kernel, dim3((unsigned)S), dim3(1024), 0, stream, base,
+                         nb);
   }
-  if (nb <= kSplitMaxBuckets && tile >= kSplitWaves * kWave)
+  if (split)
     hipLaunchKernelGGL(sort_scatter_split_kernel, dim3((unsigned)(S * ntiles)),
                        dim3(kWave * kSplitWaves), 0, stream, buckets, cnt, base, perm, inv_perm,
                        s.len, nb, nbits, tile, ntiles);
