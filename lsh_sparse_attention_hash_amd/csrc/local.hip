@@ -25,6 +25,25 @@
 
 namespace lsh {
 
+// Sum over each group of eight lanes (8m .. 8m + 7) by DPP exchanges inside
+// the lanes' row (lane ^ 1 and lane ^ 2 by quad permutes, then the other
+// quad of the eight through the half-row mirror): the additions pair the
+// lanes as lane ^ 1, ^ 2, ^ 4 would, so the sums are the same bits, with no
+// LDS permute.
+__device__ __forceinline__ float sum8_lanes(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// Maximum of lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane groups):
+// ds_swizzle for lane ^ 16 inside each half, the half swap for lane ^ 32.
+__device__ __forceinline__ float max4_groups(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  return fmaxf(v, other_half(v));
+}
+
 constexpr int kKeyStride = 72;   // bf16 per key row in LDS (144 B)
 constexpr int kVtRowDw = 36;     // dwords per V^T row: 32 key pairs + 4 pad
 constexpr float kLog2eL = 1.4426950408889634f;
@@ -85,11 +104,8 @@ __device__ __forceinline__ void commit_keys(LocalLds& sm, const KeyRegs& g) {
     sa += a0 * a0 + a1 * a1;
     sc += c0 * c0 + c1 * c1;
   }
-#pragma unroll
-  for (int off = 1; off < 8; off <<= 1) {
-    sa += __shfl_xor(sa, off);
-    sc += __shfl_xor(sc, off);
-  }
+  sa = sum8_lanes(sa);
+  sc = sum8_lanes(sc);
   if (dblk == 0) {
     sm.kinv[2 * p] = (kLog2eL / 8.0f) * __builtin_amdgcn_rsqf(fmaxf(sa, kEps * kEps));
     sm.kinv[2 * p + 1] = (kLog2eL / 8.0f) * __builtin_amdgcn_rsqf(fmaxf(sc, kEps * kEps));
@@ -132,8 +148,7 @@ __device__ __forceinline__ void attend_keys(const LocalLds& sm, const bf16x8 (&q
       cm = fmaxf(cm, s[t][i]);
     }
   }
-  cm = fmaxf(cm, __shfl_xor(cm, 16));
-  cm = fmaxf(cm, __shfl_xor(cm, 32));
+  cm = max4_groups(cm);
   const float mn = fmaxf(st.m, cm);
   const float msafe = mn == -INFINITY ? 0.f : mn;
   const float scale = __builtin_amdgcn_exp2f(st.m - msafe);   // 0 while nothing was kept
