@@ -63,6 +63,9 @@ CASES = {
     "ragged": synth.Workload("u_rag", 3, 1, 64 * 21, 64, 10, 3, 64, False, False, "bf16", 57),
     # 5 to 8 rounds: the round-key table's 8-wide variant with padded slots
     "six_rounds": synth.Workload("u_r6", 1, 2, 2048, 64, 16, 6, 64, True, True, "bf16", 59),
+    # many buckets: the hash's quad epilogue and the eight-wave sort scatter
+    "many_buckets": synth.Workload("u_b4096", 1, 2, 4096, 64, 4096, 3, 64, True, True, "bf16",
+                                   64),
     # bf16 inputs with fp32 per-round rows, 8 rounds, no masks: the 8-wide
     # kernel's least common form
     "eight_rounds_f32_rows": synth.Workload("u_r8f", 1, 2, 2048, 64, 16, 8, 64, False, False,
